@@ -1,0 +1,317 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Every check here is independent of the oracle's own code: a pure-Python
+brute force, torch's scaled_dot_product_attention, closed forms derived by
+hand, invariants of softmax attention, and the OCP E4M3FN / bfloat16 format
+definitions cross-checked against torch's casts.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as A
+from tests._brute import brute_head
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_case(rng, B, Hq, Hkv, lq, lk, d):
+    q = rng.standard_normal((B, Hq, lq, d))
+    k = rng.standard_normal((B, Hkv, lk, d))
+    v = rng.standard_normal((B, Hkv, lk, d))
+    return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny inputs.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(40))
+def test_oracle_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    Hkv = int(rng.integers(1, 3))
+    ratio = int(rng.integers(1, 3))
+    Hq = Hkv * ratio
+    B = int(rng.integers(1, 3))
+    sq, sk = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+    d = int(rng.integers(1, 9))
+    q, k, v = _rand_case(rng, B, Hq, Hkv, sq, sk, d)
+    scale = float(rng.uniform(0.2, 1.5))
+    softcap = float(rng.choice([0.0, 0.0, 0.7, 3.0]))
+    wl = int(rng.choice([-1, -1, 0, 1, 3]))
+    wr = int(rng.choice([-1, 0, 0, 2]))
+    used_q = rng.integers(0, sq + 1, size=B) if seed % 3 == 0 else None
+    used_k = rng.integers(0, sk + 1, size=B) if seed % 4 == 0 else None
+    o, lse = oracle.attention_batch(q, k, v, scale, softcap, wl, wr, used_q, used_k)
+    for b in range(B):
+        lq = sq if used_q is None else int(used_q[b])
+        lk = sk if used_k is None else int(used_k[b])
+        for h in range(Hq):
+            g = h // ratio
+            bo, bl = brute_head(q[b, h, :lq].tolist(), k[b, g, :lk].tolist(), v[b, g, :lk].tolist(),
+                                scale, softcap, wl, wr)
+            if lq:
+                np.testing.assert_allclose(o[b, h, :lq], np.array(bo).reshape(lq, d), atol=1e-12, rtol=0)
+                np.testing.assert_array_equal(np.isinf(lse[b, h, :lq]), np.isinf(bl))
+                fin = np.isfinite(bl)
+                np.testing.assert_allclose(lse[b, h, :lq][fin], np.array(bl)[fin], atol=1e-12, rtol=0)
+            assert np.isnan(o[b, h, lq:]).all() and np.isnan(lse[b, h, lq:]).all()
+
+
+# ---------------------------------------------------------------------------
+# Library routine: torch SDPA in fp64 on the CPU (square problems only, since
+# its causal flag is top-left aligned, which equals bottom-right when sq == sk).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_matches_torch_sdpa(causal):
+    rng = np.random.default_rng(7)
+    q, k, v = _rand_case(rng, 2, 3, 3, 37, 37, 16)
+    scale = 0.3
+    o, _ = oracle.attention_batch(q, k, v, scale, 0.0, -1, 0 if causal else -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=causal, scale=scale)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms derived by hand (tests/golden/closed_form.json).
+# ---------------------------------------------------------------------------
+
+def _ev(x):
+    if isinstance(x, str):
+        return float(eval(x, {"__builtins__": {}}, {"log": math.log, "atanh": math.atanh,
+                                                   "inf": math.inf}))
+    return float(x)
+
+
+def test_closed_form_golden_cases():
+    with open(os.path.join(GOLDEN, "closed_form.json")) as f:
+        cases = json.load(f)["cases"]
+    assert len(cases) >= 5
+    for c in cases:
+        q = np.array([[_ev(x) for x in r] for r in c["q"]])
+        k = np.array([[_ev(x) for x in r] for r in c["k"]], dtype=np.float64)
+        v = np.array([[_ev(x) for x in r] for r in c["v"]], dtype=np.float64)
+        o, lse = oracle.head_attention(q, k, v, c["scale"], c["softcap"], c["window_left"],
+                                       c["window_right"])
+        np.testing.assert_allclose(o, np.array(c["o"], dtype=np.float64), atol=1e-12, err_msg=c["name"])
+        exp_lse = np.array([_ev(x) for x in c["lse"]])
+        assert np.array_equal(np.isinf(lse), np.isinf(exp_lse)), c["name"]
+        fin = np.isfinite(exp_lse)
+        np.testing.assert_allclose(lse[fin], exp_lse[fin], atol=1e-12, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------------------
+# Invariants.
+# ---------------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(1)
+    q, k, v = _rand_case(rng, 1, 1, 1, 300, 170, 8)
+    _, _, p = oracle.head_attention(q[0, 0], k[0, 0], v[0, 0], 0.9, 0.0, 40, 0, return_probs=True)
+    sums = p.sum(axis=1)
+    has = A.masked_allowed(np.arange(300), 300, 170, 40, 0).any(axis=1)
+    np.testing.assert_allclose(sums[has], 1.0, atol=1e-12)
+    assert (sums[~has] == 0).all() and (~has).any()
+
+
+def test_equal_value_rows_give_that_row():
+    rng = np.random.default_rng(2)
+    q, k, _ = _rand_case(rng, 1, 2, 1, 20, 33, 8)
+    row = rng.standard_normal(8)
+    v = np.broadcast_to(row, (1, 1, 33, 8)).copy()
+    o, _ = oracle.attention_batch(q, k, v, 0.5, 0.0, -1, 0)
+    np.testing.assert_allclose(o, np.broadcast_to(row, o.shape), atol=1e-12)
+
+
+def test_zero_query_gives_uniform_weights():
+    rng = np.random.default_rng(3)
+    lq, lk, wl, wr = 12, 20, 5, 0
+    q = np.zeros((lq, 4))
+    k = rng.standard_normal((lk, 4))
+    v = rng.standard_normal((lk, 4))
+    o, lse = oracle.head_attention(q, k, v, 1.0, 0.0, wl, wr)
+    for i in range(lq):
+        js = [j for j in range(lk) if i + lk - lq - wl <= j <= i + lk - lq + wr]
+        np.testing.assert_allclose(o[i], v[js].mean(axis=0), atol=1e-12)
+        assert abs(lse[i] - math.log(len(js))) < 1e-12
+
+
+def test_causal_row_zero_and_key_counts():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand_case(rng, 1, 1, 1, 16, 16, 8)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    o, lse, p = oracle.head_attention(q, k, v, 0.7, 0.0, -1, 0, return_probs=True)
+    np.testing.assert_allclose(o[0], v[0], atol=1e-12)
+    assert abs(lse[0] - 0.7 * float(q[0] @ k[0])) < 1e-12
+    for i in range(16):
+        assert (p[i, :i + 1] > 0).all() and (p[i, i + 1:] == 0).all()
+
+
+def test_decode_query_sees_every_key_bottom_right():
+    rng = np.random.default_rng(5)
+    q, k, v = _rand_case(rng, 1, 1, 1, 1, 50, 8)
+    oc, lc = oracle.head_attention(q[0, 0], k[0, 0], v[0, 0], 0.4, 0.0, -1, 0)
+    on, ln = oracle.head_attention(q[0, 0], k[0, 0], v[0, 0], 0.4, 0.0, -1, -1)
+    np.testing.assert_array_equal(oc, on)
+    np.testing.assert_array_equal(lc, ln)
+
+
+def test_key_permutation_invariance_without_mask():
+    rng = np.random.default_rng(6)
+    q, k, v = _rand_case(rng, 1, 1, 1, 40, 64, 16)
+    perm = rng.permutation(64)
+    o1, l1 = oracle.head_attention(q[0, 0], k[0, 0], v[0, 0], 0.25)
+    o2, l2 = oracle.head_attention(q[0, 0], k[0, 0, perm], v[0, 0, perm], 0.25)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+
+
+def test_lse_is_log_sum_exp_of_logits():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand_case(rng, 1, 1, 1, 10, 25, 4)
+    q, k, v = q[0, 0] * 0.3, k[0, 0], v[0, 0]
+    _, lse = oracle.head_attention(q, k, v, 0.5)
+    for i in range(10):
+        direct = math.log(math.fsum(math.exp(0.5 * sum(q[i, c] * k[j, c] for c in range(4)))
+                                    for j in range(25)))
+        assert abs(lse[i] - direct) < 1e-12
+
+
+def test_softcap_limits():
+    rng = np.random.default_rng(9)
+    q, k, v = _rand_case(rng, 1, 1, 1, 30, 40, 16)
+    q, k, v = q[0, 0] * 3, k[0, 0] * 3, v[0, 0]
+    o0, l0 = oracle.head_attention(q, k, v, 1.0)
+    o1, l1 = oracle.head_attention(q, k, v, 1.0, 1e9)
+    np.testing.assert_allclose(o1, o0, atol=1e-9)
+    np.testing.assert_allclose(l1, l0, atol=1e-9)
+    # every capped logit lies in (-cap, cap), so LSE is bounded by cap + ln(Lk)
+    cap = 2.0
+    _, lc = oracle.head_attention(q, k, v, 1.0, cap)
+    assert (lc < cap + math.log(40)).all() and (lc > -cap + math.log(40)).all()
+    # zero or negative cap disables it
+    on, ln = oracle.head_attention(q, k, v, 1.0, -1.0)
+    np.testing.assert_array_equal(on, o0)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    rng = np.random.default_rng(10)
+    q, k, v = _rand_case(rng, 2, 6, 2, 9, 14, 8)
+    o_g, l_g = oracle.attention_batch(q, k, v, 0.6, 0.0, -1, 0)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    o_m, l_m = oracle.attention_batch(q, kr, vr, 0.6, 0.0, -1, 0)
+    np.testing.assert_array_equal(o_g, o_m)
+    np.testing.assert_array_equal(l_g, l_m)
+    with pytest.raises(ValueError):
+        oracle.attention_batch(q[:, :5], k, v, 0.6)
+
+
+def test_varlen_equals_per_sequence_batch():
+    rng = np.random.default_rng(11)
+    lq = [3, 0, 7, 5]
+    lk = [3, 4, 9, 5]
+    cq, ck = np.cumsum([0] + lq), np.cumsum([0] + lk)
+    q = rng.standard_normal((cq[-1], 4, 8))
+    k = rng.standard_normal((ck[-1], 2, 8))
+    v = rng.standard_normal((ck[-1], 2, 8))
+    o, lse = oracle.attention_varlen(q, k, v, cq, ck, 0.4, 0.0, -1, 0)
+    for s in range(4):
+        for h in range(4):
+            bo, bl = brute_head(q[cq[s]:cq[s + 1], h].tolist(), k[ck[s]:ck[s + 1], h // 2].tolist(),
+                                v[ck[s]:ck[s + 1], h // 2].tolist(), 0.4, 0.0, -1, 0)
+            if lq[s]:
+                np.testing.assert_allclose(o[cq[s]:cq[s + 1], h], np.array(bo), atol=1e-12)
+                np.testing.assert_allclose(lse[h, cq[s]:cq[s + 1]], bl, atol=1e-12)
+
+
+def test_paged_gather_is_layout_independent():
+    rng = np.random.default_rng(12)
+    P, Hkv, d, lens = 4, 2, 8, [5, 12, 1]
+    n_pages = [-(-L // P) for L in lens]
+    n = sum(n_pages)
+    k_cont = [rng.standard_normal((Hkv, L, d)) for L in lens]
+    v_cont = [rng.standard_normal((Hkv, L, d)) for L in lens]
+    q = rng.standard_normal((3, 4, 2, d))
+
+    def build(perm):
+        kp = np.full((n + 1, P, Hkv, d), np.nan)
+        vp = np.full((n + 1, P, Hkv, d), np.nan)
+        table = np.full((3, max(n_pages) + 1), n, dtype=np.int32)
+        off = 0
+        for r, L in enumerate(lens):
+            for t in range(L):
+                page = perm[off + t // P]
+                kp[page, t % P] = k_cont[r][:, t]
+                vp[page, t % P] = v_cont[r][:, t]
+            table[r, :n_pages[r]] = perm[off:off + n_pages[r]]
+            off += n_pages[r]
+        return kp, vp, table
+
+    res = []
+    for perm in (np.arange(n), rng.permutation(n)):
+        kp, vp, table = build(perm)
+        res.append(oracle.attention_paged(q, kp, vp, table, lens, 0.5))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+    for r, L in enumerate(lens):
+        o, lse = oracle.attention_batch(q[r:r + 1], k_cont[r][None], v_cont[r][None], 0.5)
+        np.testing.assert_array_equal(res[1][0][r], o[0])
+        np.testing.assert_array_equal(res[1][1][r], lse[0])
+    assert np.isfinite(res[1][0]).all()
+
+
+def test_empty_inputs():
+    o, lse = oracle.head_attention(np.zeros((3, 4)), np.zeros((0, 4)), np.zeros((0, 4)), 1.0)
+    assert (o == 0).all() and np.isneginf(lse).all()
+    o, lse = oracle.head_attention(np.zeros((0, 4)), np.zeros((5, 4)), np.zeros((5, 4)), 1.0)
+    assert o.shape == (0, 4) and lse.shape == (0,)
+
+
+def test_thread_pool_matches_serial():
+    rng = np.random.default_rng(13)
+    q, k, v = _rand_case(rng, 2, 4, 2, 33, 40, 8)
+    a = oracle.attention_batch(q, k, v, 0.3, 5.0, -1, 0, workers=1)
+    b = oracle.attention_batch(q, k, v, 0.3, 5.0, -1, 0, workers=4)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Stored formats.
+# ---------------------------------------------------------------------------
+
+def test_e4m3fn_table_matches_format_definition_and_torch():
+    t = oracle.E4M3FN_TABLE
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0          # largest finite
+    assert t[0x01] == 2.0 ** -9                             # smallest subnormal
+    assert t[0x08] == 2.0 ** -6                             # smallest normal
+    assert t[0x38] == 1.0 and t[0x00] == 0.0 and t[0x80] == 0.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isnan(t).sum() == 2
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = ref.numpy()
+    same = (ref == t) | (np.isnan(ref) & np.isnan(t))
+    assert same.all()
+
+
+def test_e4m3fn_decode_with_descale():
+    b = np.array([0x38, 0xB8, 0x7E, 0x01], dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3fn_bits_to_f64(b, 0.5), [0.5, -0.5, 224.0, 2.0 ** -10])
+
+
+def test_bf16_decode_matches_torch():
+    x = torch.randn(1000, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16)
+    x[0] = float("inf")
+    x[1] = -0.0
+    bits = x.view(torch.int16).numpy()
+    dec = oracle.bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(dec, x.to(torch.float64).numpy())
+    assert oracle.bf16_bits_to_f64(np.array([0x3F80], dtype=np.uint16))[0] == 1.0
+    assert oracle.bf16_bits_to_f64(np.array([0xC000], dtype=np.uint16))[0] == -2.0
