@@ -1,0 +1,199 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  * batch-mode causal prefill, bf16, B=4, H=16, s=2048, d=128 (scale 1/sqrt(d),
+    bf16 O, fp32 LSE) -> TFLOP/s, the headline value;
+  * paged-KV decode, bf16, 64 requests with context lengths ~ U[1024, 32768],
+    128-token pages in a randomly permuted pool, Hq=32, Hkv=8, d=128 (split-KV
+    kernel + combine) -> HBM GB/s.
+Inputs are generated on the GPU and resident in HBM before timing. Each launch
+is bracketed by HIP events on the stream the library enqueues on; values are
+algorithmic work / mean launch duration:
+  prefill flops = 4 d * (visible query-key pairs) per q-head,
+  decode bytes  = K + V of every valid token and kv-head, + Q + O + LSE + the
+                  used block-table entries + seqlens.
+The CPU baseline is the fp64 oracle on a bounded sample (a subset of the
+prefill's heads), timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (bf16 causal d=128) + paged-decode HBM GB/s, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def prefill_flops(case) -> float:
+    m = case.meta
+    sq, sk, d, B, Hq = m["sq"], m["sk"], m["d"], m["B"], m["Hq"]
+    assert sq == sk and case.causal
+    pairs = sq * (sq + 1) // 2
+    return 4.0 * d * pairs * B * Hq
+
+
+def decode_bytes(case) -> float:
+    m = case.meta
+    lens = m["lens_k"]
+    kv = 2 * sum(lens) * m["Hkv"] * m["d"] * 2
+    q = m["B"] * m["Hq"] * m["sq"] * m["d"] * 2
+    o = q
+    lse = m["B"] * m["Hq"] * m["sq"] * 4
+    table = sum(-(-L // m["page_size"]) for L in lens) * 4
+    return float(kv + q + o + lse + table + m["B"] * 4)
+
+
+def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
+    """The fp64 oracle on the first n_heads (batch, head) pairs of the prefill
+    workload, with its own thread pool over heads (one BLAS thread per worker),
+    timed on the host cores; repeated until about min_seconds have elapsed."""
+    import oracle
+    from tests._cases import decode
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    m = case.meta
+    assert m["Hq"] == m["Hkv"]
+    n = min(n_heads, m["B"] * m["Hq"])
+    # the first n (batch, head) pairs in row-major order, as one batch entry of n heads
+    q = decode(case.t["q"].reshape(1, -1, m["sq"], m["d"])[:, :n], "bf16")
+    k = decode(case.t["k"].reshape(1, -1, m["sk"], m["d"])[:, :n], "bf16")
+    v = decode(case.t["v"].reshape(1, -1, m["sk"], m["d"])[:, :n], "bf16")
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:  # repeat the sample until about min_seconds of CPU work is timed
+            oracle.attention_batch(q, k, v, case.scale, 0.0, -1, 0, workers=cores)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    dt /= reps
+    flops = prefill_flops(case) * n / (m["B"] * m["Hq"])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle on {n} of {m['B'] * m['Hq']} (batch, head) pairs of the prefill workload, "
+                      f"{dt:.3f} s per pass (mean of {reps} passes) on {cores} threads, one BLAS thread each; "
+                      f"value = those heads' algorithmic (causal) flops / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--decode-split", type=int, default=0, help="keys per split-KV unit (0 = library default)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_attn_amd as pk
+    import synth
+
+    dev = "cuda"
+    print("bench: generating workloads on the GPU", file=sys.stderr, flush=True)
+    pre = synth.workload(2, dev)
+    dec = synth.workload(4, dev)
+    t = pre.t
+    o_pre = torch.empty_like(t["q"])
+    l_pre = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=dev)
+    td = dec.t
+    o_dec = torch.empty_like(td["q"])
+    l_dec = torch.empty(td["q"].shape[:3], dtype=torch.float32, device=dev)
+    p_dec = pk.attn_params(torch.bfloat16, 128, kv_split_tokens=args.decode_split)
+    W = td["block_table"].shape[1]
+    ws_bytes = pk.attn_workspace_bytes(p_dec, 64, 32, 8, 1, 128, W * 128)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def run_prefill():
+        pk.attn_fwd(t["q"], t["k"], t["v"], scale=pre.scale, causal=True, out=o_pre, lse=l_pre)
+
+    def run_decode():
+        pk.attn_fwd_paged(td["q"], td["k_pool"], td["v_pool"], td["block_table"], td["seqlens_k"], scale=dec.scale,
+                          out=o_dec, lse=l_dec, kv_split_tokens=args.decode_split, workspace=ws)
+
+    for _ in range(args.warmup):
+        run_prefill()
+        run_decode()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        run_prefill()
+        ev[i][1].record()
+        ev[i][2].record()
+        run_decode()
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    t_pre = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    t_dec = sorted(e[2].elapsed_time(e[3]) for e in ev)
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    pre_ms, dec_ms = mean(t_pre), mean(t_dec)
+    flops = prefill_flops(pre)
+    dbytes = decode_bytes(dec)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    gbs = dbytes / (dec_ms * 1e-3) / 1e9
+    print(f"bench: prefill {pre_ms * 1e3:.1f} us (min {t_pre[0] * 1e3:.1f}) {tflops:.1f} TFLOP/s; "
+          f"decode {dec_ms * 1e3:.1f} us (min {t_dec[0] * 1e3:.1f}) {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(pre, args.cpu_heads)
+        print(f"bench: cpu oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads", file=sys.stderr,
+              flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 causal prefill, batch mode B=4 H=16 sq=sk=2048 d=128, bf16 O + fp32 LSE",
+                   "batch": 4, "heads": 16, "seq_len": 2048, "head_dim": 128, "mask": "causal"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<128, bf16, batch, causal>", "launch_us": round(pre_ms * 1e3, 2),
+                     "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+        "paged_decode": {
+            "value": round(gbs, 1), "unit": "GB/s",
+            "workload": "bf16 paged decode, 64 requests L~U[1024,32768], page 128, Hq=32 Hkv=8 d=128, sq=1",
+            "launch_us": round(dec_ms * 1e3, 2), "min_us": round(t_dec[0] * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "decode_kernel<128, paged> + combine_kernel", "algorithmic_bytes": dbytes},
+            "splits": pk.attn_num_splits(p_dec, 64, 32, 8, 1, W * 128),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

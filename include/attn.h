@@ -1,0 +1,182 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention forward library
+ * (libattn.so).
+ *
+ * One operation, three addressing modes. For every query row i of sequence b
+ * and q-head h, with kv-head g = h / (Hq / Hkv) and used lengths Lq, Lk:
+ *
+ *     S[i,j]   = scale * dot(Q[b,h,i,:], K[b,g,j,:])            (0 <= j < Lk)
+ *     S[i,j]   = softcap * tanh(S[i,j] / softcap)               if softcap > 0
+ *     visible  = (wl < 0 || j >= i + Lk - Lq - wl) && (wr < 0 || j <= i + Lk - Lq + wr)
+ *     O[b,h,i] = sum_j softmax_j(S[i, visible]) * V[b,g,j,:]
+ *     LSE[b,h,i] = ln sum_{visible j} exp(S[i,j])
+ *
+ * This is the math contract printed at the top of the Composable Kernel page
+ * "fmha_fwd_pagedkv_kernel.hpp Source File" (S = Q K^T, S' = S * scale,
+ * P = softmax, O = P V), with the logit soft-cap and window-mask arguments of the
+ * same page's kernel-argument structs (FmhaFwdLogitsSoftCapKargs, FmhaFwdMaskKargs),
+ * its grouped-query head map (kv head = q head / nhead_ratio_qk), and the LSE
+ * output and empty-row convention of the flash-attention page
+ * "hopper/epilogue_fwd.hpp" (CollectiveEpilogueFwd::store / store_zero: a row
+ * with no visible key gets O = 0 and LSE = -inf). The mask diagonal is aligned
+ * bottom-right (offset Lk - Lq), so causal = (wl, wr) = (-1, 0) and a single
+ * decode query sees every key.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers; every buffer is allocated and
+ *     owned by the caller. The library never allocates, frees or synchronises:
+ *     a call validates its arguments on the host, enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the legacy default stream) and returns.
+ *   - Strides are in ELEMENTS of the stored type; the head dimension d is
+ *     contiguous (unit stride). Every tensor base pointer must be 16-byte
+ *     aligned and every stride a multiple of 16 bytes.
+ *   - Supported: d in {64, 128}; (in_dtype, out_dtype) in {(F32, F32),
+ *     (BF16, BF16), (FP8_E4M3, BF16)}; F32 only in batch mode with no window
+ *     and sk <= 4096. FP8 means OCP E4M3FN; the value of a stored byte x is
+ *     e4m3(x) * descale of its tensor.
+ *   - lse may be NULL (not stored). LSE is fp32, natural log.
+ *   - Rows at or beyond a sequence's used query length are never written, in O
+ *     or LSE (the predicated stores of the flash-attention epilogue page).
+ *     K/V rows at or beyond the used key length, block-table entries past
+ *     ceil(Lk / page_size) and slots past Lk in the last page are never read as
+ *     keys.
+ *   - Device-resident metadata (seqused, cu_seqlens, seqlens_k, block tables)
+ *     is a precondition: monotone, in range, page ids < num_pages. Violating it
+ *     is undefined behaviour (it is not checked on the device).
+ *   - Results are deterministic: the same call gives the same bits. Calls that
+ *     differ only in addressing (paged vs contiguous KV with the same logical
+ *     contents and the same split size; varlen vs padded batch with seqused)
+ *     give bit-identical results on every valid row.
+ *   - Return value: ATTN_OK, or an error status with no kernel launched (except
+ *     ATTN_ELAUNCH, reported when the runtime rejects a launch). attn_last_error()
+ *     then describes it.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,      /* IEEE binary32 */
+  ATTN_BF16 = 1,     /* bfloat16 */
+  ATTN_FP8_E4M3 = 2  /* OCP FP8 E4M3FN, per-tensor descale */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,     /* bad argument: NULL pointer, bad size, stride, alignment */
+  ATTN_ENOTSUP = 2,    /* valid but not implemented (head dim, dtype pair, mode) */
+  ATTN_EWORKSPACE = 3, /* workspace smaller than attn_workspace_bytes() */
+  ATTN_ELAUNCH = 4     /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+typedef struct {
+  int in_dtype;        /* attn_dtype_t of Q, K and V */
+  int out_dtype;       /* attn_dtype_t of O */
+  float scale;         /* multiplies q.k (scale_s of the Composable Kernel page) */
+  float softcap;       /* > 0 enables cap * tanh(s / cap); <= 0 disables */
+  int window_left;     /* -1 = unbounded; causal = (-1, 0) */
+  int window_right;
+  float q_descale;     /* FP8 only: stored value * descale = real value; else ignored */
+  float k_descale;
+  float v_descale;
+  int kv_split_tokens; /* decode path: keys per split-KV work unit, a multiple of 64;
+                          0 = choose from the shape. Calls that must agree bit for bit
+                          pass the same value (or the same shape with 0). */
+} attn_params_t;
+
+/* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
+ * descales 1, automatic split size. */
+void attn_params_init(attn_params_t* p, float scale);
+
+/*
+ * Batch mode. Q [B, Hq, sq, d], K and V [B, Hkv, sk, d], O [B, Hq, sq, d],
+ * each addressed as base + b*stride[0] + head*stride[1] + row*stride[2] + c.
+ * lse (nullable) is a dense fp32 [B, Hq, sq] array.
+ * seqused_q / seqused_k (nullable, int32 [B] on the device) give per-batch used
+ * lengths Lq <= sq, Lk <= sk; NULL means Lq = sq, Lk = sk.
+ * Short query blocks (sq * Hq / Hkv <= 16) run the split-KV decode path, which
+ * needs `workspace` of attn_workspace_bytes() bytes (else workspace may be NULL).
+ * (Batch-mode arguments of the Composable Kernel page's MakeKargs; the
+ * [B, H, N, d] tensors of the FlashAttention-2 mma page's entry point.)
+ */
+attn_status_t attn_fwd(const attn_params_t* p,
+                       const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int sq, int sk, int d,
+                       const int64_t q_stride[3], const int64_t k_stride[3],
+                       const int64_t v_stride[3], const int64_t o_stride[3],
+                       const int32_t* seqused_q, const int32_t* seqused_k,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Varlen (group) mode. n sequences packed along the token axis:
+ * Q [total_q, Hq, d], K and V [total_k, Hkv, d], O [total_q, Hq, d], addressed
+ * as base + token*stride[0] + head*stride[1] + c. Sequence s owns query tokens
+ * cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and key tokens likewise
+ * (int32 [n+1] device arrays, the seqstart_q/k pointers of the Composable Kernel
+ * page's group-mode MakeKargs). max_seqlen_q / max_seqlen_k bound every
+ * sequence's lengths (they size the grid). lse (nullable) is fp32 [Hq, total_q].
+ * Needs no workspace.
+ */
+attn_status_t attn_fwd_varlen(const attn_params_t* p,
+                              const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int n, int total_q, int max_seqlen_q, int max_seqlen_k,
+                              int Hq, int Hkv, int d,
+                              const int64_t q_stride[2], const int64_t k_stride[2],
+                              const int64_t v_stride[2], const int64_t o_stride[2],
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged-KV mode (decode). Q [B, Hq, sq, d] and O [B, Hq, sq, d] strided as in
+ * attn_fwd; K and V live in page pools of num_pages pages of page_size tokens,
+ * addressed as pool + page*kv_stride[0] + head*kv_stride[1] + slot*kv_stride[2] + c
+ * (64-bit offsets). Token t of request b is slot t % page_size of page
+ * block_table[b*block_table_stride + t / page_size] (the page-block navigator
+ * of the Composable Kernel page: block_table_ptr, batch_stride_block_table,
+ * page_block_size). seqlens_k (int32 [B], device) gives Lk per request;
+ * Lq = sq. page_size must be a multiple of 64; block_table_stride * page_size
+ * bounds every Lk. Requires sq * Hq / Hkv <= 16 (decode shapes). lse (nullable)
+ * is fp32 [B, Hq, sq]. Needs a workspace of attn_workspace_bytes() bytes with
+ * max_seqlen_k = block_table_stride * page_size.
+ */
+attn_status_t attn_fwd_paged(const attn_params_t* p,
+                             const void* q, const void* k_pool, const void* v_pool,
+                             void* o, float* lse,
+                             const int32_t* block_table, int block_table_stride,
+                             const int32_t* seqlens_k,
+                             int B, int sq, int Hq, int Hkv, int d,
+                             int page_size, int num_pages,
+                             const int64_t q_stride[3], const int64_t kv_stride[3],
+                             const int64_t o_stride[3],
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by attn_fwd / attn_fwd_paged for this shape (0 when
+ * the shape takes the prefill path). max_seqlen_k is sk for attn_fwd and
+ * block_table_stride * page_size for attn_fwd_paged. Returns 0 for invalid
+ * shapes as well; the entry point then reports the error.
+ */
+size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d,
+                            int max_seqlen_k);
+
+/* Number of split-KV work units per (request, kv-head) the decode path uses for
+ * this shape (1 if it takes the prefill path). */
+int attn_num_splits(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int max_seqlen_k);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

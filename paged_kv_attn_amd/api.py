@@ -1,0 +1,145 @@
+"""Python binding of libattn with the C ABI's names.
+
+Argument marshalling only: tensors become device pointers and element
+strides, outputs and the split-KV workspace are allocated with torch, and every
+call is enqueued on torch's current stream of the tensors' device. Every step
+of the attention computation runs in the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import AttnParams, check, i64_array, lib
+
+_IN_TYPES = {torch.float32: _lib.ATTN_F32, torch.bfloat16: _lib.ATTN_BF16,
+             torch.float8_e4m3fn: _lib.ATTN_FP8_E4M3}
+
+
+def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens):
+    if dtype not in _IN_TYPES:
+        raise TypeError(f"unsupported input dtype {dtype}")
+    p = AttnParams()
+    lib().attn_params_init(ctypes.byref(p), float(scale if scale is not None else 1.0 / math.sqrt(d)))
+    p.in_dtype = _IN_TYPES[dtype]
+    p.out_dtype = _lib.ATTN_F32 if dtype == torch.float32 else _lib.ATTN_BF16
+    p.softcap = float(softcap)
+    if window is not None:
+        p.window_left, p.window_right = int(window[0]), int(window[1])
+    elif causal:
+        p.window_left, p.window_right = -1, 0
+    p.q_descale, p.k_descale, p.v_descale = (float(x) for x in descale)
+    p.kv_split_tokens = int(kv_split_tokens)
+    return p
+
+
+def out_dtype_for(dtype):
+    return torch.float32 if dtype == torch.float32 else torch.bfloat16
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def attn_params(dtype, d, scale=None, causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0),
+                kv_split_tokens=0) -> AttnParams:
+    """The attn_params_t a call with these options passes to the library."""
+    return _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens)
+
+
+def attn_workspace_bytes(params: AttnParams, B, Hq, Hkv, sq, d, max_seqlen_k) -> int:
+    return int(lib().attn_workspace_bytes(ctypes.byref(params), B, Hq, Hkv, sq, d, max_seqlen_k))
+
+
+def attn_num_splits(params: AttnParams, B, Hq, Hkv, sq, max_seqlen_k) -> int:
+    return int(lib().attn_num_splits(ctypes.byref(params), B, Hq, Hkv, sq, max_seqlen_k))
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode(errors="replace")
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seqused_q=None,
+             seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
+             kv_split_tokens=0, workspace=None):
+    """Batch mode. q [B, Hq, sq, d], k / v [B, Hkv, sk, d] (any strides, d
+    contiguous). Returns (out [B, Hq, sq, d], lse [B, Hq, sq] or None)."""
+    B, Hq, sq, d = q.shape
+    Hkv, sk = k.shape[1], k.shape[2]
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens)
+    if out is None:
+        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
+    ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, sk)
+    ws = _workspace(ws_bytes, q.device, workspace)
+    st = lambda t: i64_array(t.stride()[:3])  # noqa: E731
+    check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                         B, Hq, Hkv, sq, sk, d, st(q), st(k), st(v), st(out),
+                         _ptr(seqused_q), _ptr(seqused_k), _ptr(ws), ws_bytes, _stream(q)))
+    return out, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
+                    causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
+                    return_lse=True):
+    """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
+    on the device. Returns (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    n = cu_seqlens_q.numel() - 1
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0)
+    if out is None:
+        out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype), device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    st = lambda t: i64_array(t.stride()[:2])  # noqa: E731
+    check(lib().attn_fwd_varlen(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), n, Tq, int(max_seqlen_q),
+                                int(max_seqlen_k), Hq, Hkv, d, st(q), st(k), st(v), st(out),
+                                ctypes.c_void_p(0), 0, _stream(q)))
+    return out, lse
+
+
+def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
+                   softcap=0.0, out=None, lse=None, return_lse=True, kv_split_tokens=0, workspace=None):
+    """Paged-KV decode. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
+    (any strides, d contiguous; K and V pools with equal strides);
+    block_table int32 [B, W]; seqlens_k int32 [B]. Returns (out, lse)."""
+    B, Hq, sq, d = q.shape
+    num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same strides")
+    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise TypeError("block_table and seqlens_k must be int32")
+    W = block_table.shape[1]
+    p = _params(q.dtype, d, scale, causal, window, softcap, (1.0, 1.0, 1.0), kv_split_tokens)
+    if out is None:
+        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
+    ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, W * page_size)
+    ws = _workspace(ws_bytes, q.device, workspace)
+    kv_stride = i64_array([k_pool.stride(0), k_pool.stride(2), k_pool.stride(1)])
+    st = lambda t: i64_array(t.stride()[:3])  # noqa: E731
+    check(lib().attn_fwd_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
+                               _ptr(block_table), int(block_table.stride(0)), _ptr(seqlens_k),
+                               B, sq, Hq, Hkv, d, page_size, num_pages, st(q), kv_stride, st(out),
+                               _ptr(ws), ws_bytes, _stream(q)))
+    return out, lse

@@ -1,0 +1,346 @@
+// C ABI of libattn: argument validation, path selection and launch set-up.
+//
+// Every check runs on the host before any launch, so a rejected call touches
+// no device state. Errors follow the convention of the FlashAttention-2 mma
+// page's torch entry point (unsupported head dims / dtypes are refused up
+// front) and of the Composable Kernel page's MakeKargs (strides, head ratio,
+// page-block size are arguments, not assumptions).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int elem_bytes(int t) { return t == ATTN_F32 ? 4 : (t == ATTN_BF16 ? 2 : 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Decode-path choice: the packed query block (positions x q-heads of one
+// kv-head) fits the 16 columns of one MFMA tile.
+bool takes_decode_path(int in_dtype, int sq, int ratio) {
+  return in_dtype != ATTN_F32 && (int64_t)sq * ratio <= 16;
+}
+
+// Keys per split-KV work unit: unless the caller fixes it, the smallest power
+// of two >= 256 that keeps the (request, kv-head, split) grid near 8192 units.
+int plan_split_tokens(const attn_params_t* p, int B, int Hkv, int max_len) {
+  if (p->kv_split_tokens > 0) return p->kv_split_tokens;
+  const int64_t units = (int64_t)B * Hkv;
+  int c = 256;
+  while (c < 4096 && units * ((max_len + c - 1) / c) > 8192) c *= 2;
+  return c;
+}
+
+int n_splits_for(int split, int max_len) { return max_len > 0 ? (max_len + split - 1) / split : 1; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_ws_bytes(int B, int Hkv, int n_splits, int m_rows, int d) {
+  const size_t units = (size_t)B * Hkv * n_splits * m_rows;
+  return align256(units * d * sizeof(float)) + align256(units * sizeof(float));
+}
+
+attn_status_t check_params(const attn_params_t* p, int d) {
+  if (!p) return fail(ATTN_EINVAL, "params is NULL");
+  const bool pair_ok = (p->in_dtype == ATTN_F32 && p->out_dtype == ATTN_F32) ||
+                       (p->in_dtype == ATTN_BF16 && p->out_dtype == ATTN_BF16) ||
+                       (p->in_dtype == ATTN_FP8_E4M3 && p->out_dtype == ATTN_BF16);
+  if (!pair_ok) return fail(ATTN_ENOTSUP, "unsupported (in_dtype, out_dtype) = (%d, %d)", p->in_dtype, p->out_dtype);
+  if (d != 64 && d != 128) return fail(ATTN_ENOTSUP, "head dim %d not supported (64 or 128)", d);
+  if (!(p->scale > 0.0f) || !std::isfinite(p->scale)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
+  if (!std::isfinite(p->softcap)) return fail(ATTN_EINVAL, "softcap must be finite");
+  if (p->window_left < -1 || p->window_right < -1) return fail(ATTN_EINVAL, "window bounds must be >= -1");
+  if (p->in_dtype == ATTN_FP8_E4M3) {
+    const float ds[3] = {p->q_descale, p->k_descale, p->v_descale};
+    for (float x : ds)
+      if (!(x > 0.0f) || !std::isfinite(x)) return fail(ATTN_EINVAL, "fp8 descales must be finite and > 0");
+  }
+  if (p->kv_split_tokens < 0 || p->kv_split_tokens % 64 != 0)
+    return fail(ATTN_EINVAL, "kv_split_tokens must be 0 or a positive multiple of 64");
+  return ATTN_OK;
+}
+
+attn_status_t check_strides(const char* name, const int64_t* st, int n, int eb) {
+  if (!st) return fail(ATTN_EINVAL, "%s stride array is NULL", name);
+  for (int i = 0; i < n; ++i) {
+    if (st[i] < 0) return fail(ATTN_EINVAL, "%s stride[%d] is negative", name, i);
+    if ((st[i] * eb) % 16 != 0) return fail(ATTN_EINVAL, "%s stride[%d] is not a multiple of 16 bytes", name, i);
+  }
+  return ATTN_OK;
+}
+
+attn_status_t check_ptr(const char* name, const void* ptr) {
+  if (!ptr) return fail(ATTN_EINVAL, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+// exp2-domain constants shared by all paths
+void logit_consts(const attn_params_t* p, float* c_exp2, float* pre, float* post) {
+  double s = p->scale;
+  if (p->in_dtype == ATTN_FP8_E4M3) s *= (double)p->q_descale * (double)p->k_descale;
+  if (p->softcap > 0.0f) {
+    *pre = (float)(s / p->softcap);
+    *post = (float)(p->softcap * 1.4426950408889634);
+    *c_exp2 = 1.0f;
+  } else {
+    *pre = 0.0f;
+    *post = 0.0f;
+    *c_exp2 = (float)(s * 1.4426950408889634);
+  }
+}
+
+attn_status_t launched(hipError_t e) {
+  if (e != hipSuccess) return fail(ATTN_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+#define TRY(x)                       \
+  do {                               \
+    attn_status_t st_ = (x);         \
+    if (st_ != ATTN_OK) return st_;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err; }
+
+const char* attn_version(void) { return "libattn 0.1 (gfx950)"; }
+
+void attn_params_init(attn_params_t* p, float scale) {
+  if (!p) return;
+  memset(p, 0, sizeof(*p));
+  p->in_dtype = ATTN_BF16;
+  p->out_dtype = ATTN_BF16;
+  p->scale = scale;
+  p->softcap = 0.0f;
+  p->window_left = -1;
+  p->window_right = -1;
+  p->q_descale = p->k_descale = p->v_descale = 1.0f;
+  p->kv_split_tokens = 0;
+}
+
+size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
+  if (!p || B <= 0 || Hq <= 0 || Hkv <= 0 || sq <= 0 || max_seqlen_k < 0 || Hq % Hkv) return 0;
+  const int ratio = Hq / Hkv;
+  if (!takes_decode_path(p->in_dtype, sq, ratio)) return 0;
+  const int split = plan_split_tokens(p, B, Hkv, max_seqlen_k);
+  return decode_ws_bytes(B, Hkv, n_splits_for(split, max_seqlen_k), sq * ratio, d);
+}
+
+int attn_num_splits(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int max_seqlen_k) {
+  if (!p || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || sq <= 0) return 1;
+  if (!takes_decode_path(p->in_dtype, sq, Hq / Hkv)) return 1;
+  return n_splits_for(plan_split_tokens(p, B, Hkv, max_seqlen_k), max_seqlen_k);
+}
+
+attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int sq, int sk, int d, const int64_t q_stride[3],
+                       const int64_t k_stride[3], const int64_t v_stride[3], const int64_t o_stride[3],
+                       const int32_t* seqused_q, const int32_t* seqused_k, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  TRY(check_params(p, d));
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || sq < 0 || sk < 0) return fail(ATTN_EINVAL, "bad sizes B=%d Hq=%d Hkv=%d sq=%d sk=%d", B, Hq, Hkv, sq, sk);
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  const int eb = elem_bytes(p->in_dtype), ob = elem_bytes(p->out_dtype);
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("k", k));
+  TRY(check_ptr("v", v));
+  TRY(check_ptr("o", o));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
+  TRY(check_strides("q", q_stride, 3, eb));
+  TRY(check_strides("k", k_stride, 3, eb));
+  TRY(check_strides("v", v_stride, 3, eb));
+  TRY(check_strides("o", o_stride, 3, ob));
+  if (B == 0 || sq == 0) return ATTN_OK;
+  const int ratio = Hq / Hkv;
+  hipStream_t s = (hipStream_t)stream;
+  float c_exp2, pre, post;
+  logit_consts(p, &c_exp2, &pre, &post);
+
+  if (p->in_dtype == ATTN_F32) {
+    attn::F32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v; a.o = (float*)o; a.lse = lse;
+    a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
+    a.k_sb = k_stride[0]; a.k_sh = k_stride[1]; a.k_sr = k_stride[2];
+    a.v_sb = v_stride[0]; a.v_sh = v_stride[1]; a.v_sr = v_stride[2];
+    a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_sr = o_stride[2];
+    a.seqused_q = seqused_q; a.seqused_k = seqused_k;
+    a.B = B; a.sq = sq; a.sk = sk; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
+    a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+    a.wl = p->window_left; a.wr = p->window_right;
+    return launched(attn::launch_f32(a, d, s));
+  }
+
+  if (takes_decode_path(p->in_dtype, sq, ratio)) {
+    if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "the decode path (sq*Hq/Hkv <= 16) supports bf16 only");
+    if (seqused_q) return fail(ATTN_ENOTSUP, "seqused_q is not supported on the decode path (sq*Hq/Hkv <= 16)");
+    const int split = plan_split_tokens(p, B, Hkv, sk);
+    const int nsp = n_splits_for(split, sk);
+    const int m_rows = sq * ratio;
+    const size_t need = decode_ws_bytes(B, Hkv, nsp, m_rows, d);
+    if (!workspace || workspace_bytes < need)
+      return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    TRY(check_ptr("workspace", workspace));
+    attn::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
+    a.k_sb = k_stride[0]; a.k_sh = k_stride[1]; a.k_sr = k_stride[2];
+    a.v_sb = v_stride[0]; a.v_sh = v_stride[1]; a.v_sr = v_stride[2];
+    a.seqlens_k = seqused_k; a.block_table = nullptr; a.bt_stride = 0; a.page_size = 0;
+    a.sk = sk; a.sq = sq; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio; a.m_rows = m_rows;
+    a.split_tokens = split; a.n_splits = nsp;
+    a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+    a.wl = p->window_left; a.wr = p->window_right;
+    const size_t units = (size_t)B * Hkv * nsp * m_rows;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
+    attn::CombineArgs c{};
+    c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
+    c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
+    c.seqlens_k = seqused_k; c.sk = sk;
+    c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
+    c.split_tokens = split; c.n_splits = nsp; c.o_mul = 1.0f;
+    return launched(attn::launch_decode(a, c, d, false, B, s));
+  }
+
+  attn::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
+  a.k_sb = k_stride[0]; a.k_sh = k_stride[1]; a.k_sr = k_stride[2];
+  a.v_sb = v_stride[0]; a.v_sh = v_stride[1]; a.v_sr = v_stride[2];
+  a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_sr = o_stride[2];
+  a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
+  a.seqused_q = seqused_q; a.seqused_k = seqused_k;
+  a.sq = sq; a.sk = sk; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
+  a.n_qtiles = (int)(((int64_t)sq * ratio + 127) / 128);
+  a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+  a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
+  a.wl = p->window_left; a.wr = p->window_right;
+  return launched(attn::launch_prefill(a, d, p->in_dtype, false, B, s));
+}
+
+attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
+                              float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n,
+                              int total_q, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
+                              const int64_t q_stride[2], const int64_t k_stride[2], const int64_t v_stride[2],
+                              const int64_t o_stride[2], void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)max_seqlen_k;
+  TRY(check_params(p, d));
+  if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "fp32 inputs are supported in batch mode only");
+  if (n < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0)
+    return fail(ATTN_EINVAL, "bad sizes n=%d total_q=%d max_q=%d max_k=%d Hq=%d Hkv=%d", n, total_q, max_seqlen_q,
+                max_seqlen_k, Hq, Hkv);
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_EINVAL, "cu_seqlens_q / cu_seqlens_k is NULL");
+  const int eb = elem_bytes(p->in_dtype), ob = elem_bytes(p->out_dtype);
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("k", k));
+  TRY(check_ptr("v", v));
+  TRY(check_ptr("o", o));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
+  TRY(check_strides("q", q_stride, 2, eb));
+  TRY(check_strides("k", k_stride, 2, eb));
+  TRY(check_strides("v", v_stride, 2, eb));
+  TRY(check_strides("o", o_stride, 2, ob));
+  if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
+  float c_exp2, pre, post;
+  logit_consts(p, &c_exp2, &pre, &post);
+  const int ratio = Hq / Hkv;
+  attn::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.q_sb = 0; a.q_sh = q_stride[1]; a.q_sr = q_stride[0];
+  a.k_sb = 0; a.k_sh = k_stride[1]; a.k_sr = k_stride[0];
+  a.v_sb = 0; a.v_sh = v_stride[1]; a.v_sr = v_stride[0];
+  a.o_sb = 0; a.o_sh = o_stride[1]; a.o_sr = o_stride[0];
+  a.lse_sb = 0; a.lse_sh = total_q;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
+  a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + 127) / 128);
+  a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+  a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
+  a.wl = p->window_left; a.wr = p->window_right;
+  return launched(attn::launch_prefill(a, d, p->in_dtype, true, n, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* k_pool, const void* v_pool, void* o,
+                             float* lse, const int32_t* block_table, int block_table_stride,
+                             const int32_t* seqlens_k, int B, int sq, int Hq, int Hkv, int d, int page_size,
+                             int num_pages, const int64_t q_stride[3], const int64_t kv_stride[3],
+                             const int64_t o_stride[3], void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_params(p, d));
+  if (B < 0 || sq < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
+    return fail(ATTN_EINVAL, "bad sizes B=%d sq=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", B, sq, Hq, Hkv,
+                block_table_stride, num_pages);
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  if (page_size <= 0 || page_size % 32) return fail(ATTN_ENOTSUP, "page_size %d is not a positive multiple of 32", page_size);
+  if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "paged KV supports bf16 only");
+  const int ratio = Hq / Hkv;
+  if (!takes_decode_path(p->in_dtype, sq, ratio))
+    return fail(ATTN_ENOTSUP, "paged KV needs sq*Hq/Hkv <= 16 (got %d)", sq * ratio);
+  if (!block_table || !seqlens_k) return fail(ATTN_EINVAL, "block_table / seqlens_k is NULL");
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("k_pool", k_pool));
+  TRY(check_ptr("v_pool", v_pool));
+  TRY(check_ptr("o", o));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
+  TRY(check_strides("q", q_stride, 3, 2));
+  TRY(check_strides("kv", kv_stride, 3, 2));
+  TRY(check_strides("o", o_stride, 3, 2));
+  if (B == 0 || sq == 0) return ATTN_OK;
+  const int64_t max_len64 = (int64_t)block_table_stride * page_size;
+  if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
+  const int max_len = (int)max_len64;
+  const int split = plan_split_tokens(p, B, Hkv, max_len);
+  const int nsp = n_splits_for(split, max_len);
+  const int m_rows = sq * ratio;
+  const size_t need = decode_ws_bytes(B, Hkv, nsp, m_rows, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  TRY(check_ptr("workspace", workspace));
+  float c_exp2, pre, post;
+  logit_consts(p, &c_exp2, &pre, &post);
+  attn::DecodeArgs a{};
+  a.q = q; a.k = k_pool; a.v = v_pool;
+  a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
+  a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
+  a.v_sb = kv_stride[0]; a.v_sh = kv_stride[1]; a.v_sr = kv_stride[2];
+  a.seqlens_k = seqlens_k; a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
+  a.sk = max_len; a.sq = sq; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio; a.m_rows = m_rows;
+  a.split_tokens = split; a.n_splits = nsp;
+  a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+  a.wl = p->window_left; a.wr = p->window_right;
+  const size_t units = (size_t)B * Hkv * nsp * m_rows;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
+  attn::CombineArgs c{};
+  c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
+  c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
+  c.seqlens_k = seqlens_k; c.sk = max_len;
+  c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
+  c.split_tokens = split; c.n_splits = nsp; c.o_mul = 1.0f;
+  return launched(attn::launch_decode(a, c, d, true, B, (hipStream_t)stream));
+}
+
+}  // extern "C"

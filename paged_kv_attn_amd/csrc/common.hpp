@@ -1,0 +1,120 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Operand layouts of the matrix-core instructions used here (wave64; lane l):
+//   v_mfma_f32_32x32x16_bf16 / _fp8_fp8:  A[i][k] in lane (i + 32*(k/8)), slot k%8;
+//       B[k][j] in lane (j + 32*(k/8)), slot k%8;
+//       C[i][j] in lane (j + 32*((i/4)%2)), register 4*(i/8) + i%4.
+//   v_mfma_f32_16x16x32_bf16:  A[i][k] in lane (i + 16*(k/8)), slot k%8;
+//       B[k][j] in lane (j + 16*(k/8)), slot k%8;
+//       C[i][j] in lane (j + 16*(i/4)), register i%4.
+//   ds_read_b64_tr_b16 (per group of 16 lanes): lane L supplies an 8-byte LDS
+//       address holding 4 16-bit values x_L[0..3]; lane l receives
+//       { x_{4j + l/4}[l%4] : j = 0..3 }.
+// These were checked on the hardware with in-bounds probes before use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+struct alignas(16) U128 { uint32_t x, y, z, w; };
+struct alignas(8) U64 { uint32_t x, y; };
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const U128& u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const U64& a, const U64& b) {
+  U128 u{a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_fp8(const U64& a, const U64& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
+                                                    c, 0, 0, 0);
+}
+
+// 4 bf16 values of one LDS transpose read (see the layout note above).
+__device__ __forceinline__ U64 lds_read_tr16(const void* lds_addr) {
+  auto p = (lds_s16x4*)(lds_addr);
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  return __builtin_bit_cast(U64, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Value from the lane 32 places away, combined with this lane's by max / sum.
+// v_permlane32_swap swaps the upper half of its first operand with the lower
+// half of its second; swapping x with itself hands each lane (r0, r1) =
+// (x[l mod 32], x[l mod 32 + 32]), i.e. both halves' values in every lane.
+__device__ __forceinline__ float max_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Round-to-nearest-even pack of two floats into bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// OCP E4M3FN byte -> float (hardware decode; exact).
+__device__ __forceinline__ float fp8_to_f32(uint32_t packed, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 3);
+  }
+}
+
+// 8 fp8 bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
+__device__ __forceinline__ U128 fp8x8_to_bf16x8(U64 in) {
+  U128 r;
+  uint32_t* o = &r.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w = h ? in.y : in.x;
+    float f0 = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    float f1 = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    float f2 = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    float f3 = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+    // exact values: truncating the fp32 bits to their upper half is exact
+    o[2 * h + 0] = (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xFFFF0000u);
+    o[2 * h + 1] = (__builtin_bit_cast(uint32_t, f2) >> 16) | (__builtin_bit_cast(uint32_t, f3) & 0xFFFF0000u);
+  }
+  return r;
+}
+
+// tanh for the logit soft-cap, from exp: tanh(x) = sign(x) (1 - e) / (1 + e),
+// e = exp(-2|x|). Relative error a few ulp of fp32 away from 0; near 0 the
+// absolute error is ~1e-7, far below the bf16 rounding of P.
+__device__ __forceinline__ float tanh_fast(float x) {
+  float ax = fabsf(x);
+  float e = fast_exp2(-2.0f * kLog2e * ax);
+  float t = (1.0f - e) * fast_rcp(1.0f + e);
+  return copysignf(t, x);
+}
+
+}  // namespace attn

@@ -1,0 +1,137 @@
+// fp32 attention forward (batch mode), for small problems where fp32 inputs
+// and an fp32 result are wanted (the FP32 data type of the Composable Kernel
+// page "fmha_fwd_pagedkv_kernel.hpp Source File").
+//
+// Vector-ALU kernel: each query row is owned by D/64 lanes (64 d-values each),
+// holding its q slice and O accumulator in registers. K/V tiles of 32 keys are
+// staged in LDS with 128-bit loads and read back as broadcasts (every lane of
+// a row group reads the same key row). Per tile: the 32 logits, soft-cap and
+// mask, tile max, one rescale of O and l by alpha = exp(m_old - m_new), then
+// O += p_j V_j (the FlashAttention-2 loop of the CUDA-Learn-Notes page
+// "flash_attn_mma_share_kv_F32F16F16F32.cu", without matrix cores).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kThreads = 128;
+constexpr int kTileN = 32;
+
+template <int D, bool MASK, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
+  constexpr int LPR = D / 64;              // lanes per query row
+  constexpr int ROWS = kThreads / LPR;     // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) float ks[kTileN * D];
+  __shared__ __attribute__((aligned(16))) float vs[kTileN * D];
+
+  const int tid = threadIdx.x;
+  const int part = tid % LPR;
+  const int bh = blockIdx.y;
+  const int b = bh / a.hq, hq = bh % a.hq;
+  const int g = hq / a.ratio;
+  const int Lq = a.seqused_q ? a.seqused_q[b] : a.sq;
+  const int Lk = a.seqused_k ? a.seqused_k[b] : a.sk;
+  const int r0 = blockIdx.x * ROWS;
+  if (r0 >= Lq) return;
+  const int row = r0 + tid / LPR;
+  const bool row_ok = row < Lq;
+  const int off = Lk - Lq;
+  const int rmax = min(r0 + ROWS, Lq) - 1;
+  int j_lo = 0, j_hi = Lk;
+  int lim_lo = 0, lim_hi = Lk - 1;
+  if (MASK) {
+    if (a.wl >= 0) { j_lo = max(0, r0 + off - a.wl); lim_lo = row + off - a.wl; }
+    if (a.wr >= 0) { j_hi = min(Lk, rmax + off + a.wr + 1); lim_hi = min(Lk - 1, row + off + a.wr); }
+  }
+
+  float q[64], o[64];
+  const float* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_sr + part * 64;
+#pragma unroll
+  for (int c = 0; c < 64; ++c) {
+    q[c] = row_ok ? qp[c] : 0.0f;
+    o[c] = 0.0f;
+  }
+  const float* kg = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
+  const float* vg = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
+  const float c2 = a.c_exp2;
+  float m_run = kNegInf, l_run = 0.0f;
+
+  for (int j0 = (j_lo / kTileN) * kTileN; j0 < j_hi; j0 += kTileN) {
+    __syncthreads();
+    for (int e = tid; e < kTileN * D / 4; e += kThreads) {
+      const int r = e / (D / 4), cc = (e % (D / 4)) * 4;
+      const int key = j0 + r;
+      f32x4 kv = {}, vv = {};
+      if (key < Lk) {
+        kv = *(const f32x4*)(kg + (int64_t)key * a.k_sr + cc);
+        vv = *(const f32x4*)(vg + (int64_t)key * a.v_sr + cc);
+      }
+      *(f32x4*)(ks + r * D + cc) = kv;
+      *(f32x4*)(vs + r * D + cc) = vv;
+    }
+    __syncthreads();
+    float s[kTileN];
+    float mt = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kTileN; ++j) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 64; ++c) dot = __builtin_fmaf(q[c], ks[j * D + part * 64 + c], dot);
+      if (LPR == 2) dot += __shfl_xor(dot, 1);
+      float x = SOFTCAP ? a.softcap_post * tanh_fast(dot * a.softcap_pre) : dot;
+      const int key = j0 + j;
+      x = (key >= lim_lo && key <= lim_hi) ? x : kNegInf;
+      s[j] = x;
+      mt = fmaxf(mt, x);
+    }
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * c2);
+    l_run *= alpha;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) o[c] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < kTileN; ++j) {
+      const float p = fast_exp2(__builtin_fmaf(s[j], c2, -m_use * c2));
+      l_run += p;
+#pragma unroll
+      for (int c = 0; c < 64; ++c) o[c] = __builtin_fmaf(p, vs[j * D + part * 64 + c], o[c]);
+    }
+  }
+
+  if (!row_ok) return;
+  const bool empty = !(l_run > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / l_run;
+  float* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)row * a.o_sr + part * 64;
+#pragma unroll
+  for (int c = 0; c < 64; c += 4) *(f32x4*)(op + c) = f32x4{o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
+  if (a.lse && part == 0)
+    a.lse[((int64_t)b * a.hq + hq) * a.sq + row] = empty ? kNegInf : (m_run * c2 + __builtin_log2f(l_run)) * kLn2;
+}
+
+template <int D, bool MASK, bool SOFTCAP>
+hipError_t launch_t(const F32Args& a, hipStream_t s) {
+  constexpr int ROWS = kThreads / (D / 64);
+  dim3 grid((a.sq + ROWS - 1) / ROWS, a.B * a.hq);
+  hipLaunchKernelGGL((f32_kernel<D, MASK, SOFTCAP>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const F32Args& a, bool mask, bool softcap, hipStream_t s) {
+  if (mask) return softcap ? launch_t<D, true, true>(a, s) : launch_t<D, true, false>(a, s);
+  return softcap ? launch_t<D, false, true>(a, s) : launch_t<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_f32(const F32Args& a, int d, hipStream_t s) {
+  const bool mask = a.wl >= 0 || a.wr >= 0;
+  const bool softcap = a.softcap_pre != 0.0f;
+  if (a.B <= 0 || a.hq <= 0 || a.sq <= 0) return hipSuccess;
+  return d == 128 ? launch_d<128>(a, mask, softcap, s) : launch_d<64>(a, mask, softcap, s);
+}
+
+}  // namespace attn

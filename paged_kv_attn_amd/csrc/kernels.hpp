@@ -1,0 +1,97 @@
+// Launch-side view of the attention kernels: argument blocks and launchers.
+// Host code (api.cpp) fills these after validating the C-ABI arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum InType : int { kInF32 = 0, kInBF16 = 1, kInFP8 = 2 };
+
+// Prefill (one workgroup = 128 packed query rows of one sequence and kv-head).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                 // nullable
+  // element strides: batch (0 in varlen mode), head, row/token
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int64_t lse_sb, lse_sh;     // lse index = b*lse_sb + h*lse_sh + token
+  const int32_t* seqused_q;   // batch mode, nullable
+  const int32_t* seqused_k;   // batch mode, nullable
+  const int32_t* cu_q;        // varlen mode (non-null selects varlen)
+  const int32_t* cu_k;
+  int sq, sk;                 // batch-mode extents
+  int hq, hkv, ratio;
+  int n_qtiles;               // grid x extent (packed-row tiles)
+  float c_exp2;               // multiplier taking the kernel's logit domain to log2 units
+  float softcap_pre;          // softcap: raw dot * softcap_pre = (scaled logit) / cap
+  float softcap_post;         // softcap: cap * log2(e)
+  float o_mul;                // value descale applied to O (1 unless FP8)
+  int wl, wr;                 // window (-1 = unbounded)
+};
+
+// Split-KV decode (one workgroup = one split of one request and kv-head).
+struct DecodeArgs {
+  const void* q;
+  const void* k;              // contiguous K, or the page pool
+  const void* v;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;   // contiguous: batch, head, row. paged: page, head, slot
+  int64_t v_sb, v_sh, v_sr;
+  const int32_t* seqlens_k;   // per-request Lk (paged: required; contiguous: nullable)
+  const int32_t* block_table; // paged only
+  int64_t bt_stride;
+  int page_size;
+  int sk;                     // contiguous: Lk when seqlens_k is null
+  int sq, hq, hkv, ratio, m_rows;  // m_rows = sq * ratio (<= 16)
+  int split_tokens, n_splits;
+  float c_exp2;
+  float softcap_pre, softcap_post;
+  int wl, wr;
+  float* part_o;              // [B][hkv][n_splits][m_rows][d] fp32
+  float* part_lse;            // [B][hkv][n_splits][m_rows]
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;                 // nullable, [B, hq, sq]
+  int64_t o_sb, o_sh, o_sr;
+  const int32_t* seqlens_k;   // nullable (then sk)
+  int sk;
+  int B, sq, hq, hkv, ratio, m_rows, split_tokens, n_splits;
+  float o_mul;
+};
+
+// fp32 path (batch mode).
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  const int32_t* seqused_q;
+  const int32_t* seqused_k;
+  int B, sq, sk, hq, hkv, ratio;
+  float c_exp2, softcap_pre, softcap_post;
+  int wl, wr;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, bool varlen, int batch_or_seqs,
+                          hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, bool paged, int B,
+                         hipStream_t stream);
+hipError_t launch_f32(const F32Args& a, int d, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,186 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol declared in
+include/attn.h, and rejects invalid arguments with the documented status
+before any launch (fake but aligned device pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+from paged_kv_attn_amd import _lib  # noqa: E402
+from paged_kv_attn_amd._lib import AttnParams, i64_array, lib  # noqa: E402
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: every call below fails validation
+MISALIGNED = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"attn_fwd", "attn_fwd_varlen", "attn_fwd_paged", "attn_workspace_bytes", "attn_last_error"} <= set(names)
+    handle = lib()
+    for n in names:
+        assert hasattr(handle, n), f"{n} declared in attn.h but not exported"
+
+
+def test_params_struct_layout_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} attn_params_t;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(int|float)\s+([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)\s*;", body)
+    names = [n.strip() for _, group in fields for n in group.split(",")]
+    assert names == [f for f, _ in AttnParams._fields_]
+
+
+def _params(**kw):
+    p = AttnParams()
+    lib().attn_params_init(ctypes.byref(p), 0.125)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _fwd(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, Hq=2, Hkv=2, sq=64, sk=64, d=128, strides=None, ws=NULL, wsb=0):
+    st = strides or [2 * 64 * 128, 64 * 128, 128]
+    return lib().attn_fwd(ctypes.byref(p), q, k, v, o, NULL, B, Hq, Hkv, sq, sk, d, i64_array(st), i64_array(st),
+                          i64_array(st), i64_array(st), NULL, NULL, ws, wsb, NULL)
+
+
+def _err():
+    return lib().attn_last_error().decode()
+
+
+def test_params_init_defaults():
+    p = _params()
+    assert (p.in_dtype, p.out_dtype, p.window_left, p.window_right, p.kv_split_tokens) == (1, 1, -1, -1, 0)
+    assert p.q_descale == 1.0 and p.softcap == 0.0 and abs(p.scale - 0.125) < 1e-9
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=96), 2, "head dim"),
+    (dict(Hq=3, Hkv=2), 1, "multiple"),
+    (dict(Hkv=0), 1, "bad sizes"),
+    (dict(sq=-1), 1, "bad sizes"),
+    (dict(q=NULL), 1, "q is NULL"),
+    (dict(k=MISALIGNED), 1, "aligned"),
+    (dict(strides=[2 * 64 * 128, 64 * 128, 100]), 1, "16 bytes"),
+    (dict(strides=[-1, 64 * 128, 128]), 1, "negative"),
+])
+def test_attn_fwd_rejects_bad_arguments(kw, status, msg):
+    p = _params()
+    assert _fwd(p, **kw) == status
+    assert msg in _err()
+
+
+@pytest.mark.parametrize("field,value,status,msg", [
+    ("in_dtype", 7, 2, "unsupported"),
+    ("out_dtype", 0, 2, "unsupported"),
+    ("scale", 0.0, 1, "scale"),
+    ("scale", float("inf"), 1, "scale"),
+    ("softcap", float("nan"), 1, "softcap"),
+    ("window_left", -2, 1, "window"),
+    ("kv_split_tokens", 100, 1, "multiple of 64"),
+])
+def test_params_validation(field, value, status, msg):
+    p = _params(**{field: value})
+    assert _fwd(p) == status
+    assert msg in _err()
+
+
+def test_fp8_descale_validation():
+    p = _params(in_dtype=_lib.ATTN_FP8_E4M3, out_dtype=_lib.ATTN_BF16, k_descale=0.0)
+    assert _fwd(p) == 1 and "descale" in _err()
+
+
+def test_decode_path_needs_workspace():
+    p = _params()
+    need = lib().attn_workspace_bytes(ctypes.byref(p), 4, 32, 8, 1, 128, 4096)
+    assert need > 0
+    st = [32 * 128, 128, 128]
+    kst = [8 * 4096 * 128, 4096 * 128, 128]
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
+                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, NULL, 0, NULL)
+    assert r == 3 and "workspace" in _err()
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
+                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, need - 1, NULL)
+    assert r == 3
+
+
+def test_workspace_and_split_queries():
+    p = _params()
+    assert lib().attn_workspace_bytes(ctypes.byref(p), 4, 16, 16, 2048, 128, 2048) == 0   # prefill path
+    assert lib().attn_num_splits(ctypes.byref(p), 4, 16, 16, 2048, 2048) == 1
+    p.kv_split_tokens = 256
+    assert lib().attn_num_splits(ctypes.byref(p), 64, 32, 8, 1, 32768) == 128
+    ws = lib().attn_workspace_bytes(ctypes.byref(p), 64, 32, 8, 1, 128, 32768)
+    units = 64 * 8 * 128 * 4
+    assert ws >= units * 129 * 4
+    assert lib().attn_workspace_bytes(ctypes.byref(p), 1, 3, 2, 1, 128, 100) == 0       # invalid ratio
+
+
+def _paged(p, page=64, sq=1, Hq=8, Hkv=2, table=FAKE, lens=FAKE, ws=FAKE, wsb=1 << 30, d=128, num_pages=10):
+    st = [Hq * sq * 128, sq * 128, 128]
+    kv = [page * Hkv * 128, 128, Hkv * 128]
+    return lib().attn_fwd_paged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, table, 16, lens, 2, sq, Hq, Hkv, d,
+                                page, num_pages, i64_array(st), i64_array(kv), i64_array(st), ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(page=48), 2, "page_size"),
+    (dict(sq=8), 2, "sq*Hq/Hkv"),
+    (dict(table=NULL), 1, "block_table"),
+    (dict(lens=NULL), 1, "seqlens_k"),
+    (dict(ws=NULL), 3, "workspace"),
+    (dict(wsb=1024), 3, "workspace"),
+    (dict(num_pages=0), 1, "bad sizes"),
+])
+def test_attn_fwd_paged_rejects_bad_arguments(kw, status, msg):
+    p = _params()
+    assert _paged(p, **kw) == status
+    assert msg in _err()
+
+
+def test_paged_rejects_non_bf16():
+    p = _params(in_dtype=_lib.ATTN_FP8_E4M3, out_dtype=_lib.ATTN_BF16)
+    assert _paged(p) == 2
+
+
+def test_varlen_rejects_bad_arguments():
+    p = _params()
+    st = [2 * 128, 128]
+    r = lib().attn_fwd_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, 2, 10, 5, 5, 2, 2, 128,
+                              i64_array(st), i64_array(st), i64_array(st), i64_array(st), NULL, 0, NULL)
+    assert r == 1 and "cu_seqlens" in _err()
+    p32 = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)
+    r = lib().attn_fwd_varlen(ctypes.byref(p32), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 2, 10, 5, 5, 2, 2, 128,
+                              i64_array(st), i64_array(st), i64_array(st), i64_array(st), NULL, 0, NULL)
+    assert r == 2
+
+
+def test_empty_problems_return_ok_without_launch():
+    p = _params()
+    assert _fwd(p, B=0) == 0
+    assert _fwd(p, sq=0) == 0
+
+
+def test_product_path_has_no_oracle_dependency():
+    import ast
+    pkg = os.path.join(ROOT, "paged_kv_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                tree = ast.parse(open(os.path.join(dirpath, f)).read())
+                for node in ast.walk(tree):
+                    if isinstance(node, (ast.Import, ast.ImportFrom)):
+                        mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+                        assert not any(m.split(".")[0] in ("oracle", "tests", "synth") for m in mods), (f, mods)

@@ -1,0 +1,156 @@
+"""GPU parity of the prefill paths (batch and varlen, bf16 / fp8 / fp32) against
+the fp64 oracle, plus the bit-exact cross-mode checks. Shapes span several
+128-row query tiles and 64-key tiles and end on ragged tails."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import _cases as C
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dense(*args, **kw):
+    kw.setdefault("device", DEV)
+    return synth.dense_case(*args, **kw)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,sq,sk,d,causal", [
+    (2, 4, 4, 333, 333, 128, True),
+    (2, 4, 4, 333, 333, 128, False),
+    (1, 2, 2, 130, 257, 64, True),
+    (1, 8, 2, 200, 450, 128, True),      # GQA, sk > sq (bottom-right)
+    (1, 4, 1, 450, 200, 128, True),      # sq > sk: leading rows see nothing
+    (3, 2, 2, 1000, 1000, 128, True),
+    (1, 16, 16, 64, 64, 128, True),
+])
+def test_bf16_batch_parity(B, Hq, Hkv, sq, sk, d, causal):
+    case = _dense(B, Hq, Hkv, sq, sk, d, "bf16", seed=sq + sk + Hq, causal=causal)
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "bf16", f"bf16 {B}x{Hq}/{Hkv}x{sq}x{sk}x{d} causal={causal}")
+
+
+@pytest.mark.parametrize("window,softcap", [((50, 10), 0.0), ((0, 0), 0.0), ((-1, 37), 0.0), ((100, -1), 0.0),
+                                            ((-1, 0), 30.0), ((-1, -1), 5.0)])
+def test_bf16_window_and_softcap(window, softcap):
+    case = _dense(2, 4, 2, 300, 280, 128, "bf16", seed=11, window=window, softcap=softcap, scale=0.3)
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "bf16", f"window={window} softcap={softcap}")
+
+
+def test_bf16_seqused_poisoned_tails_and_untouched_rows():
+    su_q, su_k = [300, 1, 0, 129], [250, 300, 17, 0]
+    case = _dense(4, 4, 2, 300, 300, 128, "bf16", seed=5, causal=True, seqused_q=su_q, seqused_k=su_k)
+    sentinel = torch.full((4, 4, 300, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    lse_s = torch.full((4, 4, 300), 7.0, dtype=torch.float32, device=DEV)
+    out, lse = C.run_dense(case, out=sentinel, lse=lse_s)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "bf16", "seqused")
+    for b, lq in enumerate(su_q):
+        assert (out[b, :, lq:] == 7.0).all() and (lse[b, :, lq:] == 7.0).all(), "rows >= Lq were written"
+    # Lk = 0: every valid row is empty -> O = 0, LSE = -inf
+    assert (out[3, :, :129] == 0).all() and torch.isneginf(lse[3, :, :129]).all()
+
+
+def test_bf16_strided_inputs():
+    case = _dense(2, 4, 4, 200, 200, 128, "bf16", seed=3, causal=True)
+    # BSHD views of the same data: strides differ from BHSD, values identical
+    q = case.t["q"].transpose(1, 2).contiguous().transpose(1, 2)
+    k = case.t["k"].transpose(1, 2).contiguous().transpose(1, 2)
+    v = case.t["v"].transpose(1, 2).contiguous().transpose(1, 2)
+    out_ref, lse_ref = C.run_dense(case)
+    import paged_kv_attn_amd as pk
+    out, lse = pk.attn_fwd(q, k, v, scale=case.scale, causal=True)
+    assert torch.equal(C.bits(out), C.bits(out_ref)) and torch.equal(C.bits(lse), C.bits(lse_ref))
+
+
+def test_fp8_softcap_causal_parity():
+    case = _dense(1, 4, 4, 520, 520, 128, "fp8", seed=21, causal=True, softcap=30.0)
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "fp8", "fp8 softcap causal")
+
+
+def test_fp8_gqa_varlen_parity():
+    case = synth.varlen_case([130, 7, 400], [130, 7, 400], 8, 2, 128, "fp8", seed=22, causal=True, softcap=30.0,
+                             device=DEV)
+    out, lse = C.run_varlen(case)
+    O, LSE = C.oracle_varlen(case)
+    C.assert_parity(out, lse.T, O, LSE.T, "fp8", "fp8 varlen")
+
+
+@pytest.mark.parametrize("B,H,s,d,causal,hkv", [(1, 2, 128, 64, False, 2), (2, 4, 77, 128, True, 2),
+                                                 (1, 2, 300, 64, True, 1)])
+def test_f32_parity(B, H, s, d, causal, hkv):
+    case = _dense(B, H, hkv, s, s, d, "f32", seed=s + d, causal=causal)
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "f32", f"f32 {B}x{H}x{s}x{d}")
+
+
+def test_f32_softcap_window_seqused():
+    case = _dense(2, 2, 2, 150, 170, 64, "f32", seed=9, window=(40, 5), softcap=3.0, seqused_q=[150, 60],
+                  seqused_k=[170, 90])
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "f32", "f32 window softcap seqused")
+
+
+def test_varlen_parity_with_empty_and_ragged_sequences():
+    lens_q = [1, 77, 300, 0, 129, 513]
+    lens_k = [1, 77, 300, 0, 129, 513]
+    case = synth.varlen_case(lens_q, lens_k, 8, 2, 128, "bf16", seed=31, causal=True, device=DEV)
+    out, lse = C.run_varlen(case)
+    O, LSE = C.oracle_varlen(case)
+    C.assert_parity(out, lse.T, O, LSE.T, "bf16", "varlen")
+
+
+def test_varlen_bitexact_vs_padded_batch_and_per_sequence():
+    lens = [1, 77, 300, 129, 513]
+    Hq, Hkv, d = 8, 2, 128
+    case = synth.varlen_case(lens, lens, Hq, Hkv, d, "bf16", seed=32, causal=True, device=DEV)
+    out_v, lse_v = C.run_varlen(case)
+    cu = case.t["cu_seqlens_q"].cpu().numpy()
+    n, smax = len(lens), max(lens)
+    qp = torch.full((n, Hq, smax, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kp = torch.full((n, Hkv, smax, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vp = torch.full((n, Hkv, smax, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for s in range(n):
+        a, b = int(cu[s]), int(cu[s + 1])
+        qp[s, :, :b - a] = case.t["q"][a:b].transpose(0, 1)
+        kp[s, :, :b - a] = case.t["k"][a:b].transpose(0, 1)
+        vp[s, :, :b - a] = case.t["v"][a:b].transpose(0, 1)
+    import paged_kv_attn_amd as pk
+    used = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out_b, lse_b = pk.attn_fwd(qp, kp, vp, scale=case.scale, causal=True, seqused_q=used, seqused_k=used)
+    for s in range(n):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        ref_o = out_v[a:b].transpose(0, 1)
+        assert torch.equal(C.bits(out_b[s, :, :L]), C.bits(ref_o)), f"padded batch differs on seq {s}"
+        assert torch.equal(C.bits(lse_b[s, :, :L]), C.bits(lse_v[:, a:b])), f"padded LSE differs on seq {s}"
+        if L * (Hq // Hkv) <= 16:
+            continue  # a B = 1 call this short takes the decode path (a different kernel)
+        o1, l1 = pk.attn_fwd(qp[s:s + 1, :, :L], kp[s:s + 1, :, :L], vp[s:s + 1, :, :L], scale=case.scale,
+                             causal=True)
+        assert torch.equal(C.bits(o1[0]), C.bits(ref_o)), f"per-sequence call differs on seq {s}"
+        assert torch.equal(C.bits(l1[0]), C.bits(lse_v[:, a:b])), f"per-sequence LSE differs on seq {s}"
+
+
+def test_prefill_deterministic():
+    case = _dense(2, 8, 2, 700, 700, 128, "bf16", seed=41, causal=True)
+    o1, l1 = C.run_dense(case)
+    o2, l2 = C.run_dense(case)
+    assert torch.equal(C.bits(o1), C.bits(o2)) and torch.equal(C.bits(l1), C.bits(l2))
+
+
+def test_lse_optional():
+    case = _dense(1, 2, 2, 100, 100, 128, "bf16", seed=42, causal=True)
+    o1, _ = C.run_dense(case)
+    o2, l2 = C.run_dense(case, return_lse=False)
+    assert l2 is None and torch.equal(C.bits(o1), C.bits(o2))
