@@ -73,20 +73,43 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// Round-to-nearest-even pack of two floats into bf16x2 (low half = a).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even pack of two floats into bf16x2 (low half = a); one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
-// OCP E4M3FN byte -> float (hardware decode; exact).
-__device__ __forceinline__ float fp8_to_f32(uint32_t packed, int sel) {
-  switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 0);
-    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 1);
-    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 2);
-    default: return __builtin_amdgcn_cvt_f32_fp8((int)packed, 3);
-  }
+// Index of this thread's wave in the workgroup, as a scalar (wave-uniform)
+// value so that everything derived from it stays in scalar registers and
+// branches on it stay uniform.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Raw buffer resource over [base, base + bytes): 128-bit loads at byte offsets
+// at or beyond `bytes` return zeros (hardware range check), which zero-fills
+// tile rows past a sequence's end without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// lds_wave_base + 16 l (one contiguous 1 KiB block per wave instruction); bytes
+// outside the buffer's range arrive as zeros. Tracked by vmcnt.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, byte_off,
+                                           0, 0, 0);
+}
+
+// Wait until this wave's vector-memory loads (including loads into LDS) have
+// completed: s_waitcnt vmcnt(0) with the LDS and export counters left free.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return __builtin_bit_cast(U128, v);
 }
 
 // 8 fp8 bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).

@@ -20,12 +20,22 @@
 // each lane again owns one output row, so the rescale by
 // alpha = exp(m_old - m_new) is a per-lane scalar multiply.
 //
-// K and V tiles are double-buffered in LDS; the next tile's global loads
-// (128-bit, coalesced along d) are issued before the current tile's math.
+// K and V tiles travel from HBM straight into LDS (buffer_load_dwordx4 ... lds,
+// 128-bit per lane, coalesced along d; rows past the sequence end arrive as
+// zeros from the buffer range check), K two tiles ahead and V one tile ahead,
+// so no registers are spent on staging. Within LDS each 16-byte chunk of a row
+// is XOR-swizzled by the row index, which keeps the K operand reads and the V
+// transpose reads free of bank conflicts. The loop is software-pipelined: the
+// scores of tile t+1 are computed on the matrix cores while the softmax of
+// tile t runs on the vector ALUs.
 // Softmax runs in the exp2 domain with scale * log2(e) folded into one FMA
 // (the FAST_EXP2 folding of the Composable Kernel page's MakeKargs).
 #include "common.hpp"
 #include "kernels.hpp"
+
+#ifndef ATTN_PREFILL_PIPELINED
+#define ATTN_PREFILL_PIPELINED 0
+#endif
 
 namespace attn {
 namespace {
@@ -39,17 +49,30 @@ struct Traits {
   static constexpr int kElem = FP8 ? 1 : 2;              // stored bytes per Q/K/V element
   static constexpr int kQkSteps = D / 16;                // k-steps of S^T = K Q^T
   static constexpr int kDBlocks = D / 32;                // 32-row blocks of O^T
-  static constexpr int kKPitch = D * kElem + 16;         // bytes per K row in LDS
-  static constexpr int kVPitch = 160;                    // bf16 elements per V row in LDS (80 dwords)
-  static constexpr int kKTile = kBlockN * kKPitch;
-  static constexpr int kVTile = kBlockN * kVPitch * 2;
-  static constexpr int kBuf = kKTile + kVTile;
-  static constexpr int kChunks = D * kElem / 16;         // 16-byte chunks per K/V row
-  static constexpr int kLoads = kBlockN * kChunks / kThreads;
-  static constexpr int kRowStep = kThreads / kChunks;
-  static_assert(kLoads >= 1 && kBlockN * kChunks == kLoads * kThreads, "tile/threads mismatch");
-  static_assert(D <= 128, "V pitch assumes d <= 128");
+  static constexpr int kKRow = D * kElem;                // bytes per K row in LDS (no padding)
+  static constexpr int kKCh = kKRow / 16;                // 16-byte chunks per K row
+  static constexpr int kVRow = D * 2;                    // bytes per V row in LDS (bf16)
+  static constexpr int kVCh = kVRow / 16;
+  static constexpr int kKTile = kBlockN * kKRow;
+  static constexpr int kVTile = kBlockN * kVRow;
+  static constexpr int kKInstr = kKTile / 1024 / 4;      // direct-to-LDS instructions per wave per K tile
+  static constexpr int kVInstr = kVTile / 1024 / 4;
+  static constexpr int kSmem = 2 * kKTile + 2 * kVTile;
+  // fp8 V goes through registers (to widen to bf16): 16-byte fp8 chunks per thread
+  static constexpr int kV8Ch = D / 16;
+  static constexpr int kV8Loads = kBlockN * kV8Ch / kThreads;
+  static_assert(kKInstr >= 1 && kVInstr >= 1, "tile too small for 4 waves");
+  static_assert(!FP8 || kV8Loads >= 1, "fp8 V staging needs >= 1 chunk per thread");
 };
+
+// Chunk swizzle of LDS row R: chunk c of the row is stored in slot c ^ swz(R).
+// swz is a bijection on 0..15 over any 16 consecutive rows (K operand reads)
+// and its top two bits differ across any 4 rows 4m..4m+3 (V transpose reads).
+__device__ __forceinline__ int swz(int row, int nchunks) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (nchunks - 1);
+}
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 template <bool FP8> struct QFrag;
 template <> struct QFrag<false> { using T = U128; };
@@ -59,10 +82,10 @@ template <int D, bool FP8, bool VARLEN, bool MASK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Tr = Traits<D, FP8>;
   using QT = typename QFrag<FP8>::T;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Tr::kBuf];
+  __shared__ __attribute__((aligned(16))) char smem[Tr::kSmem];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int h = lane >> 5;          // which half of the key / d sub-blocks this lane holds
   const int g = blockIdx.y;         // kv-head
   const int z = blockIdx.z;         // batch entry or sequence
@@ -106,13 +129,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int t_begin = j_lo / kBlockN;
   const int t_end = (j_hi > j_lo) ? (j_hi + kBlockN - 1) / kBlockN : t_begin;
 
-  // ---- this lane's query row ----
+  // ---- this lane's query row; the wave's row range (scalar) ----
   const int row = r0 + wave * 32 + (lane & 31);
   const bool row_ok = row < rows_total;
   const int pos = row / ratio;
   const int hq = g * ratio + row % ratio;
   const int wr0 = r0 + wave * 32;
-  const bool wave_active = wr0 < rows_total;
   const int pw_lo = wr0 / ratio;
   const int pw_hi = (min(wr0 + 32, rows_total) - 1) / ratio;
   int lim_lo = 0, lim_hi = Lk - 1;  // visible keys of this row: lim_lo <= j <= lim_hi
@@ -133,127 +155,178 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- K/V staging: thread -> (row, 16-byte chunk) ----
-  const int tid = threadIdx.x;
-  const int ch = tid % Tr::kChunks;
-  const int rb = tid / Tr::kChunks;
-  const char* kg = (const char*)a.k + (k_off + (int64_t)g * a.k_sh) * Tr::kElem + ch * 16;
-  const char* vg = (const char*)a.v + (v_off + (int64_t)g * a.v_sh) * Tr::kElem + ch * 16;
-  U128 kreg[Tr::kLoads], vreg[Tr::kLoads];
-
-  auto load_tile = [&](int t) {
+  // ---- K/V staging: HBM -> LDS directly; rows past Lk arrive as zeros ----
+  const char* kh = (const char*)a.k + (k_off + (int64_t)g * a.k_sh) * Tr::kElem;
+  const char* vh = (const char*)a.v + (v_off + (int64_t)g * a.v_sh) * Tr::kElem;
+  const int64_t krow = a.k_sr * Tr::kElem, vrow = a.v_sr * Tr::kElem;  // global bytes per key row
+  char* const kslot0 = smem;
+  char* const vslot0 = smem + 2 * Tr::kKTile;
+  // Wave w fills LDS blocks w, w+4, ... (1 KiB each) of a tile; lane l of block q
+  // covers LDS bytes 1024 q + 16 l = (row R, slot s), fetching global chunk s ^ swz(R).
+  int koff[Tr::kKInstr], voff[Tr::kVInstr];
+#pragma unroll
+  for (int i = 0; i < Tr::kKInstr; ++i) {
+    const int B = 1024 * (wave + 4 * i) + 16 * lane;
+    const int R = B / Tr::kKRow, sl = (B % Tr::kKRow) / 16;
+    koff[i] = (int)(R * krow) + 16 * (sl ^ swz(R, Tr::kKCh));
+  }
+#pragma unroll
+  for (int i = 0; i < Tr::kVInstr; ++i) {
+    const int B = 1024 * (wave + 4 * i) + 16 * lane;
+    const int R = B / Tr::kVRow, sl = (B % Tr::kVRow) / 16;
+    voff[i] = (int)(R * vrow) + 16 * (sl ^ swz(R, Tr::kVCh));
+  }
+  auto load_k = [&](int t, int slot) {
     const int j0 = t * kBlockN;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + j0 * krow, (uint32_t)(min(kBlockN, Lk - j0) * krow));
+    char* base = kslot0 + slot * Tr::kKTile;
 #pragma unroll
-    for (int i = 0; i < Tr::kLoads; ++i) {
-      const int key = j0 + rb + i * Tr::kRowStep;
-      if (key < Lk) {  // rows past the used length are zero-filled, never read
-        kreg[i] = *(const U128*)(kg + (int64_t)key * a.k_sr * Tr::kElem);
-        vreg[i] = *(const U128*)(vg + (int64_t)key * a.v_sr * Tr::kElem);
-      } else {
-        kreg[i] = U128{0, 0, 0, 0};
-        vreg[i] = U128{0, 0, 0, 0};
-      }
+    for (int i = 0; i < Tr::kKInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), koff[i]);
+  };
+  // fp8 V: through registers, widened to bf16 on the way into LDS
+  U128 v8[FP8 ? Tr::kV8Loads : 1];
+  const int v8ch = threadIdx.x % Tr::kV8Ch, v8row = threadIdx.x / Tr::kV8Ch;
+  auto load_v = [&](int t, int slot) {
+    const int j0 = t * kBlockN;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + j0 * vrow, (uint32_t)(min(kBlockN, Lk - j0) * vrow));
+    if (FP8) {
+#pragma unroll
+      for (int i = 0; i < Tr::kV8Loads; ++i)
+        v8[i] = buf_load16(r, (int)((v8row + i * (kThreads / Tr::kV8Ch)) * vrow) + 16 * v8ch);
+    } else {
+      char* base = vslot0 + slot * Tr::kVTile;
+#pragma unroll
+      for (int i = 0; i < Tr::kVInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), voff[i]);
     }
   };
-  auto store_tile = [&](int buf) {
-    char* kt = smem + buf * Tr::kBuf;
-    char* vt = kt + Tr::kKTile;
+  auto store_v8 = [&](int slot) {  // fp8 only
+    char* base = vslot0 + slot * Tr::kVTile;
 #pragma unroll
-    for (int i = 0; i < Tr::kLoads; ++i) {
-      const int r = rb + i * Tr::kRowStep;
-      *(U128*)(kt + r * Tr::kKPitch + ch * 16) = kreg[i];
-      if (FP8) {
-        // V goes to LDS as bf16 (exact widening of E4M3FN); P V runs on bf16 MFMA.
-        U128 lo = fp8x8_to_bf16x8(U64{vreg[i].x, vreg[i].y});
-        U128 hi = fp8x8_to_bf16x8(U64{vreg[i].z, vreg[i].w});
-        *(U128*)(vt + (r * Tr::kVPitch + ch * 16) * 2) = lo;
-        *(U128*)(vt + (r * Tr::kVPitch + ch * 16 + 8) * 2) = hi;
-      } else {
-        *(U128*)(vt + (r * Tr::kVPitch + ch * 8) * 2) = vreg[i];
-      }
+    for (int i = 0; i < (FP8 ? Tr::kV8Loads : 0); ++i) {
+      const int R = v8row + i * (kThreads / Tr::kV8Ch);
+      const int c0 = 2 * v8ch;  // bf16 chunks 2c, 2c+1 of the row
+      *(U128*)(base + R * Tr::kVRow + 16 * (c0 ^ swz(R, Tr::kVCh))) = fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y});
+      *(U128*)(base + R * Tr::kVRow + 16 * ((c0 + 1) ^ swz(R, Tr::kVCh))) = fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w});
     }
   };
 
-  // lane-constant LDS offsets
-  const int k_lane = (lane & 31) * Tr::kKPitch + 8 * h * Tr::kElem;
+  // lane-constant LDS read offsets. K operand: row lane%32 (+32 for the second
+  // block, same swizzle), chunk (16 kk + 8 h) * elem / 16.
+  const int kR = lane & 31;
+  const int k_swz = swz(kR, Tr::kKCh);
+  auto k_addr = [&](int kk) -> int {
+    const int byte = (16 * kk + 8 * h) * Tr::kElem;
+    return kR * Tr::kKRow + 16 * ((byte >> 4) ^ k_swz) + (byte & 15);
+  };
+  // V transpose read of group (lanes 16 gi .. 16 gi + 15, L = lane & 15): rows
+  // kb + 8 a + 4 (gi >> 1) + L / 4, bf16 columns 32 dblk + 16 (gi & 1) + 4 (L & 3).
   const int L = lane & 15;
-  const int v_lane = ((4 * h + (L >> 2)) * Tr::kVPitch + 16 * ((lane >> 4) & 1) + 4 * (L & 3)) * 2;
+  const int gi = lane >> 4;
+  auto v_addr = [&](int kb, int aa, int dblk) -> int {
+    const int R = kb + 8 * aa + 4 * (gi >> 1) + (L >> 2);
+    const int byte = 2 * (32 * dblk + 16 * (gi & 1) + 4 * (L & 3));
+    return R * Tr::kVRow + 16 * ((byte >> 4) ^ swz(R, Tr::kVCh)) + (byte & 15);
+  };
 
   const float c = a.c_exp2;
-  float m_run = kNegInf;
-  float l_run = 0.0f;
+  float m_run = kNegInf;   // reference max (raised lazily, see below)
+  float l_run = 0.0f;      // this lane's partial row sum (its half of the keys)
   f32x16 acc[Tr::kDBlocks];
 #pragma unroll
   for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] = f32x16{};
 
-  auto compute = [&](int t, int buf) {
-    const char* kt = smem + buf * Tr::kBuf;
-    const char* vt = kt + Tr::kKTile;
+  // S^T = K Q^T for the tile in K slot `slot`: two interleaved 32-key chains
+  auto qk = [&](int slot, f32x16& s0, f32x16& s1) {
+    const char* kt = kslot0 + slot * Tr::kKTile;
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
+      const char* p = kt + k_addr(kk);
+      if (FP8) {
+        s0 = mfma32_fp8(*(const U64*)p, *(const U64*)&qf[kk], s0);
+        s1 = mfma32_fp8(*(const U64*)(p + 32 * Tr::kKRow), *(const U64*)&qf[kk], s1);
+      } else {
+        s0 = mfma32_bf16(as_bf16x8(*(const U128*)p), as_bf16x8(*(const U128*)&qf[kk]), s0);
+        s1 = mfma32_bf16(as_bf16x8(*(const U128*)(p + 32 * Tr::kKRow)), as_bf16x8(*(const U128*)&qf[kk]), s1);
+      }
+    }
+  };
+
+  // Softmax of tile t's scores (s0, s1) into bf16 P, with the lazy rescale of O.
+  // Register r of block b is key j0 + 32b + 8(r/4) + 4h + r%4 of this lane's row.
+  auto softmax = [&](auto masked_tag, int t, f32x16 s0, f32x16 s1, uint32_t (&pk)[2][8]) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int j0 = t * kBlockN;
-
-    // S^T = K Q^T, two 32-key blocks
-    f32x16 s[2];
+    f32x16 s[2] = {s0, s1};
+    if (SOFTCAP) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
-        const char* p = kt + k_lane + 32 * b * Tr::kKPitch + 16 * kk * Tr::kElem;
-        if (FP8) s[b] = mfma32_fp8(*(const U64*)p, *(const U64*)&qf[kk], s[b]);
-        else s[b] = mfma32_bf16(as_bf16x8(*(const U128*)p), as_bf16x8(*(const U128*)&qf[kk]), s[b]);
-      }
+        for (int r = 0; r < 16; ++r) s[b][r] = a.softcap_post * tanh_fast(s[b][r] * a.softcap_pre);
     }
-
-    // logit transform (soft-cap) and mask; register r of block b is key
-    // j0 + 32b + 8(r/4) + 4h + r%4 of this lane's row
-    bool need_mask = j0 + kBlockN > Lk;
-    if (MASK) {
-      if (a.wr >= 0 && j0 + kBlockN - 1 > pw_lo + off + a.wr) need_mask = true;
-      if (a.wl >= 0 && j0 < pw_hi + off - a.wl) need_mask = true;
-    }
-    float mt = kNegInf;
+    if (kMasked) {
+      const int hi = lim_hi - j0 - 4 * h;
+      const int lo = lim_lo - j0 - 4 * h;
+      const bool two_sided = MASK && a.wl >= 0;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[b][r];
-        if (SOFTCAP) x = a.softcap_post * tanh_fast(x * a.softcap_pre);
-        if (need_mask) {
-          const int j = j0 + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-          x = (j >= lim_lo && j <= lim_hi) ? x : kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int jr = 32 * b + 8 * (r >> 2) + (r & 3);
+          const bool vis = (jr <= hi) && (!two_sided || jr >= lo);
+          s[b][r] = vis ? s[b][r] : kNegInf;
         }
-        s[b][r] = x;
-        mt = fmaxf(mt, x);
-      }
     }
-    mt = max_across_halves(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * c);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    // row max: four independent chains (each starting at -inf, which lets the
+    // compiler use v_max3 without NaN canonicalisation), then the lane halves
+    float mx[4];
 #pragma unroll
-      for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] *= alpha;
+    for (int q = 0; q < 4; ++q) {
+      mx[q] = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[q] = __builtin_fmaxf(mx[q], s[q >> 1][8 * (q & 1) + i]);
+#pragma unroll
+      for (int i = 4; i < 8; ++i) mx[q] = __builtin_fmaxf(mx[q], s[q >> 1][8 * (q & 1) + i]);
     }
-    l_run *= alpha;
-    m_run = m_new;
+    float mrow = kNegInf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mrow = __builtin_fmaxf(mrow, mx[q]);
+    const float mt = max_across_halves(mrow);
 
-    // P = exp2(x c - m c), packed to bf16 pairs in MFMA B-operand order
-    const float mc = m_use * c;
-    float lsum = 0.0f;
-    uint32_t pk[2][8];
+    // Lazy rescale: the reference max only moves when the tile max exceeds it
+    // by more than 8 in log2 units, so P <= 2^8 and the rescale of O and l is
+    // rare. O / l and m + log2(l) are unchanged by the choice of reference.
+    const bool raise = (mt - m_run) * c > 8.0f;   // m_run = -inf, mt finite -> true; both -inf -> false
+    const float alpha = raise ? fast_exp2((m_run - mt) * c) : 1.0f;   // 0 when m_run = -inf
+    m_run = raise ? mt : m_run;
+    l_run *= alpha;
+    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+
+    // P = exp2(x c - m c), packed to bf16 pairs in MFMA B-operand order;
+    // four independent partial sums
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(s[b][r], c, -mc));
         const float p1 = fast_exp2(__builtin_fmaf(s[b][r + 1], c, -mc));
-        lsum += p0 + p1;
+        ls[(r >> 1) & 3] += p0 + p1;
         pk[b][r >> 1] = pack_bf16x2(p0, p1);
       }
     }
-    l_run += lsum;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    return alpha;
+  };
 
-    // O^T += V^T P^T over four 16-key steps
+  // O^T = alpha O^T + V^T P^T over four 16-key steps (V slot `vslot`)
+  auto pv = [&](int vslot, float alpha, const uint32_t (&pk)[2][8]) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] *= alpha;
+    }
+    const char* vt = vslot0 + vslot * Tr::kVTile;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -263,33 +336,104 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int kb = 32 * b + 16 * gm;
 #pragma unroll
         for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
-          const char* p = vt + v_lane + (kb * Tr::kVPitch + 32 * dblk) * 2;
-          const U64 v0 = lds_read_tr16(p);
-          const U64 v1 = lds_read_tr16(p + 8 * Tr::kVPitch * 2);
+          const U64 v0 = lds_read_tr16(vt + v_addr(kb, 0, dblk));
+          const U64 v1 = lds_read_tr16(vt + v_addr(kb, 1, dblk));
           acc[dblk] = mfma32_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
         }
       }
     }
   };
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-    __syncthreads();
-    for (int t = t_begin; t < t_end; ++t) {
-      const int buf = (t - t_begin) & 1;
-      const bool more = t + 1 < t_end;
-      if (more) load_tile(t + 1);
-      const int j0 = t * kBlockN;
-      bool skip = !wave_active;
-      if (MASK) {
-        if (a.wr >= 0 && j0 > pw_hi + off + a.wr) skip = true;
-        if (a.wl >= 0 && j0 + kBlockN - 1 < pw_lo + off - a.wl) skip = true;
-      }
-      if (!skip) compute(t, buf);
-      if (more) store_tile(buf ^ 1);
-      __syncthreads();
+  using MaskedT = BoolTag<true>;
+  using PlainT = BoolTag<false>;
+
+  // does some row of this wave see only part of tile t (mask edge or Lk tail)?
+  auto tile_needs_mask = [&](int t) {
+    const int j0 = t * kBlockN;
+    bool need = j0 + kBlockN > Lk;
+    if (MASK) {
+      if (a.wr >= 0 && j0 + kBlockN - 1 > pw_lo + off + a.wr) need = true;
+      if (a.wl >= 0 && j0 < pw_hi + off - a.wl) need = true;
     }
+    return need;
+  };
+
+  if (t_begin < t_end) {
+#if ATTN_PREFILL_PIPELINED
+    // prologue: K(t0), V(t0), K(t0 + 1) into LDS; scores of tile t0
+    load_k(t_begin, 0);
+    load_v(t_begin, 0);
+    if (t_begin + 1 < t_end) load_k(t_begin + 1, 1);
+    if (FP8) store_v8(0);
+    wait_vmem();
+    __syncthreads();
+    f32x16 s0, s1;
+    qk(0, s0, s1);
+    // Iteration t: start the loads of K(t+2) and V(t+1) into the slots the last
+    // iteration freed; scores of tile t+1 on the matrix cores while the softmax
+    // of tile t runs; O += P V(t); wait for the loads; barrier. Unrolled by two
+    // so that the score registers ping-pong and the LDS slots are constants.
+    auto body = [&](auto parity_tag, auto masked_tag, auto has1_tag, int t, f32x16& c0, f32x16& c1, f32x16& n0,
+                    f32x16& n1) {
+      constexpr int P = decltype(parity_tag)::value ? 1 : 0;
+      uint32_t pk[2][8];
+      if (decltype(has1_tag)::value) qk(1 - P, n0, n1);
+      const float alpha = softmax(masked_tag, t, c0, c1, pk);
+      pv(P, alpha, pk);
+    };
+    auto step = [&](auto parity_tag, int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1) {
+      constexpr int P = decltype(parity_tag)::value ? 1 : 0;
+      const bool has1 = t + 1 < t_end;
+      const bool has2 = t + 2 < t_end;
+      if (has2) load_k(t + 2, P);
+      if (has1) load_v(t + 1, 1 - P);
+      if (has1) {
+        if (tile_needs_mask(t)) body(parity_tag, MaskedT{}, BoolTag<true>{}, t, c0, c1, n0, n1);
+        else body(parity_tag, PlainT{}, BoolTag<true>{}, t, c0, c1, n0, n1);
+      } else {
+        if (tile_needs_mask(t)) body(parity_tag, MaskedT{}, BoolTag<false>{}, t, c0, c1, n0, n1);
+        else body(parity_tag, PlainT{}, BoolTag<false>{}, t, c0, c1, n0, n1);
+      }
+      if (FP8 && has1) store_v8(1 - P);
+      wait_vmem();
+      __syncthreads();
+    };
+    f32x16 s2, s3;
+    for (int t = t_begin; t < t_end; t += 2) {
+      step(BoolTag<false>{}, t, s0, s1, s2, s3);
+      if (t + 1 >= t_end) break;
+      step(BoolTag<true>{}, t + 1, s2, s3, s0, s1);
+    }
+#else
+    // Tile t lives in LDS slot (t - t0) % 2; the loads of tile t+1 into the
+    // other slot are in flight (HBM -> LDS) while tile t is computed.
+    load_k(t_begin, 0);
+    load_v(t_begin, 0);
+    if (FP8) store_v8(0);
+    wait_vmem();
+    __syncthreads();
+    auto step = [&](auto parity_tag, int t) {
+      constexpr int P = decltype(parity_tag)::value ? 1 : 0;
+      const bool has1 = t + 1 < t_end;
+      if (has1) {
+        load_k(t + 1, 1 - P);
+        load_v(t + 1, 1 - P);
+      }
+      f32x16 s0, s1;
+      qk(P, s0, s1);
+      uint32_t pk[2][8];
+      const float alpha = tile_needs_mask(t) ? softmax(MaskedT{}, t, s0, s1, pk) : softmax(PlainT{}, t, s0, s1, pk);
+      pv(P, alpha, pk);
+      if (FP8 && has1) store_v8(1 - P);
+      wait_vmem();
+      __syncthreads();
+    };
+    for (int t = t_begin; t < t_end; t += 2) {
+      step(BoolTag<false>{}, t);
+      if (t + 1 >= t_end) break;
+      step(BoolTag<true>{}, t + 1);
+    }
+#endif
   }
 
   // ---- epilogue: normalise, LSE, predicated stores (rows < Lq only) ----
