@@ -28,7 +28,8 @@ struct PrefillArgs {
   const int32_t* cu_k;
   int sq, sk;                 // batch-mode extents
   int hq, hkv, ratio;
-  int n_qtiles;               // grid x extent (packed-row tiles)
+  int n_qtiles;               // packed-row tiles per (sequence, kv-head)
+  int nz;                     // batch entries (batch mode) or sequences (varlen); set by the launcher
   float c_exp2;               // multiplier taking the kernel's logit domain to log2 units
   float softcap_pre;          // softcap: raw dot * softcap_pre = (scaled logit) / cap
   float softcap_post;         // softcap: cap * log2(e)

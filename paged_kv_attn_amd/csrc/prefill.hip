@@ -43,6 +43,7 @@ namespace {
 constexpr int kBlockM = 128;
 constexpr int kBlockN = 64;
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;         // accelerator complex dies on MI355X
 
 template <int D, bool FP8>
 struct Traits {
@@ -87,10 +88,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int h = lane >> 5;          // which half of the key / d sub-blocks this lane holds
-  const int g = blockIdx.y;         // kv-head
-  const int z = blockIdx.z;         // batch entry or sequence
-  int qt = blockIdx.x;
-  if (MASK) qt = a.n_qtiles - 1 - qt;  // heaviest (latest) query tiles launch first
+  // XCD-aware work order. Workgroups are dispatched round-robin over the 8
+  // XCDs (hardware id w goes to XCD w % 8), each with its own L2. Give XCD x a
+  // contiguous range of the logical order, which runs (sequence, kv-head)-major
+  // so that all query tiles of one head, which read the same K/V, share an L2;
+  // within a head the heaviest (latest, under a causal mask) tiles come first.
+  const int n_wg = a.n_qtiles * a.hkv * a.nz;
+  const int per_xcd = (n_wg + kXcds - 1) / kXcds;
+  const int logical = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (logical >= n_wg) return;
+  const int qt_i = logical % a.n_qtiles;
+  const int g = (logical / a.n_qtiles) % a.hkv;    // kv-head
+  const int z = logical / (a.n_qtiles * a.hkv);    // batch entry or sequence
+  const int qt = MASK ? a.n_qtiles - 1 - qt_i : qt_i;
 
   // ---- sequence geometry (batch: seqused; varlen: cumulative offsets) ----
   int Lq, Lk;
@@ -462,8 +472,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
 template <int D, bool FP8, bool VARLEN, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
-  dim3 grid(a.n_qtiles, a.hkv, nz);
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, VARLEN, MASK, SOFTCAP>), grid, dim3(kThreads), 0, stream, a);
+  PrefillArgs b = a;
+  b.nz = nz;
+  const int64_t n_wg = (int64_t)a.n_qtiles * a.hkv * nz;
+  const int64_t grid = (n_wg + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, VARLEN, MASK, SOFTCAP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
 
