@@ -83,7 +83,13 @@ template <int D, bool FP8, bool VARLEN, bool MASK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Tr = Traits<D, FP8>;
   using QT = typename QFrag<FP8>::T;
-  __shared__ __attribute__((aligned(16))) char smem[Tr::kSmem];
+  // Separate LDS objects per slot: the compiler can then prove that reads of
+  // one slot do not alias the HBM->LDS loads in flight into the other, and
+  // does not wait for those loads before reading.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[Tr::kKTile];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[Tr::kKTile];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[Tr::kVTile];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[Tr::kVTile];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -169,8 +175,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const char* kh = (const char*)a.k + (k_off + (int64_t)g * a.k_sh) * Tr::kElem;
   const char* vh = (const char*)a.v + (v_off + (int64_t)g * a.v_sh) * Tr::kElem;
   const int64_t krow = a.k_sr * Tr::kElem, vrow = a.v_sr * Tr::kElem;  // global bytes per key row
-  char* const kslot0 = smem;
-  char* const vslot0 = smem + 2 * Tr::kKTile;
+  auto kslot = [&](int slot) -> char* { return slot ? k_lds1 : k_lds0; };
+  auto vslot = [&](int slot) -> char* { return slot ? v_lds1 : v_lds0; };
   // Wave w fills LDS blocks w, w+4, ... (1 KiB each) of a tile; lane l of block q
   // covers LDS bytes 1024 q + 16 l = (row R, slot s), fetching global chunk s ^ swz(R).
   int koff[Tr::kKInstr], voff[Tr::kVInstr];
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   auto load_k = [&](int t, int slot) {
     const int j0 = t * kBlockN;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + j0 * krow, (uint32_t)(min(kBlockN, Lk - j0) * krow));
-    char* base = kslot0 + slot * Tr::kKTile;
+    char* base = kslot(slot);
 #pragma unroll
     for (int i = 0; i < Tr::kKInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), koff[i]);
   };
@@ -204,13 +210,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < Tr::kV8Loads; ++i)
         v8[i] = buf_load16(r, (int)((v8row + i * (kThreads / Tr::kV8Ch)) * vrow) + 16 * v8ch);
     } else {
-      char* base = vslot0 + slot * Tr::kVTile;
+      char* base = vslot(slot);
 #pragma unroll
       for (int i = 0; i < Tr::kVInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), voff[i]);
     }
   };
   auto store_v8 = [&](int slot) {  // fp8 only
-    char* base = vslot0 + slot * Tr::kVTile;
+    char* base = vslot(slot);
 #pragma unroll
     for (int i = 0; i < (FP8 ? Tr::kV8Loads : 0); ++i) {
       const int R = v8row + i * (kThreads / Tr::kV8Ch);
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // S^T = K Q^T for the tile in K slot `slot`: two interleaved 32-key chains
   auto qk = [&](int slot, f32x16& s0, f32x16& s1) {
-    const char* kt = kslot0 + slot * Tr::kKTile;
+    const char* kt = kslot(slot);
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
@@ -331,12 +337,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   // O^T = alpha O^T + V^T P^T over four 16-key steps (V slot `vslot`)
-  auto pv = [&](int vslot, float alpha, const uint32_t (&pk)[2][8]) {
+  auto pv = [&](int vs, float alpha, const uint32_t (&pk)[2][8]) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
       for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] *= alpha;
     }
-    const char* vt = vslot0 + vslot * Tr::kVTile;
+    const char* vt = vslot(vs);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
