@@ -33,10 +33,6 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
-#ifndef ATTN_PREFILL_PIPELINED
-#define ATTN_PREFILL_PIPELINED 0
-#endif
-
 namespace attn {
 namespace {
 
@@ -363,6 +359,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using MaskedT = BoolTag<true>;
   using PlainT = BoolTag<false>;
 
+  // does no row of this wave see any key of tile t?
+  auto tile_skipped = [&](int t) {
+    const int j0 = t * kBlockN;
+    bool skip = wr0 >= rows_total;
+    if (MASK) {
+      if (a.wr >= 0 && j0 > pw_hi + off + a.wr) skip = true;
+      if (a.wl >= 0 && j0 + kBlockN - 1 < pw_lo + off - a.wl) skip = true;
+    }
+    return skip;
+  };
   // does some row of this wave see only part of tile t (mask edge or Lk tail)?
   auto tile_needs_mask = [&](int t) {
     const int j0 = t * kBlockN;
@@ -375,52 +381,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   if (t_begin < t_end) {
-#if ATTN_PREFILL_PIPELINED
-    // prologue: K(t0), V(t0), K(t0 + 1) into LDS; scores of tile t0
-    load_k(t_begin, 0);
-    load_v(t_begin, 0);
-    if (t_begin + 1 < t_end) load_k(t_begin + 1, 1);
-    if (FP8) store_v8(0);
-    wait_vmem();
-    __syncthreads();
-    f32x16 s0, s1;
-    qk(0, s0, s1);
-    // Iteration t: start the loads of K(t+2) and V(t+1) into the slots the last
-    // iteration freed; scores of tile t+1 on the matrix cores while the softmax
-    // of tile t runs; O += P V(t); wait for the loads; barrier. Unrolled by two
-    // so that the score registers ping-pong and the LDS slots are constants.
-    auto body = [&](auto parity_tag, auto masked_tag, auto has1_tag, int t, f32x16& c0, f32x16& c1, f32x16& n0,
-                    f32x16& n1) {
-      constexpr int P = decltype(parity_tag)::value ? 1 : 0;
-      uint32_t pk[2][8];
-      if (decltype(has1_tag)::value) qk(1 - P, n0, n1);
-      const float alpha = softmax(masked_tag, t, c0, c1, pk);
-      pv(P, alpha, pk);
-    };
-    auto step = [&](auto parity_tag, int t, f32x16& c0, f32x16& c1, f32x16& n0, f32x16& n1) {
-      constexpr int P = decltype(parity_tag)::value ? 1 : 0;
-      const bool has1 = t + 1 < t_end;
-      const bool has2 = t + 2 < t_end;
-      if (has2) load_k(t + 2, P);
-      if (has1) load_v(t + 1, 1 - P);
-      if (has1) {
-        if (tile_needs_mask(t)) body(parity_tag, MaskedT{}, BoolTag<true>{}, t, c0, c1, n0, n1);
-        else body(parity_tag, PlainT{}, BoolTag<true>{}, t, c0, c1, n0, n1);
-      } else {
-        if (tile_needs_mask(t)) body(parity_tag, MaskedT{}, BoolTag<false>{}, t, c0, c1, n0, n1);
-        else body(parity_tag, PlainT{}, BoolTag<false>{}, t, c0, c1, n0, n1);
-      }
-      if (FP8 && has1) store_v8(1 - P);
-      wait_vmem();
-      __syncthreads();
-    };
-    f32x16 s2, s3;
-    for (int t = t_begin; t < t_end; t += 2) {
-      step(BoolTag<false>{}, t, s0, s1, s2, s3);
-      if (t + 1 >= t_end) break;
-      step(BoolTag<true>{}, t + 1, s2, s3, s0, s1);
-    }
-#else
     // Tile t lives in LDS slot (t - t0) % 2; the loads of tile t+1 into the
     // other slot are in flight (HBM -> LDS) while tile t is computed.
     load_k(t_begin, 0);
@@ -435,11 +395,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         load_k(t + 1, 1 - P);
         load_v(t + 1, 1 - P);
       }
-      f32x16 s0, s1;
-      qk(P, s0, s1);
-      uint32_t pk[2][8];
-      const float alpha = tile_needs_mask(t) ? softmax(MaskedT{}, t, s0, s1, pk) : softmax(PlainT{}, t, s0, s1, pk);
-      pv(P, alpha, pk);
+      if (!tile_skipped(t)) {
+        f32x16 s0, s1;
+        qk(P, s0, s1);
+        uint32_t pk[2][8];
+        const float alpha =
+            tile_needs_mask(t) ? softmax(MaskedT{}, t, s0, s1, pk) : softmax(PlainT{}, t, s0, s1, pk);
+        pv(P, alpha, pk);
+      }
       if (FP8 && has1) store_v8(1 - P);
       wait_vmem();
       __syncthreads();
@@ -449,7 +412,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       if (t + 1 >= t_end) break;
       step(BoolTag<true>{}, t + 1);
     }
-#endif
   }
 
   // ---- epilogue: normalise, LSE, predicated stores (rows < Lq only) ----
@@ -501,6 +463,8 @@ hipError_t launch_d(const PrefillArgs& a, int in_type, bool varlen, int nz, bool
 }
 
 }  // namespace
+
+int prefill_rows_per_tile() { return kBlockM; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, bool varlen, int nz, hipStream_t stream) {
   const bool mask = a.wl >= 0 || a.wr >= 0;
