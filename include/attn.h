@@ -85,8 +85,8 @@ typedef struct {
   float q_descale;     /* FP8 only: stored value * descale = real value; else ignored */
   float k_descale;
   float v_descale;
-  int kv_split_tokens; /* decode path: keys per split-KV work unit, a multiple of 64;
-                          0 = choose from the shape. Calls that must agree bit for bit
+  int kv_split_tokens; /* decode path: keys per split-KV work unit, a multiple of 64
+                          in [64, 2048]; 0 = choose from the shape. Calls that must agree bit for bit
                           pass the same value (or the same shape with 0). */
 } attn_params_t;
 

@@ -20,6 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "f32.hip"]
+# Per-source code-generation options. The decode kernel keeps its MFMA
+# accumulators in ordinary VGPRs: its online-softmax rescale touches them
+# between matrix ops, and accumulation registers would cost a copy each way.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 
@@ -36,7 +40,7 @@ def _flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln)

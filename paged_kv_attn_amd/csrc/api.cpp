@@ -38,13 +38,15 @@ bool takes_decode_path(int in_dtype, int sq, int ratio) {
   return in_dtype != ATTN_F32 && (int64_t)sq * ratio <= 16;
 }
 
-// Keys per split-KV work unit: unless the caller fixes it, the smallest power
-// of two >= 256 that keeps the (request, kv-head, split) grid near 8192 units.
+// Keys per split-KV work unit (one wave each): unless the caller fixes it, the
+// smallest power of two in [256, 2048] that keeps the (request, kv-head, split)
+// grid at or below 32768 units -- about 16 waves for each resident slot of the
+// chip, with at least 8 pipeline steps per wave.
 int plan_split_tokens(const attn_params_t* p, int B, int Hkv, int max_len) {
   if (p->kv_split_tokens > 0) return p->kv_split_tokens;
   const int64_t units = (int64_t)B * Hkv;
   int c = 256;
-  while (c < 4096 && units * ((max_len + c - 1) / c) > 8192) c *= 2;
+  while (c < 2048 && units * ((max_len + c - 1) / c) > 32768) c *= 2;
   return c;
 }
 
@@ -72,8 +74,8 @@ attn_status_t check_params(const attn_params_t* p, int d) {
     for (float x : ds)
       if (!(x > 0.0f) || !std::isfinite(x)) return fail(ATTN_EINVAL, "fp8 descales must be finite and > 0");
   }
-  if (p->kv_split_tokens < 0 || p->kv_split_tokens % 64 != 0)
-    return fail(ATTN_EINVAL, "kv_split_tokens must be 0 or a positive multiple of 64");
+  if (p->kv_split_tokens < 0 || p->kv_split_tokens % 64 != 0 || p->kv_split_tokens > 2048)
+    return fail(ATTN_EINVAL, "kv_split_tokens must be 0 or a multiple of 64 in [64, 2048]");
   return ATTN_OK;
 }
 

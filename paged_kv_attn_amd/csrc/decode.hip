@@ -1,27 +1,30 @@
 // Split-KV decode for short query blocks (sq * Hq/Hkv <= 16 packed rows), with
 // the keys either contiguous or in a paged pool, plus the split combine.
 //
-// Work unit = (split, kv-head, request). A split is a fixed, key-aligned range
-// of split_tokens keys, so a paged call and a contiguous call with the same
-// logical keys and the same split size perform identical arithmetic in the same
-// order and give identical bits. Inside a workgroup, wave w takes the 32-key
-// granules w, w+4, w+8, ... of its split; every granule lies in one page
-// (page_size is a multiple of 32), whose physical id is read once per granule
-// from the block table (the page-block navigator of the Composable Kernel page
-// "fmha_fwd_pagedkv_kernel.hpp Source File": one table row per request,
-// page_block_size tokens per page, 64-bit page base + in-page offset).
+// Work unit = (split, kv-head, request), one wave each. A split is a fixed,
+// key-aligned range of split_tokens keys, so a paged call and a contiguous call
+// with the same logical keys and the same split size perform identical
+// arithmetic in the same order and give identical bits. The wave walks its
+// split in 32-key granules; every granule lies in one page (page_size is a
+// multiple of 32), whose physical id comes from the block table (the
+// page-block navigator of the Composable Kernel page "fmha_fwd_pagedkv_kernel.hpp
+// Source File": one table row per request, page_block_size tokens per page,
+// 64-bit page base + in-page offset).
 //
 // Math per granule, on v_mfma_f32_16x16x32_bf16 with the <= 16 packed query
 // rows (request position x q-heads of this kv-head) as the MFMA column
-// dimension: S^T = K Q^T with K fed straight from global memory in A-operand
-// layout (128-bit loads along d), online softmax over keys (max / sum across
-// the four 16-lane groups), O^T += V^T P^T with V staged row-major in the
-// wave's own LDS slice and read back transposed (ds_read_b64_tr_b16).
+// dimension: S^T = K Q^T with K fed straight from global memory into A-operand
+// registers (128-bit loads along d), online softmax over keys (max / sum across
+// the four 16-lane groups), O^T += V^T P^T with V copied HBM -> LDS by the
+// buffer unit and read back transposed (ds_read_b64_tr_b16).
 //
-// The four waves' (m, l, O) are merged through LDS into one partial per split,
-// stored normalised with its log-sum-exp (the num_splits axis of O / LSE in the
-// flash-attention epilogue page "hopper/epilogue_fwd.hpp"). The combine kernel
-// then forms, per query row and in a fixed split order,
+// Software pipeline: the next granule's K (registers) and V (the other LDS
+// buffer) are in flight while the current one is computed. There is no
+// barrier anywhere: all data a wave touches is its own.
+//
+// Each unit stores its (O, LSE) normalised (the num_splits axis of O / LSE in
+// the flash-attention epilogue page "hopper/epilogue_fwd.hpp"). The combine
+// kernel then forms, per query row and in a fixed split order,
 //     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
 // which equals attention over the union of the splits' keys.
 #include "common.hpp"
@@ -30,22 +33,31 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kGran = 32;        // keys per wave step
-constexpr int kVPitch = 144;     // bf16 elements per V row in LDS (72 dwords)
-constexpr int kVStage = kGran * kVPitch * 2;  // bytes per wave
+constexpr int kGran = 32;  // keys per pipeline step
 
 template <int D>
 struct DTr {
-  static constexpr int kSteps = D / 32;       // k-steps of S^T = K Q^T (32 d each)
-  static constexpr int kDBlocks = D / 16;     // 16-row blocks of O^T
-  static constexpr int kChunks = D / 8;       // 16-byte chunks per K/V row
-  static constexpr int kVLoads = kGran * kChunks / 64;
-  static constexpr int kKeyStep = 64 / kChunks;
-  static constexpr int kMergeBytes = kWaves * (16 * D * 4 + 2 * 16 * 4);
-  static constexpr int kSmem = (kWaves * kVStage > kMergeBytes) ? kWaves * kVStage : kMergeBytes;
+  static constexpr int kSteps = D / 32;        // k-steps of S^T = K Q^T (32 d each)
+  static constexpr int kDBlocks = D / 16;      // 16-row blocks of O^T
+  static constexpr int kRow = D * 2;           // bytes per K/V row
+  static constexpr int kCh = kRow / 16;        // 16-byte chunks per row
+  static constexpr int kVBuf = kGran * kRow;   // one V granule in LDS
+  static constexpr int kVBlocks = kVBuf / 1024;
+  static constexpr int kOps = 2 * kSteps + kVBlocks;  // vector-memory ops per granule
+  static_assert(kVBlocks >= 1, "V granule smaller than one direct-to-LDS block");
 };
+
+// Chunk swizzle of an LDS V row (chunk c of row R lives in slot c ^ vswz(R));
+// makes the transpose reads of 4 rows x 32 bytes per 16-lane group conflict-free.
+__device__ __forceinline__ int vswz(int row, int nchunks) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (nchunks - 1);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 __device__ __forceinline__ float xor_shfl(float x, int mask) {
   const int lane = threadIdx.x & 63;
@@ -53,12 +65,14 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) {
 }
 
 template <int D, bool PAGED, bool MASK, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   using Tr = DTr<D>;
-  __shared__ __attribute__((aligned(16))) char smem[Tr::kSmem];
+  // One LDS object per pipeline buffer, so the compiler can tell the
+  // HBM->LDS copies into one buffer from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) char vbuf0[Tr::kVBuf];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[Tr::kVBuf];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
@@ -76,9 +90,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int hq = g * ratio + qc % ratio;
   const int off = Lk - a.sq;
   int lim_lo = 0, lim_hi = Lk - 1;
+  // keys any row of the unit can see (bottom-right aligned window)
+  int t_lo = t0, t_hi = t1;
   if (MASK) {
-    if (a.wr >= 0) lim_hi = min(Lk - 1, pos + off + a.wr);
-    if (a.wl >= 0) lim_lo = pos + off - a.wl;
+    if (a.wr >= 0) {
+      lim_hi = min(Lk - 1, pos + off + a.wr);
+      t_hi = min(t1, (a.sq - 1) + off + a.wr + 1);
+    }
+    if (a.wl >= 0) {
+      lim_lo = pos + off - a.wl;
+      t_lo = max(t0, off - a.wl);
+    }
+    t_lo = t0 + (max(0, t_lo - t0) / kGran) * kGran;  // keep granules aligned to the split
+  }
+
+  // The split's page ids, one per lane (a split spans at most 64 pages).
+  const int p_first = PAGED ? t0 / a.page_size : 0;
+  int pg = 0;
+  if (PAGED) {
+    const int n_pg = (t1 - 1) / a.page_size - p_first + 1;
+    if (lane < n_pg) pg = a.block_table[(int64_t)b * a.bt_stride + p_first + lane];
   }
 
   // Q^T as the B operand: lane (column qc, group j4) holds Q[qc][32s + 8 j4 .. +7]
@@ -89,11 +120,53 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int s = 0; s < Tr::kSteps; ++s) qf[s] = row_ok ? *(const U128*)(qp + (32 * s + 8 * j4) * 2) : U128{0, 0, 0, 0};
   }
 
-  char* vstage = smem + wave * kVStage;
+  const int64_t krow = a.k_sr * 2, vrow = a.v_sr * 2;   // bytes per key row
   const int L = lane & 15;
-  const int v_lane = ((4 * j4 + (L >> 2)) * kVPitch + 4 * (L & 3)) * 2;
-  const int vch = lane % Tr::kChunks;
-  const int vkey = lane / Tr::kChunks;
+  // K as the A operand, straight from HBM: lane (key 16 kb + L, group j4)
+  // loads K[key][32 st + 8 j4 .. +7].
+  auto k_off = [&](int kb, int st) -> int { return (int)((16 * kb + L) * krow) + 2 * (32 * st + 8 * j4); };
+  // V granule -> LDS: block q, lane l covers LDS bytes 1024 q + 16 l =
+  // (row R, slot sl) and fetches chunk sl ^ vswz(R) of row R.
+  int voff[Tr::kVBlocks];
+#pragma unroll
+  for (int q = 0; q < Tr::kVBlocks; ++q) {
+    const int B = 1024 * q + 16 * lane;
+    const int R = B / Tr::kRow, sl = (B % Tr::kRow) / 16;
+    voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz(R, Tr::kCh));
+  }
+  // transpose reads: group j4 (16 lanes) reads rows 16 kb + 4 j4 + L / 4, bf16
+  // columns 16 dblk + 4 (L & 3); vswz(row) = ((L >> 2) << 2) | j4 for these rows.
+  const int v_sw = (((L >> 2) << 2) | j4) & (Tr::kCh - 1);
+  const int v_base0 = (4 * j4 + (L >> 2)) * Tr::kRow + 16 * (((L & 3) >> 1) ^ (v_sw & 1)) + 8 * (L & 1);
+  const int v_swhi = 16 * (v_sw & ~1);
+
+  // base of the 32 keys starting at key gs (64-bit page base + in-page offset)
+  auto rows_base = [&](int gs, const void* pool, int64_t sb, int64_t sh, int64_t sr) -> const char* {
+    if (PAGED) {
+      const int page = __builtin_amdgcn_readlane(pg, gs / a.page_size - p_first);
+      return (const char*)pool + ((int64_t)page * sb + (int64_t)g * sh + (int64_t)(gs % a.page_size) * sr) * 2;
+    }
+    return (const char*)pool + ((int64_t)b * sb + (int64_t)g * sh + (int64_t)gs * sr) * 2;
+  };
+  // issue the loads of granule gs: K into registers, V into LDS buffer vb.
+  // A granule at or past t_hi is issued with an empty range: no memory
+  // traffic, zeros everywhere.
+  auto issue = [&](int gs, U128 (&kf)[2][Tr::kSteps], char* vb) {
+    // readfirstlane keeps the clamp (a vector med3) from making the
+    // descriptor look divergent
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kGran, t_hi - gs)));
+    const int gp = rows > 0 ? gs : t0;  // any valid page for an empty range
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc(rows_base(gp, a.k, a.k_sb, a.k_sh, a.k_sr), (uint32_t)(rows * krow));
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc(rows_base(gp, a.v, a.v_sb, a.v_sh, a.v_sr), (uint32_t)(rows * vrow));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st) kf[kb][st] = buf_load16(kr, k_off(kb, st));
+#pragma unroll
+    for (int q = 0; q < Tr::kVBlocks; ++q) buf_load16_lds(vr, vb + 1024 * q, voff[q]);
+  };
 
   const float c = a.c_exp2;
   float m_run = kNegInf;
@@ -102,46 +175,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] = f32x4{};
 
-  for (int gs = t0 + wave * kGran; gs < t1; gs += kWaves * kGran) {
-    // base of this granule's 32 key rows (64-bit page base + in-page offset)
-    const char* kbase;
-    const char* vbase;
-    if (PAGED) {
-      const int page = a.block_table[(int64_t)b * a.bt_stride + gs / a.page_size];
-      const int slot = gs % a.page_size;
-      kbase = (const char*)a.k + ((int64_t)page * a.k_sb + (int64_t)g * a.k_sh + (int64_t)slot * a.k_sr) * 2;
-      vbase = (const char*)a.v + ((int64_t)page * a.v_sb + (int64_t)g * a.v_sh + (int64_t)slot * a.v_sr) * 2;
-    } else {
-      kbase = (const char*)a.k + ((int64_t)b * a.k_sb + (int64_t)g * a.k_sh + (int64_t)gs * a.k_sr) * 2;
-      vbase = (const char*)a.v + ((int64_t)b * a.v_sb + (int64_t)g * a.v_sh + (int64_t)gs * a.v_sr) * 2;
-    }
-    const int nvalid = t1 - gs;  // keys of this granule below Lk (may exceed 32)
-
-    // K as the A operand: lane (key 16kb + L, group j4) holds K[key][32s + 8 j4 .. +7]
-    U128 kf[2][Tr::kSteps];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = 16 * kb + L;
-#pragma unroll
-      for (int s = 0; s < Tr::kSteps; ++s)
-        kf[kb][s] = key < nvalid ? *(const U128*)(kbase + (int64_t)key * a.k_sr * 2 + (32 * s + 8 * j4) * 2)
-                                 : U128{0, 0, 0, 0};
-    }
-    // V rows (zero past Lk), staged row-major in this wave's LDS slice
-    U128 vf[Tr::kVLoads];
-#pragma unroll
-    for (int i = 0; i < Tr::kVLoads; ++i) {
-      const int key = vkey + i * Tr::kKeyStep;
-      vf[i] = key < nvalid ? *(const U128*)(vbase + (int64_t)key * a.v_sr * 2 + vch * 16) : U128{0, 0, 0, 0};
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // previous granule's LDS reads stay before these writes
-#pragma unroll
-    for (int i = 0; i < Tr::kVLoads; ++i) {
-      const int key = vkey + i * Tr::kKeyStep;
-      *(U128*)(vstage + (key * kVPitch + vch * 8) * 2) = vf[i];
-    }
-
-    // S^T = K Q^T: lane (column qc, group j4) gets keys 16kb + 4 j4 + r
+  // one 32-key granule: S^T = K Q^T, online softmax, O^T += V^T P^T
+  auto compute = [&](int gs, const U128 (&kf)[2][Tr::kSteps], const char* vb) {
     f32x4 st[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -149,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_bf16(as_bf16x8(kf[kb][s]), as_bf16x8(qf[s]), st[kb]);
     }
+    // lane (column qc, group j4) holds keys gs + 16 kb + 4 j4 + r
     float mt = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -159,73 +195,72 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const int j = gs + 16 * kb + 4 * j4 + r;
         x = (j >= lim_lo && j <= lim_hi) ? x : kNegInf;
         st[kb][r] = x;
-        mt = fmaxf(mt, x);
+        mt = __builtin_fmaxf(mt, x);
       }
     }
-    mt = fmaxf(mt, xor_shfl(mt, 16));
-    mt = fmaxf(mt, xor_shfl(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * c);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    mt = __builtin_fmaxf(mt, xor_shfl(mt, 16));
+    mt = __builtin_fmaxf(mt, xor_shfl(mt, 32));
+    // lazy rescale, as in the prefill kernel: the reference max only moves when
+    // the granule max exceeds it by more than 8 in log2 units
+    const bool raise = (mt - m_run) * c > 8.0f;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? fast_exp2((m_run - mt) * c) : 1.0f;
 #pragma unroll
       for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] *= alpha;
+      l_run *= alpha;
+      m_run = raise ? mt : m_run;
     }
-    l_run *= alpha;
-    m_run = m_new;
-    const float mc = m_use * c;
+    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       p[i] = fast_exp2(__builtin_fmaf(st[i >> 2][i & 3], c, -mc));
       l_run += p[i];
     }
-    // P^T as the B operand: slot 4kb + r <-> key 16kb + 4 j4 + r
+    // P^T as the B operand: slot 4 kb + r <-> key 16 kb + 4 j4 + r
     const U128 pu{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     const bf16x8 pb = as_bf16x8(pu);
-    // O^T += V^T P^T: transpose reads give lane (d, j4) V[16kb + 4 j4 + r][d]
+    int v_base = v_base0, v_hi = v_swhi;
+    asm volatile("" : "+v"(v_base), "+v"(v_hi));
 #pragma unroll
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
-      const char* vp = vstage + v_lane + 16 * dblk * 2;
+      const char* vp = vb + v_base + ((32 * dblk) ^ v_hi);
       const U64 v0 = lds_read_tr16(vp);
-      const U64 v1 = lds_read_tr16(vp + 16 * kVPitch * 2);
+      const U64 v1 = lds_read_tr16(vp + 16 * Tr::kRow);
       acc[dblk] = mfma16_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
     }
+  };
+
+  int gs = t_lo;
+  if (gs < t_hi) {
+    U128 kA[2][Tr::kSteps], kB[2][Tr::kSteps];
+    issue(gs, kA, vbuf0);
+    for (;;) {
+      issue(gs + kGran, kB, vbuf1);
+      wait_vmem_le<Tr::kOps>();
+      compute(gs, kA, vbuf0);
+      gs += kGran;
+      if (gs >= t_hi) break;
+      issue(gs + kGran, kA, vbuf0);
+      wait_vmem_le<Tr::kOps>();
+      compute(gs, kB, vbuf1);
+      gs += kGran;
+      if (gs >= t_hi) break;
+    }
+    wait_vmem_le<0>();
   }
 
-  // ---- merge the four waves' running states through LDS ----
+  // normalised partial: lane (qc, j4) holds O^T[16 dblk + 4 j4 + r][qc]
   l_run += xor_shfl(l_run, 16);
   l_run += xor_shfl(l_run, 32);
-  __syncthreads();  // all waves done with their V slices
-  float* mo = (float*)smem;                           // [wave][16][D]
-  float* mm = mo + kWaves * 16 * D;                   // [wave][16]
-  float* ml = mm + kWaves * 16;                       // [wave][16]
-#pragma unroll
-  for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk)
-    *(f32x4*)(mo + (wave * 16 + qc) * D + 16 * dblk + 4 * j4) = acc[dblk];
-  if (j4 == 0) {
-    mm[wave * 16 + qc] = m_run;
-    ml[wave * 16 + qc] = l_run;
-  }
-  __syncthreads();
   const int64_t unit = ((int64_t)b * a.hkv + g) * a.n_splits + split;
-  for (int e = threadIdx.x; e < a.m_rows * D; e += kThreads) {
-    const int r = e / D, d = e % D;
-    float M = kNegInf;
+  if (row_ok) {
+    const bool live = m_run != kNegInf;
+    const float inv = live ? 1.0f / l_run : 0.0f;
+    float* po = a.part_o + (unit * a.m_rows + qc) * D + 4 * j4;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 16 + r]);
-    float o = 0.0f, lsum = 0.0f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float wt = fast_exp2((mm[w * 16 + r] - M) * c);
-        o += wt * mo[(w * 16 + r) * D + d];
-        lsum += wt * ml[w * 16 + r];
-      }
-      o /= lsum;
-    }
-    a.part_o[(unit * a.m_rows + r) * D + d] = o;
-    if (d == 0) a.part_lse[unit * a.m_rows + r] = (M == kNegInf) ? kNegInf : (M * c + __builtin_log2f(lsum)) * kLn2;
+    for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) *(f32x4*)(po + 16 * dblk) = acc[dblk] * inv;
+    if (j4 == 0) a.part_lse[unit * a.m_rows + qc] = live ? (m_run * c + __builtin_log2f(l_run)) * kLn2 : kNegInf;
   }
 }
 
@@ -273,7 +308,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 template <int D, bool PAGED, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_t s) {
   dim3 grid(a.n_splits, a.hkv, B);
-  hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP>), grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)B * c.hq * c.sq;

@@ -90,6 +90,7 @@ def test_attn_fwd_rejects_bad_arguments(kw, status, msg):
     ("softcap", float("nan"), 1, "softcap"),
     ("window_left", -2, 1, "window"),
     ("kv_split_tokens", 100, 1, "multiple of 64"),
+    ("kv_split_tokens", 4096, 1, "2048"),
 ])
 def test_params_validation(field, value, status, msg):
     p = _params(**{field: value})

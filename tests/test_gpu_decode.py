@@ -19,6 +19,8 @@ DEV = "cuda"
     ([4096, 77, 2049], 128, 32, 8, 128),
     ([300, 5], 32, 16, 1, 64),        # ratio 16 fills the 16 packed rows
     ([700], 64, 4, 4, 0),             # no GQA
+    ([9000, 4097, 130], 32, 8, 2, 2048),  # largest split: 64 pages of 32 keys per unit
+    ([2100, 96], 96, 8, 2, 192),      # page size not a power of two; split not a page multiple
 ])
 def test_paged_decode_parity(lens, page, Hq, Hkv, split):
     case = synth.paged_case(lens, 1, Hq, Hkv, 128, page, "bf16", seed=sum(lens) + page, device=DEV)
