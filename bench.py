@@ -54,6 +54,57 @@ def decode_bytes(case) -> float:
     return float(kv + q + o + lse + table + m["B"] * 4)
 
 
+KERNEL_SOURCES = {
+    "prefill": ["paged_kv_attn_amd/csrc/prefill.hip", "paged_kv_attn_amd/csrc/common.hpp",
+                "paged_kv_attn_amd/csrc/kernels.hpp"],
+    "decode": ["paged_kv_attn_amd/csrc/decode.hip", "paged_kv_attn_amd/csrc/common.hpp",
+               "paged_kv_attn_amd/csrc/kernels.hpp"],
+}
+PROFILES = {"prefill": "profiles/prefill_bf16_causal_b4_h16_s2048_d128.md",
+            "decode": "profiles/decode_paged_bf16_64req_hq32_hkv8_d128.md"}
+
+
+def sources_sha256(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, PROFILES[kind])
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and ln.startswith(("traffic_bytes_per_launch", "kernel_sources_sha256")):
+                k, v = ln.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != sources_sha256(kind) or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
 def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
     """The fp64 oracle on the first n_heads (batch, head) pairs of the prefill
     workload, with its own thread pool over heads (one BLAS thread per worker),
@@ -94,11 +145,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--decode-split", type=int, default=0, help="keys per split-KV unit (0 = library default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "multi-GPU sharding is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import paged_kv_attn_amd as pk
@@ -178,7 +235,7 @@ def main():
         "config": {"workload": "bf16 causal prefill, batch mode B=4 H=16 sq=sk=2048 d=128, bf16 O + fp32 LSE",
                    "batch": 4, "heads": 16, "seq_len": 2048, "head_dim": 128, "mask": "causal"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "prefill_kernel<128, bf16, batch, causal>", "launch_us": round(pre_ms * 1e3, 2),
                      "algorithmic_flops": flops},
         "cpu_baseline": cpu,
@@ -187,7 +244,7 @@ def main():
             "workload": "bf16 paged decode, 64 requests L~U[1024,32768], page 128, Hq=32 Hkv=8 d=128, sq=1",
             "launch_us": round(dec_ms * 1e3, 2), "min_us": round(t_dec[0] * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
                          "kernel": "decode_kernel<128, paged> + combine_kernel", "algorithmic_bytes": dbytes},
             "splits": pk.attn_num_splits(p_dec, 64, 32, 8, 1, W * 128),
         },

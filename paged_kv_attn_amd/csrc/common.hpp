@@ -102,6 +102,13 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* l
                                            0, 0, 0);
 }
 
+// As buf_load16_lds, with the non-temporal cache policy: for data read once
+// (streamed KV), so it does not displace reusable lines in L2.
+__device__ __forceinline__ void buf_load16_lds_stream(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, byte_off,
+                                           0, 0, /*nt*/ 2);
+}
+
 // Wait until this wave's vector-memory loads (including loads into LDS) have
 // completed: s_waitcnt vmcnt(0) with the LDS and export counters left free.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

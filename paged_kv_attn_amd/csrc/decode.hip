@@ -16,7 +16,9 @@
 // dimension: S^T = K Q^T with K fed straight from global memory into A-operand
 // registers (128-bit loads along d), online softmax over keys (max / sum across
 // the four 16-lane groups), O^T += V^T P^T with V copied HBM -> LDS by the
-// buffer unit and read back transposed (ds_read_b64_tr_b16).
+// buffer unit (non-temporal: every V row is read once) and read back
+// transposed (ds_read_b64_tr_b16). K stays on the default cache policy: its
+// 64-byte halves of a 128-byte line arrive from two different loads.
 //
 // Software pipeline: the next granule's K (registers) and V (the other LDS
 // buffer) are in flight while the current one is computed. There is no
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int st = 0; st < Tr::kSteps; ++st) kf[kb][st] = buf_load16(kr, k_off(kb, st));
 #pragma unroll
-    for (int q = 0; q < Tr::kVBlocks; ++q) buf_load16_lds(vr, vb + 1024 * q, voff[q]);
+    for (int q = 0; q < Tr::kVBlocks; ++q) buf_load16_lds_stream(vr, vb + 1024 * q, voff[q]);
   };
 
   const float c = a.c_exp2;
@@ -264,7 +266,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per output row (request, q-head, position).
+// One wave per output row (request, q-head, position). The split LSEs are
+// read 64 at a time (one per lane) for the max and the weights; the partial
+// rows are then summed in split order with 8 loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
@@ -279,20 +283,47 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int Lk = a.seqlens_k ? a.seqlens_k[b] : a.sk;
   const int n = Lk > 0 ? (Lk + a.split_tokens - 1) / a.split_tokens : 0;
   const int64_t unit0 = ((int64_t)b * a.hkv + g) * a.n_splits;
+  const float* lse_p = a.part_lse + unit0 * a.m_rows + r;   // split s at lse_p[s * m_rows]
+  const float* o_p = a.part_o + unit0 * a.m_rows * D + (int64_t)r * D;  // split s at o_p[s * m_rows * D]
+  const int64_t o_stride = (int64_t)a.m_rows * D;
   constexpr int kPer = D / 64;
+
   float M = kNegInf;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, a.part_lse[(unit0 + s) * a.m_rows + r]);
+  for (int s0 = 0; s0 < n; s0 += 64)
+    if (s0 + lane < n) M = fmaxf(M, lse_p[(int64_t)(s0 + lane) * a.m_rows]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+
   float o[kPer] = {};
   float wsum = 0.0f;
   if (M != kNegInf) {
-    for (int s = 0; s < n; ++s) {
-      const float ls = a.part_lse[(unit0 + s) * a.m_rows + r];
-      const float w = fast_exp2((ls - M) * kLog2e);
-      wsum += w;
-      const float* po = a.part_o + ((unit0 + s) * a.m_rows + r) * D;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int cnt = min(64, n - s0);
+      // this lane's split weight exp(LSE_s - M)
+      const float w_l = lane < cnt ? fast_exp2((lse_p[(int64_t)(s0 + lane) * a.m_rows] - M) * kLog2e) : 0.0f;
+      wsum += w_l;
+      int s = 0;
+      for (; s + 8 <= cnt; s += 8) {
+        float v[8][kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) o[i] += w * po[lane * kPer + i];
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) v[u][i] = o_p[(int64_t)(s0 + s + u) * o_stride + lane * kPer + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), s + u));
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) o[i] += w * v[u][i];
+        }
+      }
+      for (; s < cnt; ++s) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), s));
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) o[i] += w * o_p[(int64_t)(s0 + s) * o_stride + lane * kPer + i];
+      }
     }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) wsum += __shfl_xor(wsum, m);
   }
   const float inv = (M == kNegInf) ? 0.0f : a.o_mul / wsum;
   __bf16* op = (__bf16*)a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr;

@@ -22,12 +22,15 @@
 //
 // K and V tiles travel from HBM straight into LDS (buffer_load_dwordx4 ... lds,
 // 128-bit per lane, coalesced along d; rows past the sequence end arrive as
-// zeros from the buffer range check), K two tiles ahead and V one tile ahead,
-// so no registers are spent on staging. Within LDS each 16-byte chunk of a row
-// is XOR-swizzled by the row index, which keeps the K operand reads and the V
-// transpose reads free of bank conflicts. The loop is software-pipelined: the
-// scores of tile t+1 are computed on the matrix cores while the softmax of
-// tile t runs on the vector ALUs.
+// zeros from the buffer range check), so no registers are spent on staging.
+// Two LDS slots (separate LDS objects, so the compiler can order reads of one
+// slot against the copies into the other without waiting for them): while
+// tile t is computed from one slot, tile t+1 is in flight into the other; one
+// wait + barrier per tile. Within LDS each 16-byte chunk of a row is
+// XOR-swizzled by the row index, which keeps the K operand reads and the V
+// transpose reads free of bank conflicts. Tiles that no row of a wave can see
+// are skipped by that wave; the mask is evaluated only on tiles that cut
+// through some row's visible range.
 // Softmax runs in the exp2 domain with scale * log2(e) folded into one FMA
 // (the FAST_EXP2 folding of the Composable Kernel page's MakeKargs).
 #include "common.hpp"
