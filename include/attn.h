@@ -31,9 +31,10 @@
  *     contiguous (unit stride). Every tensor base pointer must be 16-byte
  *     aligned and every stride a multiple of 16 bytes.
  *   - Supported: d in {64, 128}; (in_dtype, out_dtype) in {(F32, F32),
- *     (BF16, BF16), (FP8_E4M3, BF16)}; F32 only in batch mode with no window
- *     and sk <= 4096. FP8 means OCP E4M3FN; the value of a stored byte x is
- *     e4m3(x) * descale of its tensor.
+ *     (BF16, BF16), (FP8_E4M3, BF16)}. F32 runs in batch mode only (a plain
+ *     vector-ALU kernel). The split-KV decode path (sq * Hq / Hkv <= 16, and
+ *     every attn_fwd_paged call) takes BF16 only. FP8 means OCP E4M3FN; the
+ *     value of a stored byte x is e4m3(x) * descale of its tensor.
  *   - lse may be NULL (not stored). LSE is fp32, natural log.
  *   - Rows at or beyond a sequence's used query length are never written, in O
  *     or LSE (the predicated stores of the flash-attention epilogue page).
@@ -140,7 +141,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p,
  * block_table[b*block_table_stride + t / page_size] (the page-block navigator
  * of the Composable Kernel page: block_table_ptr, batch_stride_block_table,
  * page_block_size). seqlens_k (int32 [B], device) gives Lk per request;
- * Lq = sq. page_size must be a multiple of 64; block_table_stride * page_size
+ * Lq = sq. page_size must be a multiple of 32; block_table_stride * page_size
  * bounds every Lk. Requires sq * Hq / Hkv <= 16 (decode shapes). lse (nullable)
  * is fp32 [B, Hq, sq]. Needs a workspace of attn_workspace_bytes() bytes with
  * max_seqlen_k = block_table_stride * page_size.
