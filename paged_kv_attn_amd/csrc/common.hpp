@@ -23,6 +23,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// LDS byte pointer. Kernels that pass LDS addresses around (through lambdas,
+// slot selects) keep them in this type: a generic pointer converted back to an
+// LDS address costs a null check per use.
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -49,6 +53,17 @@ __device__ __forceinline__ f32x16 mfma32_fp8(const U64& a, const U64& b, const f
 }
 
 // 4 bf16 values of one LDS transpose read (see the layout note above).
+// 16 bytes from LDS (ds_read_b128).
+__device__ __forceinline__ U128 lds_load16(const lds_char* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)p;
+  return __builtin_bit_cast(U128, v);
+}
+
+__device__ __forceinline__ U64 lds_read_tr16(const lds_char* lds_addr) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_addr);
+  return __builtin_bit_cast(U64, v);
+}
 __device__ __forceinline__ U64 lds_read_tr16(const void* lds_addr) {
   auto p = (lds_s16x4*)(lds_addr);
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
@@ -104,9 +119,8 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* l
 
 // As buf_load16_lds, with the non-temporal cache policy: for data read once
 // (streamed KV), so it does not displace reusable lines in L2.
-__device__ __forceinline__ void buf_load16_lds_stream(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, byte_off,
-                                           0, 0, /*nt*/ 2);
+__device__ __forceinline__ void buf_load16_lds_stream(__amdgpu_buffer_rsrc_t r, lds_char* lds_wave_base, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, byte_off, 0, 0, /*nt*/ 2);
 }
 
 // Wait until this wave's vector-memory loads (including loads into LDS) have

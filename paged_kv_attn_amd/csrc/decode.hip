@@ -43,16 +43,23 @@ struct DTr {
   static constexpr int kDBlocks = D / 16;      // 16-row blocks of O^T
   static constexpr int kRow = D * 2;           // bytes per K/V row
   static constexpr int kCh = kRow / 16;        // 16-byte chunks per row
-  static constexpr int kVBuf = kGran * kRow;   // one V granule in LDS
-  static constexpr int kVBlocks = kVBuf / 1024;
-  static constexpr int kOps = 2 * kSteps + kVBlocks;  // vector-memory ops per granule
-  static_assert(kVBlocks >= 1, "V granule smaller than one direct-to-LDS block");
+  static constexpr int kBuf = kGran * kRow;    // one K or V granule in LDS
+  static constexpr int kBlocks = kBuf / 1024;  // direct-to-LDS loads per granule per tensor
+  static constexpr int kOps = 2 * kBlocks;     // vector-memory ops per granule
+  static constexpr int kRowsPer256 = 256 / kRow;
+  static_assert(kBlocks >= 1, "granule smaller than one direct-to-LDS block");
 };
 
-// Chunk swizzle of an LDS V row (chunk c of row R lives in slot c ^ vswz(R));
-// makes the transpose reads of 4 rows x 32 bytes per 16-lane group conflict-free.
+// Chunk swizzles of the LDS rows (chunk c of row R lives in slot c ^ swz(R)).
+// V: makes the transpose reads of 4 rows x 32 bytes per 16-lane group
+// conflict-free. K: the 16 lanes of an A-operand read take one chunk of 16
+// consecutive rows; the swizzle spreads them over all 64 banks.
 __device__ __forceinline__ int vswz(int row, int nchunks) {
   return (((row & 3) << 2) | ((row >> 2) & 3)) & (nchunks - 1);
+}
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return (row / DTr<D>::kRowsPer256) & (DTr<D>::kCh - 1);
 }
 
 template <int N>
@@ -71,8 +78,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   using Tr = DTr<D>;
   // One LDS object per pipeline buffer, so the compiler can tell the
   // HBM->LDS copies into one buffer from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char vbuf0[Tr::kVBuf];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[Tr::kVBuf];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[Tr::kBuf];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[Tr::kBuf];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[Tr::kBuf];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[Tr::kBuf];
+  lds_char* const k0 = (lds_char*)kbuf0;
+  lds_char* const v0 = (lds_char*)vbuf0;
+  lds_char* const k1 = (lds_char*)kbuf1;
+  lds_char* const v1 = (lds_char*)vbuf1;
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x;
@@ -124,18 +137,22 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   const int64_t krow = a.k_sr * 2, vrow = a.v_sr * 2;   // bytes per key row
   const int L = lane & 15;
-  // K as the A operand, straight from HBM: lane (key 16 kb + L, group j4)
-  // loads K[key][32 st + 8 j4 .. +7].
-  auto k_off = [&](int kb, int st) -> int { return (int)((16 * kb + L) * krow) + 2 * (32 * st + 8 * j4); };
-  // V granule -> LDS: block q, lane l covers LDS bytes 1024 q + 16 l =
-  // (row R, slot sl) and fetches chunk sl ^ vswz(R) of row R.
-  int voff[Tr::kVBlocks];
+  // K and V granules -> LDS, whole rows per load: block q, lane l covers LDS
+  // bytes 1024 q + 16 l = (row R, slot sl) and fetches chunk sl ^ swz(R) of row R.
+  int koff[Tr::kBlocks], voff[Tr::kBlocks];
 #pragma unroll
-  for (int q = 0; q < Tr::kVBlocks; ++q) {
+  for (int q = 0; q < Tr::kBlocks; ++q) {
     const int B = 1024 * q + 16 * lane;
     const int R = B / Tr::kRow, sl = (B % Tr::kRow) / 16;
+    koff[q] = (int)(R * krow) + 16 * (sl ^ kswz<D>(R));
     voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz(R, Tr::kCh));
   }
+  // K A-operand reads: lane (key 16 kb + L, group j4) takes K[key][32 st + 8 j4 .. +7],
+  // chunk 4 st + j4 of row 16 kb + L, whose swizzle kswz(16 kb + L) = kswz(L) = ksw:
+  // slot (4 st + j4) ^ ksw = ((4 st) ^ (ksw & ~3)) + ((j4 ^ ksw) & 3).
+  const int ksw = kswz<D>(L);
+  const int k_lane0 = L * Tr::kRow + 16 * ((j4 ^ ksw) & 3);
+  const int k_hi = 16 * (ksw & ~3);
   // transpose reads: group j4 (16 lanes) reads rows 16 kb + 4 j4 + L / 4, bf16
   // columns 16 dblk + 4 (L & 3); vswz(row) = ((L >> 2) << 2) | j4 for these rows.
   const int v_sw = (((L >> 2) << 2) | j4) & (Tr::kCh - 1);
@@ -150,10 +167,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
     return (const char*)pool + ((int64_t)b * sb + (int64_t)g * sh + (int64_t)gs * sr) * 2;
   };
-  // issue the loads of granule gs: K into registers, V into LDS buffer vb.
-  // A granule at or past t_hi is issued with an empty range: no memory
-  // traffic, zeros everywhere.
-  auto issue = [&](int gs, U128 (&kf)[2][Tr::kSteps], char* vb) {
+  // issue the loads of granule gs into the LDS buffers kb / vb (whole rows,
+  // non-temporal: every K and V row is read once). A granule at or past t_hi is
+  // issued with an empty range: no memory traffic, zeros everywhere.
+  auto issue = [&](int gs, lds_char* kb, lds_char* vb) {
     // readfirstlane keeps the clamp (a vector med3) from making the
     // descriptor look divergent
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kGran, t_hi - gs)));
@@ -163,11 +180,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const __amdgpu_buffer_rsrc_t vr =
         make_rsrc(rows_base(gp, a.v, a.v_sb, a.v_sh, a.v_sr), (uint32_t)(rows * vrow));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int q = 0; q < Tr::kBlocks; ++q) buf_load16_lds_stream(kr, kb + 1024 * q, koff[q]);
 #pragma unroll
-      for (int st = 0; st < Tr::kSteps; ++st) kf[kb][st] = buf_load16(kr, k_off(kb, st));
-#pragma unroll
-    for (int q = 0; q < Tr::kVBlocks; ++q) buf_load16_lds_stream(vr, vb + 1024 * q, voff[q]);
+    for (int q = 0; q < Tr::kBlocks; ++q) buf_load16_lds_stream(vr, vb + 1024 * q, voff[q]);
   };
 
   const float c = a.c_exp2;
@@ -178,13 +193,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] = f32x4{};
 
   // one 32-key granule: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto compute = [&](int gs, const U128 (&kf)[2][Tr::kSteps], const char* vb) {
+  auto compute = [&](int gs, const lds_char* kbuf, const lds_char* vb) {
     f32x4 st[2];
+    int k_lane = k_lane0, k_x = k_hi;
+    asm volatile("" : "+v"(k_lane), "+v"(k_x));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      U128 kf[Tr::kSteps];
+#pragma unroll
+      for (int s = 0; s < Tr::kSteps; ++s)
+        kf[s] = lds_load16(kbuf + k_lane + 16 * kb * Tr::kRow + ((64 * s) ^ k_x));
       st[kb] = f32x4{};
 #pragma unroll
-      for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_bf16(as_bf16x8(kf[kb][s]), as_bf16x8(qf[s]), st[kb]);
+      for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st[kb]);
     }
     // lane (column qc, group j4) holds keys gs + 16 kb + 4 j4 + r
     float mt = kNegInf;
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     asm volatile("" : "+v"(v_base), "+v"(v_hi));
 #pragma unroll
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
-      const char* vp = vb + v_base + ((32 * dblk) ^ v_hi);
+      const lds_char* vp = vb + v_base + ((32 * dblk) ^ v_hi);
       const U64 v0 = lds_read_tr16(vp);
       const U64 v1 = lds_read_tr16(vp + 16 * Tr::kRow);
       acc[dblk] = mfma16_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
@@ -235,17 +256,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   int gs = t_lo;
   if (gs < t_hi) {
-    U128 kA[2][Tr::kSteps], kB[2][Tr::kSteps];
-    issue(gs, kA, vbuf0);
+    issue(gs, k0, v0);
     for (;;) {
-      issue(gs + kGran, kB, vbuf1);
+      issue(gs + kGran, k1, v1);
       wait_vmem_le<Tr::kOps>();
-      compute(gs, kA, vbuf0);
+      compute(gs, k0, v0);
       gs += kGran;
       if (gs >= t_hi) break;
-      issue(gs + kGran, kA, vbuf0);
+      issue(gs + kGran, k0, v0);
       wait_vmem_le<Tr::kOps>();
-      compute(gs, kB, vbuf1);
+      compute(gs, k1, v1);
       gs += kGran;
       if (gs >= t_hi) break;
     }
