@@ -255,15 +255,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const char* kt = kslot(slot);
     s0 = f32x16{};
     s1 = f32x16{};
+    if (FP8) {
 #pragma unroll
-    for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
-      const char* p = kt + k_addr(kk);
-      if (FP8) {
+      for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
+        const char* p = kt + k_addr(kk);
         s0 = mfma32_fp8(*(const U64*)p, *(const U64*)&qf[kk], s0);
         s1 = mfma32_fp8(*(const U64*)(p + 32 * Tr::kKRow), *(const U64*)&qf[kk], s1);
-      } else {
-        s0 = mfma32_bf16(as_bf16x8(*(const U128*)p), as_bf16x8(*(const U128*)&qf[kk]), s0);
-        s1 = mfma32_bf16(as_bf16x8(*(const U128*)(p + 32 * Tr::kKRow)), as_bf16x8(*(const U128*)&qf[kk]), s1);
+      }
+    } else {
+      // operands of step kk+1 are read while step kk's products run
+      U128 a0 = *(const U128*)(kt + k_addr(0));
+      U128 a1 = *(const U128*)(kt + k_addr(0) + 32 * Tr::kKRow);
+#pragma unroll
+      for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
+        U128 n0 = a0, n1 = a1;
+        if (kk + 1 < Tr::kQkSteps) {
+          n0 = *(const U128*)(kt + k_addr(kk + 1));
+          n1 = *(const U128*)(kt + k_addr(kk + 1) + 32 * Tr::kKRow);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = mfma32_bf16(as_bf16x8(a0), as_bf16x8(*(const U128*)&qf[kk]), s0);
+        s1 = mfma32_bf16(as_bf16x8(a1), as_bf16x8(*(const U128*)&qf[kk]), s1);
+        a0 = n0;
+        a1 = n1;
       }
     }
   };
