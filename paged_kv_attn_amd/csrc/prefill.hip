@@ -94,17 +94,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int wave = wave_id();
   const int h = lane >> 5;          // which half of the key / d sub-blocks this lane holds
   // XCD-aware work order. Workgroups are dispatched round-robin over the 8
-  // XCDs (hardware id w goes to XCD w % 8), each with its own L2. Give XCD x a
-  // contiguous range of the logical order, which runs (sequence, kv-head)-major
-  // so that all query tiles of one head, which read the same K/V, share an L2;
-  // within a head the heaviest (latest, under a causal mask) tiles come first.
-  const int n_wg = a.n_qtiles * a.hkv * a.nz;
-  const int per_xcd = (n_wg + kXcds - 1) / kXcds;
-  const int logical = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (logical >= n_wg) return;
-  const int qt_i = logical % a.n_qtiles;
-  const int g = (logical / a.n_qtiles) % a.hkv;    // kv-head
-  const int z = logical / (a.n_qtiles * a.hkv);    // batch entry or sequence
+  // XCDs (hardware id w goes to XCD w % 8), each with its own L2. A unit is one
+  // (sequence, kv-head): all its query tiles read the same K/V, so they run on
+  // one XCD and share its L2, one unit after another, heaviest (latest, under a
+  // causal mask) tile first. Units are dealt to the XCDs round-robin, so with
+  // sequences of different lengths every XCD still gets a similar share of the
+  // work (with Hkv a multiple of 8, XCD x takes kv-heads x, x+8, ... of every
+  // sequence).
+  const int n_units = a.hkv * a.nz;
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int k_x = (int)(blockIdx.x / kXcds);       // position in this XCD's list
+  const int unit = xcd + kXcds * (k_x / a.n_qtiles);
+  if (unit >= n_units) return;
+  const int qt_i = k_x % a.n_qtiles;
+  const int g = unit % a.hkv;                      // kv-head
+  const int z = unit / a.hkv;                      // batch entry or sequence
   const int qt = MASK ? a.n_qtiles - 1 - qt_i : qt_i;
 
   // ---- sequence geometry (batch: seqused; varlen: cumulative offsets) ----
@@ -459,8 +463,8 @@ template <int D, bool FP8, bool VARLEN, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
-  const int64_t n_wg = (int64_t)a.n_qtiles * a.hkv * nz;
-  const int64_t grid = (n_wg + kXcds - 1) / kXcds * kXcds;
+  const int64_t n_units = (int64_t)a.hkv * nz;
+  const int64_t grid = (n_units + kXcds - 1) / kXcds * kXcds * a.n_qtiles;
   hipLaunchKernelGGL((prefill_kernel<D, FP8, VARLEN, MASK, SOFTCAP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
