@@ -60,6 +60,18 @@ __device__ __forceinline__ U128 lds_load16(const lds_char* p) {
   return __builtin_bit_cast(U128, v);
 }
 
+// 8 bytes from LDS (ds_read_b64).
+__device__ __forceinline__ U64 lds_load8(const lds_char* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = *(const __attribute__((address_space(3))) u32x2*)p;
+  return __builtin_bit_cast(U64, v);
+}
+// 16 bytes to LDS (ds_write_b128).
+__device__ __forceinline__ void lds_store16(lds_char* p, const U128& x) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  *(__attribute__((address_space(3))) u32x4*)p = __builtin_bit_cast(u32x4, x);
+}
+
 __device__ __forceinline__ U64 lds_read_tr16(const lds_char* lds_addr) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_addr);
   return __builtin_bit_cast(U64, v);
@@ -115,6 +127,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int byte_off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, byte_off,
                                            0, 0, 0);
+}
+
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, lds_char* lds_wave_base, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, byte_off, 0, 0, 0);
 }
 
 // As buf_load16_lds, with the non-temporal cache policy: for data read once

@@ -178,8 +178,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const char* kh = (const char*)a.k + (k_off + (int64_t)g * a.k_sh) * Tr::kElem;
   const char* vh = (const char*)a.v + (v_off + (int64_t)g * a.v_sh) * Tr::kElem;
   const int64_t krow = a.k_sr * Tr::kElem, vrow = a.v_sr * Tr::kElem;  // global bytes per key row
-  auto kslot = [&](int slot) -> char* { return slot ? k_lds1 : k_lds0; };
-  auto vslot = [&](int slot) -> char* { return slot ? v_lds1 : v_lds0; };
+  // LDS addresses stay in the LDS address space (a generic pointer converted
+  // back would cost a null check per use)
+  lds_char* const kl0 = (lds_char*)k_lds0;
+  lds_char* const kl1 = (lds_char*)k_lds1;
+  lds_char* const vl0 = (lds_char*)v_lds0;
+  lds_char* const vl1 = (lds_char*)v_lds1;
+  auto kslot = [&](int slot) -> lds_char* { return slot ? kl1 : kl0; };
+  auto vslot = [&](int slot) -> lds_char* { return slot ? vl1 : vl0; };
   // Wave w fills LDS blocks w, w+4, ... (1 KiB each) of a tile; lane l of block q
   // covers LDS bytes 1024 q + 16 l = (row R, slot s), fetching global chunk s ^ swz(R).
   int koff[Tr::kKInstr], voff[Tr::kVInstr];
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   auto load_k = [&](int t, int slot) {
     const int j0 = t * kBlockN;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + j0 * krow, (uint32_t)(min(kBlockN, Lk - j0) * krow));
-    char* base = kslot(slot);
+    lds_char* base = kslot(slot);
 #pragma unroll
     for (int i = 0; i < Tr::kKInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), koff[i]);
   };
@@ -213,19 +219,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < Tr::kV8Loads; ++i)
         v8[i] = buf_load16(r, (int)((v8row + i * (kThreads / Tr::kV8Ch)) * vrow) + 16 * v8ch);
     } else {
-      char* base = vslot(slot);
+      lds_char* base = vslot(slot);
 #pragma unroll
       for (int i = 0; i < Tr::kVInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), voff[i]);
     }
   };
   auto store_v8 = [&](int slot) {  // fp8 only
-    char* base = vslot(slot);
+    lds_char* base = vslot(slot);
 #pragma unroll
     for (int i = 0; i < (FP8 ? Tr::kV8Loads : 0); ++i) {
       const int R = v8row + i * (kThreads / Tr::kV8Ch);
       const int c0 = 2 * v8ch;  // bf16 chunks 2c, 2c+1 of the row
-      *(U128*)(base + R * Tr::kVRow + 16 * (c0 ^ swz(R, Tr::kVCh))) = fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y});
-      *(U128*)(base + R * Tr::kVRow + 16 * ((c0 + 1) ^ swz(R, Tr::kVCh))) = fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w});
+      lds_store16(base + R * Tr::kVRow + 16 * (c0 ^ swz(R, Tr::kVCh)), fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y}));
+      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + 1) ^ swz(R, Tr::kVCh)), fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w}));
     }
   };
 
@@ -256,26 +262,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // S^T = K Q^T for the tile in K slot `slot`: two interleaved 32-key chains
   auto qk = [&](int slot, f32x16& s0, f32x16& s1) {
-    const char* kt = kslot(slot);
+    const lds_char* kt = kslot(slot);
     s0 = f32x16{};
     s1 = f32x16{};
     if (FP8) {
 #pragma unroll
       for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
-        const char* p = kt + k_addr(kk);
-        s0 = mfma32_fp8(*(const U64*)p, *(const U64*)&qf[kk], s0);
-        s1 = mfma32_fp8(*(const U64*)(p + 32 * Tr::kKRow), *(const U64*)&qf[kk], s1);
+        const lds_char* p = kt + k_addr(kk);
+        s0 = mfma32_fp8(lds_load8(p), *(const U64*)&qf[kk], s0);
+        s1 = mfma32_fp8(lds_load8(p + 32 * Tr::kKRow), *(const U64*)&qf[kk], s1);
       }
     } else {
       // operands of step kk+1 are read while step kk's products run
-      U128 a0 = *(const U128*)(kt + k_addr(0));
-      U128 a1 = *(const U128*)(kt + k_addr(0) + 32 * Tr::kKRow);
+      U128 a0 = lds_load16(kt + k_addr(0));
+      U128 a1 = lds_load16(kt + k_addr(0) + 32 * Tr::kKRow);
 #pragma unroll
       for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
         U128 n0 = a0, n1 = a1;
         if (kk + 1 < Tr::kQkSteps) {
-          n0 = *(const U128*)(kt + k_addr(kk + 1));
-          n1 = *(const U128*)(kt + k_addr(kk + 1) + 32 * Tr::kKRow);
+          n0 = lds_load16(kt + k_addr(kk + 1));
+          n1 = lds_load16(kt + k_addr(kk + 1) + 32 * Tr::kKRow);
         }
         __builtin_amdgcn_sched_barrier(0);
         s0 = mfma32_bf16(as_bf16x8(a0), as_bf16x8(*(const U128*)&qf[kk]), s0);
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] *= alpha;
     }
-    const char* vt = vslot(vs);
+    const lds_char* vt = vslot(vs);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
