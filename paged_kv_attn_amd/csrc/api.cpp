@@ -234,7 +234,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
   a.seqused_q = seqused_q; a.seqused_k = seqused_k;
   a.sq = sq; a.sk = sk; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
-  a.n_qtiles = (int)(((int64_t)sq * ratio + attn::prefill_rows_per_tile() - 1) / attn::prefill_rows_per_tile());
+  const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
+  a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
@@ -279,8 +280,8 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.lse_sb = 0; a.lse_sh = total_q;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
   a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
-  a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + attn::prefill_rows_per_tile() - 1) /
-                     attn::prefill_rows_per_tile());
+  const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
+  a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + rows_tile - 1) / rows_tile);
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;

@@ -142,6 +142,12 @@ __device__ __forceinline__ void buf_load16_lds_stream(__amdgpu_buffer_rsrc_t r, 
 // Wait until this wave's vector-memory loads (including loads into LDS) have
 // completed: s_waitcnt vmcnt(0) with the LDS and export counters left free.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// ... until at most N of them are outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 __device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -62,12 +62,6 @@ __device__ __forceinline__ int kswz(int row) {
   return (row / DTr<D>::kRowsPer256) & (DTr<D>::kCh - 1);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 __device__ __forceinline__ float xor_shfl(float x, int mask) {
   const int lane = threadIdx.x & 63;
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ mask) << 2), __builtin_bit_cast(int, x)));

@@ -89,7 +89,7 @@ struct F32Args {
   int wl, wr;
 };
 
-int prefill_rows_per_tile();  // packed query rows per prefill workgroup
+int prefill_rows_per_tile(int in_type);  // packed query rows per prefill workgroup
 hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, bool varlen, int batch_or_seqs,
                           hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, bool paged, int B,

@@ -491,7 +491,7 @@ hipError_t launch_d(const PrefillArgs& a, int in_type, bool varlen, int nz, bool
 
 }  // namespace
 
-int prefill_rows_per_tile() { return kBlockM; }
+int prefill_rows_per_tile(int) { return kBlockM; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, bool varlen, int nz, hipStream_t stream) {
   const bool mask = a.wl >= 0 || a.wr >= 0;
