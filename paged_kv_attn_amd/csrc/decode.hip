@@ -50,16 +50,20 @@ struct DTr {
   static_assert(kBlocks >= 1, "granule smaller than one direct-to-LDS block");
 };
 
-// Chunk swizzles of the LDS rows (chunk c of row R lives in slot c ^ swz(R)).
-// V: makes the transpose reads of 4 rows x 32 bytes per 16-lane group
-// conflict-free. K: the 16 lanes of an A-operand read take one chunk of 16
-// consecutive rows; the swizzle spreads them over all 64 banks.
-__device__ __forceinline__ int vswz(int row, int nchunks) {
-  return (((row & 3) << 2) | ((row >> 2) & 3)) & (nchunks - 1);
-}
+// Chunk swizzles of the LDS rows (chunk c of row R lives in slot c ^ swz(R));
+// 64 banks of 4 bytes, so rows of the same residue modulo 256 bytes share bank
+// offsets. K: the 16 lanes of an A-operand read (ds_read_b128) take one chunk
+// of 16 consecutive rows; the swizzle spreads them over all 64 banks. V: a
+// transpose read (ds_read_b64_tr_b16) of two 16-lane groups takes 8
+// consecutive rows x 2 adjacent chunks; the swizzle (bit 0 clear, so the pair
+// stays adjacent) gives the 8 rows 8 different chunk pairs.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
   return (row / DTr<D>::kRowsPer256) & (DTr<D>::kCh - 1);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return ((row / DTr<D>::kRowsPer256) & (DTr<D>::kCh / 2 - 1)) << 1;
 }
 
 __device__ __forceinline__ float xor_shfl(float x, int mask) {
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int B = 1024 * q + 16 * lane;
     const int R = B / Tr::kRow, sl = (B % Tr::kRow) / 16;
     koff[q] = (int)(R * krow) + 16 * (sl ^ kswz<D>(R));
-    voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz(R, Tr::kCh));
+    voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz<D>(R));
   }
   // K A-operand reads: lane (key 16 kb + L, group j4) takes K[key][32 st + 8 j4 .. +7],
   // chunk 4 st + j4 of row 16 kb + L, whose swizzle kswz(16 kb + L) = kswz(L) = ksw:
@@ -148,10 +152,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int k_lane0 = L * Tr::kRow + 16 * ((j4 ^ ksw) & 3);
   const int k_hi = 16 * (ksw & ~3);
   // transpose reads: group j4 (16 lanes) reads rows 16 kb + 4 j4 + L / 4, bf16
-  // columns 16 dblk + 4 (L & 3); vswz(row) = ((L >> 2) << 2) | j4 for these rows.
-  const int v_sw = (((L >> 2) << 2) | j4) & (Tr::kCh - 1);
-  const int v_base0 = (4 * j4 + (L >> 2)) * Tr::kRow + 16 * (((L & 3) >> 1) ^ (v_sw & 1)) + 8 * (L & 1);
-  const int v_swhi = 16 * (v_sw & ~1);
+  // columns 16 dblk + 4 (L & 3) .. +3 = byte 8 (L & 1) of chunk 2 dblk + (L & 3) / 2;
+  // those rows' swizzle vs = vswz(4 j4 + L / 4) has bit 0 clear, so the slot is
+  // (2 dblk ^ vs) + (L & 3) / 2.
+  const int v_sw = vswz<D>(4 * j4 + (L >> 2));
+  const int v_base0 = (4 * j4 + (L >> 2)) * Tr::kRow + 16 * ((L & 3) >> 1) + 8 * (L & 1);
+  const int v_swhi = 16 * v_sw;
 
   // base of the 32 keys starting at key gs (64-bit page base + in-page offset)
   auto rows_base = [&](int gs, const void* pool, int64_t sb, int64_t sh, int64_t sr) -> const char* {
