@@ -39,14 +39,14 @@ bool takes_decode_path(int in_dtype, int sq, int ratio) {
 }
 
 // Keys per split-KV work unit (one wave each): unless the caller fixes it, the
-// smallest power of two in [256, 2048] that keeps the (request, kv-head, split)
-// grid at or below 32768 units -- about 16 waves for each resident slot of the
-// chip, with at least 8 pipeline steps per wave.
+// largest power of two in [256, 2048] that still gives the (request, kv-head,
+// split) grid at least 4096 units, about three waves for each resident slot of
+// the chip. Long units stream longer; the kv-heads of one split run side by side.
 int plan_split_tokens(const attn_params_t* p, int B, int Hkv, int max_len) {
   if (p->kv_split_tokens > 0) return p->kv_split_tokens;
   const int64_t units = (int64_t)B * Hkv;
-  int c = 256;
-  while (c < 2048 && units * ((max_len + c - 1) / c) > 32768) c *= 2;
+  int c = 2048;
+  while (c > 256 && units * ((max_len + c - 1) / c) < 4096) c /= 2;
   return c;
 }
 

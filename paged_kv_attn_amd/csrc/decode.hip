@@ -86,8 +86,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   lds_char* const v1 = (lds_char*)vbuf1;
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  const int g = blockIdx.x;      // kv-heads fastest: the units running together read the
+  const int split = blockIdx.y;  // same token rows (shared DRAM pages in a [page, slot, head] pool)
   const int b = blockIdx.z;
   const int Lk = a.seqlens_k ? a.seqlens_k[b] : a.sk;
   const int t0 = split * a.split_tokens;
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 template <int D, bool PAGED, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_t s) {
-  dim3 grid(a.n_splits, a.hkv, B);
+  dim3 grid(a.hkv, a.n_splits, B);
   hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP>), grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

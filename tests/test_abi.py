@@ -121,6 +121,10 @@ def test_workspace_and_split_queries():
     p = _params()
     assert lib().attn_workspace_bytes(ctypes.byref(p), 4, 16, 16, 2048, 128, 2048) == 0   # prefill path
     assert lib().attn_num_splits(ctypes.byref(p), 4, 16, 16, 2048, 2048) == 1
+    # default split: the largest of 2048..256 keys that still gives >= 4096 units
+    assert lib().attn_num_splits(ctypes.byref(p), 64, 32, 8, 1, 32768) == 16     # 2048-key splits
+    assert lib().attn_num_splits(ctypes.byref(p), 1, 32, 8, 1, 32768) == 128     # 256-key floor
+    assert lib().attn_num_splits(ctypes.byref(p), 8, 32, 8, 1, 32768) == 64      # 512: 64 units x 64 = 4096
     p.kv_split_tokens = 256
     assert lib().attn_num_splits(ctypes.byref(p), 64, 32, 8, 1, 32768) == 128
     ws = lib().attn_workspace_bytes(ctypes.byref(p), 64, 32, 8, 1, 128, 32768)
