@@ -134,17 +134,21 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Paged-KV mode (decode). Q [B, Hq, sq, d] and O [B, Hq, sq, d] strided as in
- * attn_fwd; K and V live in page pools of num_pages pages of page_size tokens,
+ * Paged-KV mode. Q [B, Hq, sq, d] and O [B, Hq, sq, d] strided as in attn_fwd;
+ * K and V live in page pools of num_pages pages of page_size tokens,
  * addressed as pool + page*kv_stride[0] + head*kv_stride[1] + slot*kv_stride[2] + c
  * (64-bit offsets). Token t of request b is slot t % page_size of page
  * block_table[b*block_table_stride + t / page_size] (the page-block navigator
  * of the Composable Kernel page: block_table_ptr, batch_stride_block_table,
  * page_block_size). seqlens_k (int32 [B], device) gives Lk per request;
- * Lq = sq. page_size must be a multiple of 32; block_table_stride * page_size
- * bounds every Lk. Requires sq * Hq / Hkv <= 16 (decode shapes). lse (nullable)
- * is fp32 [B, Hq, sq]. Needs a workspace of attn_workspace_bytes() bytes with
- * max_seqlen_k = block_table_stride * page_size.
+ * Lq = sq (bottom-right aligned mask). block_table_stride * page_size bounds
+ * every Lk. lse (nullable) is fp32 [B, Hq, sq].
+ *   - Decode shapes (sq * Hq / Hkv <= 16): BF16 only, page_size a multiple of
+ *     32, split-KV kernel + combine; needs a workspace of attn_workspace_bytes()
+ *     bytes with max_seqlen_k = block_table_stride * page_size.
+ *   - Longer query blocks (paged prefill, e.g. chunked prefill into a cache):
+ *     BF16 or FP8_E4M3 (with descales), page_size a multiple of 64 (one page per
+ *     64-key tile), the prefill kernel; no workspace.
  */
 attn_status_t attn_fwd_paged(const attn_params_t* p,
                              const void* q, const void* k_pool, const void* v_pool,

@@ -245,18 +245,20 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
     then the batch definition is applied (all sq query rows valid). ``decode``
     (default: cast to fp64) maps the gathered stored values to exact fp64, so a
     large pool can stay in its stored format and only the used pages are
-    decoded. Returns O [B, Hq, sq, dv] and LSE [B, Hq, sq].
+    decoded; a (decode_k, decode_v) pair decodes the two pools differently
+    (per-tensor fp8 scales). Returns O [B, Hq, sq, dv] and LSE [B, Hq, sq].
     """
     if decode is None:
         decode = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
+    dec_k, dec_v = decode if isinstance(decode, tuple) else (decode, decode)
     q = np.asarray(q, dtype=np.float64)
     b_, hq, sq, _ = q.shape
     o = np.full((b_, hq, sq, v_pool.shape[3]), np.nan)
     lse = np.full((b_, hq, sq), np.nan)
 
     def job(b):
-        ks = decode(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]
-        vs = decode(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]
+        ks = dec_k(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]
+        vs = dec_v(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]
         return b, attention_batch(q[b:b + 1], ks, vs, scale, softcap, window_left, window_right)
 
     for b, (ob, lb) in _map_pool(job, list(range(b_)), workers):

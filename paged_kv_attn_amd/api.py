@@ -118,10 +118,13 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
-                   softcap=0.0, out=None, lse=None, return_lse=True, kv_split_tokens=0, workspace=None):
-    """Paged-KV decode. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
+                   softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
+                   workspace=None):
+    """Paged KV cache. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
     (any strides, d contiguous; K and V pools with equal strides);
-    block_table int32 [B, W]; seqlens_k int32 [B]. Returns (out, lse)."""
+    block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
+    (sq * Hq / Hkv <= 16, bf16) run the split-KV decode kernel; longer ones
+    (bf16 or fp8, page_size a multiple of 64) the prefill kernel. Returns (out, lse)."""
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if k_pool.stride() != v_pool.stride():
@@ -129,7 +132,7 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
     W = block_table.shape[1]
-    p = _params(q.dtype, d, scale, causal, window, softcap, (1.0, 1.0, 1.0), kv_split_tokens)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens)
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:

@@ -239,7 +239,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
-  return launched(attn::launch_prefill(a, d, p->in_dtype, false, B, s));
+  return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillBatch, B, s));
 }
 
 attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
@@ -285,7 +285,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
-  return launched(attn::launch_prefill(a, d, p->in_dtype, true, n, (hipStream_t)stream));
+  return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillVarlen, n, (hipStream_t)stream));
 }
 
 attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* k_pool, const void* v_pool, void* o,
@@ -299,23 +299,51 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
                 block_table_stride, num_pages);
   if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
   if (page_size <= 0 || page_size % 32) return fail(ATTN_ENOTSUP, "page_size %d is not a positive multiple of 32", page_size);
-  if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "paged KV supports bf16 only");
+  if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "paged KV supports bf16 and fp8 inputs");
   const int ratio = Hq / Hkv;
-  if (!takes_decode_path(p->in_dtype, sq, ratio))
-    return fail(ATTN_ENOTSUP, "paged KV needs sq*Hq/Hkv <= 16 (got %d)", sq * ratio);
+  const bool decode_shape = takes_decode_path(p->in_dtype, sq, ratio);
+  if (decode_shape && p->in_dtype != ATTN_BF16)
+    return fail(ATTN_ENOTSUP, "the paged decode path (sq*Hq/Hkv <= 16) supports bf16 only");
+  if (!decode_shape && page_size % 64)
+    return fail(ATTN_ENOTSUP, "paged prefill (sq*Hq/Hkv > 16) needs page_size a multiple of 64 (got %d)", page_size);
   if (!block_table || !seqlens_k) return fail(ATTN_EINVAL, "block_table / seqlens_k is NULL");
   TRY(check_ptr("q", q));
   TRY(check_ptr("k_pool", k_pool));
   TRY(check_ptr("v_pool", v_pool));
   TRY(check_ptr("o", o));
   if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
-  TRY(check_strides("q", q_stride, 3, 2));
-  TRY(check_strides("kv", kv_stride, 3, 2));
+  const int eb = elem_bytes(p->in_dtype);
+  TRY(check_strides("q", q_stride, 3, eb));
+  TRY(check_strides("kv", kv_stride, 3, eb));
   TRY(check_strides("o", o_stride, 3, 2));
   if (B == 0 || sq == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
   const int max_len = (int)max_len64;
+  float c_exp2, pre, post;
+  logit_consts(p, &c_exp2, &pre, &post);
+
+  if (!decode_shape) {
+    // paged prefill: the prefill kernel, with each 64-key tile's rows found
+    // through the block table
+    attn::PrefillArgs a{};
+    a.q = q; a.k = k_pool; a.v = v_pool; a.o = o; a.lse = lse;
+    a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
+    a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
+    a.v_sb = kv_stride[0]; a.v_sh = kv_stride[1]; a.v_sr = kv_stride[2];
+    a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_sr = o_stride[2];
+    a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
+    a.seqused_q = nullptr; a.seqused_k = seqlens_k;
+    a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
+    a.sq = sq; a.sk = max_len; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
+    const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
+    a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);
+    a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+    a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
+    a.wl = p->window_left; a.wr = p->window_right;
+    return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
+  }
+
   const int split = plan_split_tokens(p, B, Hkv, max_len);
   const int nsp = n_splits_for(split, max_len);
   const int m_rows = sq * ratio;
@@ -323,8 +351,6 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
   TRY(check_ptr("workspace", workspace));
-  float c_exp2, pre, post;
-  logit_consts(p, &c_exp2, &pre, &post);
   attn::DecodeArgs a{};
   a.q = q; a.k = k_pool; a.v = v_pool;
   a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];

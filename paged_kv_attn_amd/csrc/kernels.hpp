@@ -8,6 +8,9 @@
 namespace attn {
 
 enum InType : int { kInF32 = 0, kInBF16 = 1, kInFP8 = 2 };
+// prefill addressing modes: batch [B, H, S, d]; varlen (cu_seqlens); paged
+// (K/V rows through a block table, Lq = sq, Lk = seqlens_k)
+enum PrefillMode : int { kPrefillBatch = 0, kPrefillVarlen = 1, kPrefillPaged = 2 };
 
 // Prefill (one workgroup = 128 packed query rows of one sequence and kv-head).
 struct PrefillArgs {
@@ -18,12 +21,15 @@ struct PrefillArgs {
   float* lse;                 // nullable
   // element strides: batch (0 in varlen mode), head, row/token
   int64_t q_sb, q_sh, q_sr;
-  int64_t k_sb, k_sh, k_sr;
+  int64_t k_sb, k_sh, k_sr;   // paged mode: page, head, slot
   int64_t v_sb, v_sh, v_sr;
   int64_t o_sb, o_sh, o_sr;
   int64_t lse_sb, lse_sh;     // lse index = b*lse_sb + h*lse_sh + token
   const int32_t* seqused_q;   // batch mode, nullable
-  const int32_t* seqused_k;   // batch mode, nullable
+  const int32_t* seqused_k;   // batch mode, nullable; paged mode: seqlens_k (required)
+  const int32_t* block_table; // paged mode: [nz][bt_stride] page ids
+  int64_t bt_stride;
+  int page_size;              // paged mode: a multiple of 64 (one page per 64-key tile)
   const int32_t* cu_q;        // varlen mode (non-null selects varlen)
   const int32_t* cu_k;
   int sq, sk;                 // batch-mode extents
@@ -90,7 +96,7 @@ struct F32Args {
 };
 
 int prefill_rows_per_tile(int in_type);  // packed query rows per prefill workgroup
-hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, bool varlen, int batch_or_seqs,
+hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, int mode, int batch_or_seqs,
                           hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, bool paged, int B,
                          hipStream_t stream);

@@ -78,7 +78,7 @@ template <bool FP8> struct QFrag;
 template <> struct QFrag<false> { using T = U128; };
 template <> struct QFrag<true> { using T = U64; };
 
-template <int D, bool FP8, bool VARLEN, bool MASK, bool SOFTCAP>
+template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Tr = Traits<D, FP8>;
   using QT = typename QFrag<FP8>::T;
@@ -111,7 +111,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int z = unit / a.hkv;                      // batch entry or sequence
   const int qt = MASK ? a.n_qtiles - 1 - qt_i : qt_i;
 
-  // ---- sequence geometry (batch: seqused; varlen: cumulative offsets) ----
+  // ---- sequence geometry (batch: seqused; varlen: cumulative offsets; paged:
+  // Lq = sq, Lk = seqlens_k, K/V rows found through the block table) ----
+  constexpr bool VARLEN = MODE == kPrefillVarlen;
+  constexpr bool PAGED = MODE == kPrefillPaged;
   int Lq, Lk;
   int64_t q_off, k_off, v_off, o_off, lse_off;
   if (VARLEN) {
@@ -123,6 +126,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     v_off = (int64_t)k0 * a.v_sr;
     o_off = (int64_t)q0 * a.o_sr;
     lse_off = q0;
+  } else if (PAGED) {
+    Lq = a.sq;
+    Lk = a.seqused_k[z];
+    q_off = (int64_t)z * a.q_sb;
+    k_off = 0;  // pool base; pages are found per tile
+    v_off = 0;
+    o_off = (int64_t)z * a.o_sb;
+    lse_off = (int64_t)z * a.lse_sb;
   } else {
     Lq = a.seqused_q ? a.seqused_q[z] : a.sq;
     Lk = a.seqused_k ? a.seqused_k[z] : a.sk;
@@ -177,6 +188,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // ---- K/V staging: HBM -> LDS directly; rows past Lk arrive as zeros ----
   const char* kh = (const char*)a.k + (k_off + (int64_t)g * a.k_sh) * Tr::kElem;
   const char* vh = (const char*)a.v + (v_off + (int64_t)g * a.v_sh) * Tr::kElem;
+  // start of the 64 rows of tile j0 / 64: contiguous, or (paged) the tile's page
+  // (page_size is a multiple of 64, so a tile never straddles two pages) plus the
+  // in-page offset, as in the page-block navigator of the Composable Kernel page
+  auto tile_rows = [&](const char* head_base, int64_t page_stride, int64_t row_bytes, int j0) -> const char* {
+    if (PAGED) {
+      const int page = a.block_table[(int64_t)z * a.bt_stride + j0 / a.page_size];
+      return head_base + (int64_t)page * page_stride * Tr::kElem + (int64_t)(j0 % a.page_size) * row_bytes;
+    }
+    return head_base + j0 * row_bytes;
+  };
   const int64_t krow = a.k_sr * Tr::kElem, vrow = a.v_sr * Tr::kElem;  // global bytes per key row
   // LDS addresses stay in the LDS address space (a generic pointer converted
   // back would cost a null check per use)
@@ -203,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
   auto load_k = [&](int t, int slot) {
     const int j0 = t * kBlockN;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + j0 * krow, (uint32_t)(min(kBlockN, Lk - j0) * krow));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(kh, a.k_sb, krow, j0), (uint32_t)(min(kBlockN, Lk - j0) * krow));
     lds_char* base = kslot(slot);
 #pragma unroll
     for (int i = 0; i < Tr::kKInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), koff[i]);
@@ -213,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int v8ch = threadIdx.x % Tr::kV8Ch, v8row = threadIdx.x / Tr::kV8Ch;
   auto load_v = [&](int t, int slot) {
     const int j0 = t * kBlockN;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + j0 * vrow, (uint32_t)(min(kBlockN, Lk - j0) * vrow));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(vh, a.v_sb, vrow, j0), (uint32_t)(min(kBlockN, Lk - j0) * vrow));
     if (FP8) {
 #pragma unroll
       for (int i = 0; i < Tr::kV8Loads; ++i)
@@ -465,40 +486,45 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool FP8, bool VARLEN, bool MASK, bool SOFTCAP>
+template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
   const int64_t n_units = (int64_t)a.hkv * nz;
   const int64_t grid = (n_units + kXcds - 1) / kXcds * kXcds * a.n_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, VARLEN, MASK, SOFTCAP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, MODE, MASK, SOFTCAP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
 
-template <int D, bool FP8, bool VARLEN>
+template <int D, bool FP8, int MODE>
 hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (mask) return softcap ? launch_t<D, FP8, VARLEN, true, true>(a, nz, s) : launch_t<D, FP8, VARLEN, true, false>(a, nz, s);
-  return softcap ? launch_t<D, FP8, VARLEN, false, true>(a, nz, s) : launch_t<D, FP8, VARLEN, false, false>(a, nz, s);
+  if (mask) return softcap ? launch_t<D, FP8, MODE, true, true>(a, nz, s) : launch_t<D, FP8, MODE, true, false>(a, nz, s);
+  return softcap ? launch_t<D, FP8, MODE, false, true>(a, nz, s) : launch_t<D, FP8, MODE, false, false>(a, nz, s);
+}
+
+template <int D, bool FP8>
+hipError_t launch_f(const PrefillArgs& a, int mode, int nz, bool mask, bool softcap, hipStream_t s) {
+  if (mode == kPrefillVarlen) return launch_m<D, FP8, kPrefillVarlen>(a, nz, mask, softcap, s);
+  if (mode == kPrefillPaged) return launch_m<D, FP8, kPrefillPaged>(a, nz, mask, softcap, s);
+  return launch_m<D, FP8, kPrefillBatch>(a, nz, mask, softcap, s);
 }
 
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, int in_type, bool varlen, int nz, bool mask, bool softcap,
-                    hipStream_t s) {
-  if (in_type == kInFP8)
-    return varlen ? launch_m<D, true, true>(a, nz, mask, softcap, s) : launch_m<D, true, false>(a, nz, mask, softcap, s);
-  return varlen ? launch_m<D, false, true>(a, nz, mask, softcap, s) : launch_m<D, false, false>(a, nz, mask, softcap, s);
+hipError_t launch_d(const PrefillArgs& a, int in_type, int mode, int nz, bool mask, bool softcap, hipStream_t s) {
+  if (in_type == kInFP8) return launch_f<D, true>(a, mode, nz, mask, softcap, s);
+  return launch_f<D, false>(a, mode, nz, mask, softcap, s);
 }
 
 }  // namespace
 
 int prefill_rows_per_tile(int) { return kBlockM; }
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, bool varlen, int nz, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, int mode, int nz, hipStream_t stream) {
   const bool mask = a.wl >= 0 || a.wr >= 0;
   const bool softcap = a.softcap_pre != 0.0f;
   if (a.n_qtiles <= 0 || nz <= 0 || a.hkv <= 0) return hipSuccess;
-  if (d == 128) return launch_d<128>(a, in_type, varlen, nz, mask, softcap, stream);
-  return launch_d<64>(a, in_type, varlen, nz, mask, softcap, stream);
+  if (d == 128) return launch_d<128>(a, in_type, mode, nz, mask, softcap, stream);
+  return launch_d<64>(a, in_type, mode, nz, mask, softcap, stream);
 }
 
 }  // namespace attn

@@ -44,7 +44,8 @@ def run_varlen(case, **kw):
 def run_paged(case, **kw):
     t = case.t
     return pk.attn_fwd_paged(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"], scale=case.scale,
-                             window=(case.window_left, case.window_right), softcap=case.softcap, **kw)
+                             window=(case.window_left, case.window_right), softcap=case.softcap,
+                             descale=(case.descale["q"], case.descale["k"], case.descale["v"]), **kw)
 
 
 def oracle_dense(case, workers=8):
@@ -71,15 +72,21 @@ def oracle_paged(case, requests=None, workers=8):
     vp = t["v_pool"].detach().cpu()
     table = t["block_table"].cpu().numpy()
     lens = t["seqlens_k"].cpu().numpy()
-    q = decode(t["q"], case.dtype)
+    ds = case.descale
+    q = decode(t["q"], case.dtype, ds["q"])
     idx = list(range(q.shape[0])) if requests is None else list(requests)
-    dec = lambda a: decode(torch.from_numpy(np.ascontiguousarray(a)), case.dtype)  # noqa: E731
-    kb = kp.view(torch.int16).numpy() if case.dtype == "bf16" else kp.numpy()
-    vb = vp.view(torch.int16).numpy() if case.dtype == "bf16" else vp.numpy()
     if case.dtype == "bf16":
-        dec = lambda a: oracle.bf16_bits_to_f64(a)  # noqa: E731
+        kb, vb = kp.view(torch.int16).numpy(), vp.view(torch.int16).numpy()
+        dk = dv = oracle.bf16_bits_to_f64
+    elif case.dtype == "fp8":
+        kb, vb = kp.view(torch.uint8).numpy(), vp.view(torch.uint8).numpy()
+        dk = lambda a: oracle.e4m3fn_bits_to_f64(np.ascontiguousarray(a), ds["k"])  # noqa: E731
+        dv = lambda a: oracle.e4m3fn_bits_to_f64(np.ascontiguousarray(a), ds["v"])  # noqa: E731
+    else:
+        kb, vb = kp.numpy(), vp.numpy()
+        dk = dv = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
     return oracle.attention_paged(q[idx], kb, vb, table[idx], lens[idx], case.scale, case.softcap,
-                                  case.window_left, case.window_right, workers=workers, decode=dec)
+                                  case.window_left, case.window_right, workers=workers, decode=(dk, dv))
 
 
 def to_np(x):

@@ -142,7 +142,7 @@ def _paged(p, page=64, sq=1, Hq=8, Hkv=2, table=FAKE, lens=FAKE, ws=FAKE, wsb=1 
 
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(page=48), 2, "page_size"),
-    (dict(sq=8), 2, "sq*Hq/Hkv"),
+    (dict(sq=8, page=32), 2, "multiple of 64"),      # paged prefill tiles are 64 keys
     (dict(table=NULL), 1, "block_table"),
     (dict(lens=NULL), 1, "seqlens_k"),
     (dict(ws=NULL), 3, "workspace"),
@@ -155,9 +155,11 @@ def test_attn_fwd_paged_rejects_bad_arguments(kw, status, msg):
     assert msg in _err()
 
 
-def test_paged_rejects_non_bf16():
+def test_paged_rejects_unsupported_types():
     p = _params(in_dtype=_lib.ATTN_FP8_E4M3, out_dtype=_lib.ATTN_BF16)
-    assert _paged(p) == 2
+    assert _paged(p) == 2 and "bf16 only" in _err()           # fp8 decode shape
+    p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)
+    assert _paged(p, sq=64) == 2 and "bf16 and fp8" in _err()
 
 
 def test_varlen_rejects_bad_arguments():
