@@ -87,30 +87,42 @@ def e4m3fn_bits_to_f64(bits, descale: float = 1.0) -> np.ndarray:
 # The definition for one (sequence, q-head).
 # ----------------------------------------------------------------------------
 
-def masked_allowed(rows: np.ndarray, lq: int, lk: int, window_left: int, window_right: int) -> np.ndarray:
+def masked_allowed(rows: np.ndarray, lq: int, lk: int, window_left: int, window_right: int,
+                   sink_size: int = 0) -> np.ndarray:
     """Boolean [len(rows), lk]: which keys each query row may attend to.
 
     Bottom-right aligned local window (``window_size_left/right`` of the
-    Composable Kernel page's mask arguments); negative = unbounded.
+    Composable Kernel page's mask arguments); negative = unbounded. The first
+    ``sink_size`` keys (the page's ``sink_size`` mask argument: streaming
+    sinks) are visible to every row whose right bound reaches them, whatever
+    the left bound.
     """
     i = np.asarray(rows, dtype=np.int64)[:, None]
     j = np.arange(lk, dtype=np.int64)[None, :]
     off = lk - lq
-    allowed = np.ones((i.shape[0], lk), dtype=bool)
+    left = np.ones((i.shape[0], lk), dtype=bool)
+    right = np.ones((i.shape[0], lk), dtype=bool)
     if window_left >= 0:
-        allowed &= j >= i + off - window_left
+        left = j >= i + off - window_left
     if window_right >= 0:
-        allowed &= j <= i + off + window_right
-    return allowed
+        right = j <= i + off + window_right
+    return (left | (j < sink_size)) & right
 
 
-def head_attention(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1, return_probs=False):
+def head_attention(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1, return_probs=False,
+                   sink_size=0, sink_logit=-np.inf):
     """Attention of one head: q [Lq, d], k [Lk, d], v [Lk, dv] (fp64).
 
     Returns O [Lq, dv] and LSE [Lq] (and P [Lq, Lk] if ``return_probs``).
     Steps, in the order of the Composable Kernel page's math contract:
     S = scale * Q K^T; optional soft-cap; mask; row softmax; O = P V;
     LSE = m + ln l. Rows with no visible key: O = 0, LSE = -inf.
+
+    ``sink_logit`` (the per-head value behind the page's ``sink_ptr``, in the
+    units of the scaled, soft-capped logits): one more term exp(sink_logit) in
+    every row's softmax denominator, with no value row, so
+    l = sum_j exp(S_ij - m) + exp(sink_logit - m), m = max(max_j S_ij, sink_logit).
+    A row with no visible key then gets O = 0 and LSE = sink_logit.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -120,26 +132,29 @@ def head_attention(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1,
     o = np.zeros((lq, dv), dtype=np.float64)
     lse = np.full((lq,), -np.inf, dtype=np.float64)
     probs = np.zeros((lq, lk), dtype=np.float64) if return_probs else None
+    sink = float(sink_logit)
     if lq == 0 or lk == 0:
+        lse[:] = sink  # no key at all: only the sink term (or nothing) in the denominator
         return (o, lse, probs) if return_probs else (o, lse)
     for r0 in range(0, lq, _ROW_BLOCK):
         rows = np.arange(r0, min(lq, r0 + _ROW_BLOCK))
         s = scale * (q[rows] @ k.T)
         if softcap > 0:
             s = softcap * np.tanh(s / softcap)
-        allowed = masked_allowed(rows, lq, lk, window_left, window_right)
+        allowed = masked_allowed(rows, lq, lk, window_left, window_right, sink_size)
         has = allowed.any(axis=1)
         if not has.any():
+            lse[rows] = sink
             continue
         s_m = np.where(allowed, s, -np.inf)
-        m = s_m.max(axis=1)
+        m = np.maximum(s_m.max(axis=1), sink)
         m_safe = np.where(has, m, 0.0)
         e = np.where(allowed, np.exp(s_m - m_safe[:, None]), 0.0)
-        l = e.sum(axis=1)
+        l = e.sum(axis=1) + (np.exp(sink - m_safe) if sink > -np.inf else 0.0)
         l_safe = np.where(has, l, 1.0)
         p = e / l_safe[:, None]
         o[rows] = np.where(has[:, None], p @ v, 0.0)
-        lse[rows] = np.where(has, m_safe + np.log(l_safe), -np.inf)
+        lse[rows] = np.where(has, m_safe + np.log(l_safe), sink)
         if return_probs:
             probs[rows] = p
     return (o, lse, probs) if return_probs else (o, lse)
@@ -157,11 +172,12 @@ def _map_pool(fn, jobs, workers):
 # ----------------------------------------------------------------------------
 
 def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1,
-                    seqused_q=None, seqused_k=None, workers=1):
+                    seqused_q=None, seqused_k=None, workers=1, sink_size=0, sink_logits=None):
     """Batch mode: q [B, Hq, sq, d], k/v [B, Hkv, sk, d] (fp64).
 
     Per batch b the used lengths are Lq = seqused_q[b] (else sq) and
     Lk = seqused_k[b] (else sk); q-head h reads kv-head h // (Hq // Hkv).
+    ``sink_size`` and ``sink_logits`` ([Hq] or None) as in head_attention.
     Returns O [B, Hq, sq, dv] and LSE [B, Hq, sq]; rows at or beyond Lq are not
     defined by the method and are left NaN.
     """
@@ -181,8 +197,9 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
         lq = sq if seqused_q is None else int(seqused_q[b])
         lk = k.shape[2] if seqused_k is None else int(seqused_k[b])
         g = h // ratio
+        sink = -np.inf if sink_logits is None else float(sink_logits[h])
         oh, lh = head_attention(q[b, h, :lq], k[b, g, :lk], v[b, g, :lk], scale, softcap,
-                                window_left, window_right)
+                                window_left, window_right, sink_size=sink_size, sink_logit=sink)
         return b, h, lq, oh, lh
 
     for b, h, lq, oh, lh in _map_pool(job, [(b, h) for b in range(b_) for h in range(hq)], workers):
@@ -192,7 +209,7 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
-                     window_left=-1, window_right=-1, workers=1):
+                     window_left=-1, window_right=-1, workers=1, sink_size=0, sink_logits=None):
     """Varlen / group mode: sequences packed along the token axis.
 
     q [Tq, Hq, d], k/v [Tk, Hkv, d]; sequence s owns query tokens
@@ -214,7 +231,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
         ks = k[ck[s]:ck[s + 1]].transpose(1, 0, 2)[None]
         vs = v[ck[s]:ck[s + 1]].transpose(1, 0, 2)[None]
         os_, ls_ = attention_batch(qs, ks, vs, scale, softcap, window_left, window_right,
-                                   workers=workers)
+                                   workers=workers, sink_size=sink_size, sink_logits=sink_logits)
         o[cq[s]:cq[s + 1]] = os_[0].transpose(1, 0, 2)
         lse[:, cq[s]:cq[s + 1]] = ls_[0]
     return o, lse
@@ -237,7 +254,7 @@ def gather_paged(pool, block_table_row, seqlen):
 
 
 def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.0,
-                    window_left=-1, window_right=-1, workers=1, decode=None):
+                    window_left=-1, window_right=-1, workers=1, decode=None, sink_size=0, sink_logits=None):
     """Paged-KV mode: q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d];
     block_table [B, max_pages] int; seqlens_k [B].
 
@@ -259,7 +276,8 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
     def job(b):
         ks = dec_k(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]
         vs = dec_v(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]
-        return b, attention_batch(q[b:b + 1], ks, vs, scale, softcap, window_left, window_right)
+        return b, attention_batch(q[b:b + 1], ks, vs, scale, softcap, window_left, window_right,
+                                  sink_size=sink_size, sink_logits=sink_logits)
 
     for b, (ob, lb) in _map_pool(job, list(range(b_)), workers):
         o[b] = ob[0]

@@ -315,3 +315,88 @@ def test_bf16_decode_matches_torch():
     np.testing.assert_array_equal(dec, x.to(torch.float64).numpy())
     assert oracle.bf16_bits_to_f64(np.array([0x3F80], dtype=np.uint16))[0] == 1.0
     assert oracle.bf16_bits_to_f64(np.array([0xC000], dtype=np.uint16))[0] == -2.0
+
+
+# ---------------------------------------------------------------------------
+# Attention sinks: streaming sink keys (the mask's sink_size) and a per-head
+# sink logit (an extra softmax-denominator term with no value row).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(30))
+def test_sinks_match_brute_force(seed):
+    rng = np.random.default_rng(1000 + seed)
+    Hkv, ratio, B = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    Hq = Hkv * ratio
+    sq, sk, d = int(rng.integers(1, 10)), int(rng.integers(1, 12)), int(rng.integers(1, 7))
+    q, k, v = _rand_case(rng, B, Hq, Hkv, sq, sk, d)
+    scale = float(rng.uniform(0.2, 1.5))
+    softcap = float(rng.choice([0.0, 0.0, 2.0]))
+    wl = int(rng.choice([-1, 0, 1, 2, 4]))
+    wr = int(rng.choice([-1, 0, 0, 1]))
+    sink_size = int(rng.integers(0, 4))
+    sinks = rng.uniform(-3.0, 3.0, size=Hq) if seed % 2 == 0 else None
+    if sinks is not None and seed % 6 == 0:
+        sinks[0] = -np.inf            # one head without a sink term
+    o, lse = oracle.attention_batch(q, k, v, scale, softcap, wl, wr, sink_size=sink_size, sink_logits=sinks)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // ratio
+            sink = None if sinks is None or sinks[h] == -np.inf else float(sinks[h])
+            bo, bl = brute_head(q[b, h].tolist(), k[b, g].tolist(), v[b, g].tolist(), scale, softcap, wl, wr,
+                                sink_size=sink_size, sink=sink)
+            np.testing.assert_allclose(o[b, h], np.array(bo).reshape(sq, d), atol=1e-12, rtol=0)
+            np.testing.assert_array_equal(np.isinf(lse[b, h]), np.isinf(bl))
+            fin = np.isfinite(bl)
+            np.testing.assert_allclose(lse[b, h][fin], np.array(bl)[fin], atol=1e-12, rtol=0)
+
+
+def test_sink_logit_closed_forms():
+    """Q = 0: every visible logit is 0, so with n visible keys and sink s the
+    weights are 1 / (n + e^s): O = (sum of visible V rows) / (n + e^s) and
+    LSE = ln(n + e^s). A row with no visible key: O = 0, LSE = s."""
+    rng = np.random.default_rng(21)
+    lq, lk, wl, sink = 6, 9, 2, 0.75
+    q = np.zeros((lq, 3))
+    k = rng.standard_normal((lk, 3))
+    v = rng.standard_normal((lk, 3))
+    o, lse = oracle.head_attention(q, k, v, 1.0, 0.0, wl, 0, sink_logit=sink)
+    for i in range(lq):
+        js = [j for j in range(lk) if i + lk - lq - wl <= j <= i + lk - lq]
+        n = len(js)
+        np.testing.assert_allclose(o[i], v[js].sum(axis=0) / (n + math.exp(sink)), atol=1e-12)
+        assert abs(lse[i] - math.log(n + math.exp(sink))) < 1e-12
+    # no key at all, and keys all outside the window (sq > sk under a causal bound)
+    o2, lse2 = oracle.head_attention(q[:2], k[:0], v[:0], 1.0, 0.0, -1, -1, sink_logit=sink)
+    assert np.all(o2 == 0) and np.all(lse2 == sink)
+    o3, lse3 = oracle.head_attention(np.zeros((5, 3)), k[:2], v[:2], 1.0, 0.0, -1, 0, sink_logit=sink)
+    assert np.all(o3[:3] == 0) and np.all(lse3[:3] == sink)     # rows 0..2 precede every key
+    assert abs(lse3[4] - math.log(2 + math.exp(sink))) < 1e-12
+
+
+def test_sink_logit_limits():
+    rng = np.random.default_rng(22)
+    q, k, v = _rand_case(rng, 1, 2, 1, 7, 11, 5)
+    base_o, base_l = oracle.attention_batch(q, k, v, 0.5, 0.0, -1, 0)
+    o, l = oracle.attention_batch(q, k, v, 0.5, 0.0, -1, 0, sink_logits=np.array([-np.inf, -np.inf]))
+    np.testing.assert_array_equal(o, base_o)
+    np.testing.assert_array_equal(l, base_l)
+    # a dominant sink drains the weights: O -> 0 and LSE -> the sink logit
+    o, l = oracle.attention_batch(q, k, v, 0.5, 0.0, -1, 0, sink_logits=np.array([60.0, 60.0]))
+    assert np.abs(o).max() < 1e-20 and np.abs(l - 60.0).max() < 1e-20
+    # any sink: O is the sink-free O scaled by l / (l + e^s), LSE = logaddexp(LSE, s)
+    s = np.array([0.3, -1.2])
+    o, l = oracle.attention_batch(q, k, v, 0.5, 0.0, -1, 0, sink_logits=s)
+    for h in range(2):
+        np.testing.assert_allclose(l[0, h], np.logaddexp(base_l[0, h], s[h]), atol=1e-12)
+        np.testing.assert_allclose(o[0, h], base_o[0, h] * np.exp(base_l[0, h] - l[0, h])[:, None], atol=1e-12)
+
+
+def test_sink_keys_visible_set():
+    """Sliding window wl = 2 with causal right bound and 2 sink keys: row i of a
+    square problem sees {0, 1} (when <= i) and i-2 .. i."""
+    rng = np.random.default_rng(23)
+    q, k, v = _rand_case(rng, 1, 1, 1, 10, 10, 4)
+    o, lse, p = oracle.head_attention(q[0, 0], k[0, 0], v[0, 0], 0.6, 0.0, 2, 0, return_probs=True, sink_size=2)
+    for i in range(10):
+        want = sorted({j for j in (0, 1) if j <= i} | set(range(max(0, i - 2), i + 1)))
+        assert [j for j in range(10) if p[i, j] > 0] == want
