@@ -89,10 +89,18 @@ typedef struct {
   int kv_split_tokens; /* decode path: keys per split-KV work unit, a multiple of 64
                           in [64, 2048]; 0 = choose from the shape. Calls that must agree bit for bit
                           pass the same value (or the same shape with 0). */
+  int sink_size;       /* streaming sink keys (sink_size of the Composable Kernel page's
+                          mask): keys j < sink_size are visible to every row whose right
+                          bound reaches them, whatever window_left says; 0 = none */
+  const float* sink_logits; /* nullable DEVICE fp32 [Hq]: per-q-head sink logit (the page's
+                          sink_ptr), in the units of the scaled, soft-capped logits. It adds
+                          exp(sink) to every row's softmax denominator with no value row, so
+                          a row with no visible key gets O = 0, LSE = sink. Not capped.
+                          BF16 / FP8 only (F32: ATTN_ENOTSUP), as is sink_size > 0. */
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
- * descales 1, automatic split size. */
+ * descales 1, automatic split size, no sinks. */
 void attn_params_init(attn_params_t* p, float scale);
 
 /*

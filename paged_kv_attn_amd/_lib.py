@@ -27,6 +27,8 @@ class AttnParams(ctypes.Structure):
         ("k_descale", ctypes.c_float),
         ("v_descale", ctypes.c_float),
         ("kv_split_tokens", ctypes.c_int),
+        ("sink_size", ctypes.c_int),
+        ("sink_logits", ctypes.c_void_p),
     ]
 
 

@@ -20,7 +20,7 @@ _IN_TYPES = {torch.float32: _lib.ATTN_F32, torch.bfloat16: _lib.ATTN_BF16,
              torch.float8_e4m3fn: _lib.ATTN_FP8_E4M3}
 
 
-def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens):
+def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size=0, sink_logits=None):
     if dtype not in _IN_TYPES:
         raise TypeError(f"unsupported input dtype {dtype}")
     p = AttnParams()
@@ -34,6 +34,11 @@ def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens):
         p.window_left, p.window_right = -1, 0
     p.q_descale, p.k_descale, p.v_descale = (float(x) for x in descale)
     p.kv_split_tokens = int(kv_split_tokens)
+    p.sink_size = int(sink_size)
+    if sink_logits is not None:
+        if sink_logits.dtype != torch.float32 or not sink_logits.is_contiguous():
+            raise TypeError("sink_logits must be a contiguous float32 tensor [Hq]")
+        p.sink_logits = sink_logits.data_ptr()
     return p
 
 
@@ -77,12 +82,12 @@ def _workspace(nbytes, device, workspace):
 
 def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seqused_q=None,
              seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
-             kv_split_tokens=0, workspace=None):
+             kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None):
     """Batch mode. q [B, Hq, sq, d], k / v [B, Hkv, sk, d] (any strides, d
     contiguous). Returns (out [B, Hq, sq, d], lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
-    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits)
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:
@@ -98,13 +103,13 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
                     causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
-                    return_lse=True):
+                    return_lse=True, sink_size=0, sink_logits=None):
     """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
     on the device. Returns (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
-    p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits)
     if out is None:
         out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:
@@ -119,7 +124,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
                    softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
-                   workspace=None):
+                   workspace=None, sink_size=0, sink_logits=None):
     """Paged KV cache. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
     (any strides, d contiguous; K and V pools with equal strides);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
@@ -132,7 +137,7 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
     W = block_table.shape[1]
-    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits)
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:

@@ -76,6 +76,10 @@ attn_status_t check_params(const attn_params_t* p, int d) {
   }
   if (p->kv_split_tokens < 0 || p->kv_split_tokens % 64 != 0 || p->kv_split_tokens > 2048)
     return fail(ATTN_EINVAL, "kv_split_tokens must be 0 or a multiple of 64 in [64, 2048]");
+  if (p->sink_size < 0) return fail(ATTN_EINVAL, "sink_size must be >= 0");
+  if (p->sink_logits && ((uintptr_t)p->sink_logits & 3u)) return fail(ATTN_EINVAL, "sink_logits is not 4-byte aligned");
+  if (p->in_dtype == ATTN_F32 && (p->sink_size > 0 || p->sink_logits))
+    return fail(ATTN_ENOTSUP, "attention sinks need bf16 or fp8 inputs");
   return ATTN_OK;
 }
 
@@ -139,6 +143,8 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->window_right = -1;
   p->q_descale = p->k_descale = p->v_descale = 1.0f;
   p->kv_split_tokens = 0;
+  p->sink_size = 0;
+  p->sink_logits = nullptr;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -213,6 +219,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.split_tokens = split; a.n_splits = nsp;
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
     a.wl = p->window_left; a.wr = p->window_right;
+    a.sink_size = p->sink_size;
     const size_t units = (size_t)B * Hkv * nsp * m_rows;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
@@ -222,6 +229,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     c.seqlens_k = seqused_k; c.sk = sk;
     c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
     c.split_tokens = split; c.n_splits = nsp; c.o_mul = 1.0f;
+    c.sink_logits = p->sink_logits;
     return launched(attn::launch_decode(a, c, d, false, B, s));
   }
 
@@ -239,6 +247,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
+  a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillBatch, B, s));
 }
 
@@ -285,6 +294,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
+  a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillVarlen, n, (hipStream_t)stream));
 }
 
@@ -341,6 +351,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
     a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
     a.wl = p->window_left; a.wr = p->window_right;
+    a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
     return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
   }
 
@@ -361,6 +372,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   a.split_tokens = split; a.n_splits = nsp;
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.wl = p->window_left; a.wr = p->window_right;
+  a.sink_size = p->sink_size;
   const size_t units = (size_t)B * Hkv * nsp * m_rows;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
@@ -370,6 +382,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   c.seqlens_k = seqlens_k; c.sk = max_len;
   c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
   c.split_tokens = split; c.n_splits = nsp; c.o_mul = 1.0f;
+  c.sink_logits = p->sink_logits;
   return launched(attn::launch_decode(a, c, d, true, B, (hipStream_t)stream));
 }
 

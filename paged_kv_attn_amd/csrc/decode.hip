@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
     if (a.wl >= 0) {
       lim_lo = pos + off - a.wl;
-      t_lo = max(t0, off - a.wl);
+      t_lo = a.sink_size > t0 ? t0 : max(t0, off - a.wl);  // sink keys ignore the left bound
     }
     t_lo = t0 + (max(0, t_lo - t0) / kGran) * kGran;  // keep granules aligned to the split
   }
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         float x = st[kb][r];
         if (SOFTCAP) x = a.softcap_post * tanh_fast(x * a.softcap_pre);
         const int j = gs + 16 * kb + 4 * j4 + r;
-        x = (j >= lim_lo && j <= lim_hi) ? x : kNegInf;
+        x = ((j >= lim_lo || j < a.sink_size) && j <= lim_hi) ? x : kNegInf;
         st[kb][r] = x;
         mt = __builtin_fmaxf(mt, x);
       }
@@ -313,6 +313,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (s0 + lane < n) M = fmaxf(M, lse_p[(int64_t)(s0 + lane) * a.m_rows]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+  // the sink logit: one more denominator term exp(sink), no value row
+  const float sink = a.sink_logits ? a.sink_logits[hq] : kNegInf;
+  M = fmaxf(M, sink);
 
   float o[kPer] = {};
   float wsum = 0.0f;
@@ -344,6 +347,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) wsum += __shfl_xor(wsum, m);
+    if (sink > kNegInf) wsum += fast_exp2((sink - M) * kLog2e);
   }
   const float inv = (M == kNegInf) ? 0.0f : a.o_mul / wsum;
   __bf16* op = (__bf16*)a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr;

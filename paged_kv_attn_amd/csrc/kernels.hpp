@@ -41,6 +41,8 @@ struct PrefillArgs {
   float softcap_post;         // softcap: cap * log2(e)
   float o_mul;                // value descale applied to O (1 unless FP8)
   int wl, wr;                 // window (-1 = unbounded)
+  int sink_size;              // keys j < sink_size ignore the left bound
+  const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
 };
 
 // Split-KV decode (one workgroup = one split of one request and kv-head).
@@ -61,6 +63,7 @@ struct DecodeArgs {
   float c_exp2;
   float softcap_pre, softcap_post;
   int wl, wr;
+  int sink_size;              // keys j < sink_size ignore the left bound
   float* part_o;              // [B][hkv][n_splits][m_rows][d] fp32
   float* part_lse;            // [B][hkv][n_splits][m_rows]
 };
@@ -75,6 +78,7 @@ struct CombineArgs {
   int sk;
   int B, sq, hq, hkv, ratio, m_rows, split_tokens, n_splits;
   float o_mul;
+  const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
 };
 
 // fp32 path (batch mode).

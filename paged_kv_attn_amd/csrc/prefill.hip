@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int p_hi = (min(r0 + kBlockM, rows_total) - 1) / ratio;
   int j_lo = 0, j_hi = Lk;
   if (MASK) {
-    if (a.wl >= 0) j_lo = max(0, p_lo + off - a.wl);
+    if (a.wl >= 0 && a.sink_size <= 0) j_lo = max(0, p_lo + off - a.wl);  // sink keys start at 0
     if (a.wr >= 0) j_hi = min(Lk, p_hi + off + a.wr + 1);
   }
   const int t_begin = j_lo / kBlockN;
@@ -328,13 +328,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     if (kMasked) {
       const int hi = lim_hi - j0 - 4 * h;
       const int lo = lim_lo - j0 - 4 * h;
+      const int sk = a.sink_size - j0 - 4 * h;  // sink keys ignore the left bound
       const bool two_sided = MASK && a.wl >= 0;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jr = 32 * b + 8 * (r >> 2) + (r & 3);
-          const bool vis = (jr <= hi) && (!two_sided || jr >= lo);
+          const bool vis = (jr <= hi) && (!two_sided || jr >= lo || jr < sk);
           s[b][r] = vis ? s[b][r] : kNegInf;
         }
     }
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     bool skip = wr0 >= rows_total;
     if (MASK) {
       if (a.wr >= 0 && j0 > pw_hi + off + a.wr) skip = true;
-      if (a.wl >= 0 && j0 + kBlockN - 1 < pw_lo + off - a.wl) skip = true;
+      if (a.wl >= 0 && j0 + kBlockN - 1 < pw_lo + off - a.wl && j0 >= a.sink_size) skip = true;
     }
     return skip;
   };
@@ -465,8 +466,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // ---- epilogue: normalise, LSE, predicated stores (rows < Lq only) ----
   const float l_tot = sum_across_halves(l_run);
   if (row_ok) {
-    const bool empty = !(l_tot > 0.0f);  // no visible key: O = 0, LSE = -inf
-    const float inv = empty ? 0.0f : a.o_mul / l_tot;
+    const bool empty = !(l_tot > 0.0f);  // no visible key: O = 0, LSE = -inf (or the sink logit)
+    float inv = empty ? 0.0f : a.o_mul / l_tot;
+    float lse2 = empty ? kNegInf : m_run * c + __builtin_log2f(l_tot);  // log2 units
+    if (a.sink_logits) {
+      // one more denominator term 2^sk2 (the sink logit in log2 units), no value row
+      const float sk2 = a.sink_logits[hq] * kLog2e;
+      if (empty) {
+        lse2 = sk2;
+      } else if (sk2 > kNegInf) {
+        const float mc = m_run * c;
+        if (sk2 <= mc) {
+          const float l2 = l_tot + fast_exp2(sk2 - mc);
+          inv = a.o_mul / l2;
+          lse2 = mc + __builtin_log2f(l2);
+        } else {  // scale by 2^(mc - sk2) <= 1 so nothing overflows
+          const float f = fast_exp2(mc - sk2);
+          const float l2 = l_tot * f + 1.0f;
+          inv = a.o_mul * f / l2;
+          lse2 = sk2 + __builtin_log2f(l2);
+        }
+      }
+    }
     char* op = (char*)a.o + (o_off + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr) * 2;
 #pragma unroll
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
@@ -479,10 +500,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         *(U64*)(op + d * 2) = w;
       }
     }
-    if (a.lse && h == 0) {
-      a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] =
-          empty ? kNegInf : (m_run * c + __builtin_log2f(l_tot)) * kLn2;
-    }
+    if (a.lse && h == 0) a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] = lse2 * kLn2;
   }
 }
 

@@ -48,24 +48,24 @@ def run_paged(case, **kw):
                              descale=(case.descale["q"], case.descale["k"], case.descale["v"]), **kw)
 
 
-def oracle_dense(case, workers=8):
+def oracle_dense(case, workers=8, **sinks):
     t, d = case.t, case.descale
     su_q = t["seqused_q"].cpu().numpy() if "seqused_q" in t else None
     su_k = t["seqused_k"].cpu().numpy() if "seqused_k" in t else None
     return oracle.attention_batch(decode(t["q"], case.dtype, d["q"]), decode(t["k"], case.dtype, d["k"]),
                                   decode(t["v"], case.dtype, d["v"]), case.scale, case.softcap,
-                                  case.window_left, case.window_right, su_q, su_k, workers=workers)
+                                  case.window_left, case.window_right, su_q, su_k, workers=workers, **sinks)
 
 
-def oracle_varlen(case, workers=8):
+def oracle_varlen(case, workers=8, **sinks):
     t, d = case.t, case.descale
     return oracle.attention_varlen(decode(t["q"], case.dtype, d["q"]), decode(t["k"], case.dtype, d["k"]),
                                    decode(t["v"], case.dtype, d["v"]), t["cu_seqlens_q"].cpu().numpy(),
                                    t["cu_seqlens_k"].cpu().numpy(), case.scale, case.softcap, case.window_left,
-                                   case.window_right, workers=workers)
+                                   case.window_right, workers=workers, **sinks)
 
 
-def oracle_paged(case, requests=None, workers=8):
+def oracle_paged(case, requests=None, workers=8, **sinks):
     """Oracle for all requests (or the listed ones, in that order)."""
     t = case.t
     kp = t["k_pool"].detach().cpu()
@@ -86,7 +86,8 @@ def oracle_paged(case, requests=None, workers=8):
         kb, vb = kp.numpy(), vp.numpy()
         dk = dv = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
     return oracle.attention_paged(q[idx], kb, vb, table[idx], lens[idx], case.scale, case.softcap,
-                                  case.window_left, case.window_right, workers=workers, decode=(dk, dv))
+                                  case.window_left, case.window_right, workers=workers, decode=(dk, dv),
+                                  **sinks)
 
 
 def to_np(x):

@@ -37,7 +37,7 @@ def test_params_struct_layout_matches_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct \{(.*?)\} attn_params_t;", text, re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
-    fields = re.findall(r"\b(int|float)\s+([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)\s*;", body)
+    fields = re.findall(r"\b(int|float\s*\*?)\s*([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)\s*;", body)
     names = [n.strip() for _, group in fields for n in group.split(",")]
     assert names == [f for f, _ in AttnParams._fields_]
 
