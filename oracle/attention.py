@@ -109,8 +109,17 @@ def masked_allowed(rows: np.ndarray, lq: int, lk: int, window_left: int, window_
     return (left | (j < sink_size)) & right
 
 
+def alibi_bias(lq: int, lk: int, slope: float) -> np.ndarray:
+    """ALiBi position bias [lq, lk] (the ``alibi_slope_ptr`` arguments of the
+    Composable Kernel page, positions measured from the bottom-right corner):
+    -slope * |(i + lk - lq) - j|."""
+    i = np.arange(lq, dtype=np.float64)[:, None]
+    j = np.arange(lk, dtype=np.float64)[None, :]
+    return -float(slope) * np.abs(i + (lk - lq) - j)
+
+
 def head_attention(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1, return_probs=False,
-                   sink_size=0, sink_logit=-np.inf):
+                   sink_size=0, sink_logit=-np.inf, bias=None):
     """Attention of one head: q [Lq, d], k [Lk, d], v [Lk, dv] (fp64).
 
     Returns O [Lq, dv] and LSE [Lq] (and P [Lq, Lk] if ``return_probs``).
@@ -123,6 +132,10 @@ def head_attention(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1,
     every row's softmax denominator, with no value row, so
     l = sum_j exp(S_ij - m) + exp(sink_logit - m), m = max(max_j S_ij, sink_logit).
     A row with no visible key then gets O = 0 and LSE = sink_logit.
+
+    ``bias`` ([Lq, Lk], fp64, or None) is added to the logits after the scale
+    and the soft-cap, before the mask (S'' = S' + Bias in the page's math
+    contract); ALiBi is the bias alibi_bias(Lq, Lk, slope).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -141,6 +154,8 @@ def head_attention(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1,
         s = scale * (q[rows] @ k.T)
         if softcap > 0:
             s = softcap * np.tanh(s / softcap)
+        if bias is not None:
+            s = s + np.asarray(bias, dtype=np.float64)[rows]
         allowed = masked_allowed(rows, lq, lk, window_left, window_right, sink_size)
         has = allowed.any(axis=1)
         if not has.any():
@@ -172,12 +187,15 @@ def _map_pool(fn, jobs, workers):
 # ----------------------------------------------------------------------------
 
 def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1,
-                    seqused_q=None, seqused_k=None, workers=1, sink_size=0, sink_logits=None):
+                    seqused_q=None, seqused_k=None, workers=1, sink_size=0, sink_logits=None,
+                    bias=None, alibi_slopes=None):
     """Batch mode: q [B, Hq, sq, d], k/v [B, Hkv, sk, d] (fp64).
 
     Per batch b the used lengths are Lq = seqused_q[b] (else sq) and
     Lk = seqused_k[b] (else sk); q-head h reads kv-head h // (Hq // Hkv).
     ``sink_size`` and ``sink_logits`` ([Hq] or None) as in head_attention.
+    ``bias``: elementwise [B, Hq, sq, sk] (its top-left [Lq, Lk] block is used);
+    ``alibi_slopes``: [B, Hq] or [Hq] (shared by every batch entry).
     Returns O [B, Hq, sq, dv] and LSE [B, Hq, sq]; rows at or beyond Lq are not
     defined by the method and are left NaN.
     """
@@ -198,8 +216,15 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
         lk = k.shape[2] if seqused_k is None else int(seqused_k[b])
         g = h // ratio
         sink = -np.inf if sink_logits is None else float(sink_logits[h])
+        bh = None
+        if bias is not None:
+            bh = np.asarray(bias[b, h, :lq, :lk], dtype=np.float64)
+        if alibi_slopes is not None:
+            sl = np.asarray(alibi_slopes, dtype=np.float64)
+            ab = alibi_bias(lq, lk, sl[h] if sl.ndim == 1 else sl[b, h])
+            bh = ab if bh is None else bh + ab
         oh, lh = head_attention(q[b, h, :lq], k[b, g, :lk], v[b, g, :lk], scale, softcap,
-                                window_left, window_right, sink_size=sink_size, sink_logit=sink)
+                                window_left, window_right, sink_size=sink_size, sink_logit=sink, bias=bh)
         return b, h, lq, oh, lh
 
     for b, h, lq, oh, lh in _map_pool(job, [(b, h) for b in range(b_) for h in range(hq)], workers):
@@ -209,7 +234,8 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
-                     window_left=-1, window_right=-1, workers=1, sink_size=0, sink_logits=None):
+                     window_left=-1, window_right=-1, workers=1, sink_size=0, sink_logits=None,
+                     alibi_slopes=None):
     """Varlen / group mode: sequences packed along the token axis.
 
     q [Tq, Hq, d], k/v [Tk, Hkv, d]; sequence s owns query tokens
@@ -230,8 +256,13 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
         qs = q[cq[s]:cq[s + 1]].transpose(1, 0, 2)[None]
         ks = k[ck[s]:ck[s + 1]].transpose(1, 0, 2)[None]
         vs = v[ck[s]:ck[s + 1]].transpose(1, 0, 2)[None]
+        sl = None
+        if alibi_slopes is not None:
+            sl = np.asarray(alibi_slopes, dtype=np.float64)
+            sl = sl if sl.ndim == 1 else sl[s]
         os_, ls_ = attention_batch(qs, ks, vs, scale, softcap, window_left, window_right,
-                                   workers=workers, sink_size=sink_size, sink_logits=sink_logits)
+                                   workers=workers, sink_size=sink_size, sink_logits=sink_logits,
+                                   alibi_slopes=sl)
         o[cq[s]:cq[s + 1]] = os_[0].transpose(1, 0, 2)
         lse[:, cq[s]:cq[s + 1]] = ls_[0]
     return o, lse
@@ -254,7 +285,8 @@ def gather_paged(pool, block_table_row, seqlen):
 
 
 def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.0,
-                    window_left=-1, window_right=-1, workers=1, decode=None, sink_size=0, sink_logits=None):
+                    window_left=-1, window_right=-1, workers=1, decode=None, sink_size=0, sink_logits=None,
+                    alibi_slopes=None):
     """Paged-KV mode: q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d];
     block_table [B, max_pages] int; seqlens_k [B].
 
@@ -276,8 +308,12 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
     def job(b):
         ks = dec_k(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]
         vs = dec_v(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]
+        sl = None
+        if alibi_slopes is not None:
+            sl = np.asarray(alibi_slopes, dtype=np.float64)
+            sl = sl if sl.ndim == 1 else sl[b]
         return b, attention_batch(q[b:b + 1], ks, vs, scale, softcap, window_left, window_right,
-                                  sink_size=sink_size, sink_logits=sink_logits)
+                                  sink_size=sink_size, sink_logits=sink_logits, alibi_slopes=sl)
 
     for b, (ob, lb) in _map_pool(job, list(range(b_)), workers):
         o[b] = ob[0]

@@ -2,7 +2,8 @@
 
 An independent restatement of the definition used to pin the numpy oracle: no
 numpy, no vectorisation, no shared helper. Per query row i of a head it forms
-every logit s_ij = scale * sum_c q_ic k_jc, optionally soft-caps it, keeps the
+every logit s_ij = scale * sum_c q_ic k_jc, optionally soft-caps it, adds an
+optional bias b_ij, keeps the
 keys inside the bottom-right-aligned window (plus the first ``sink_size`` keys
 when the right bound reaches them), and returns
 O_i = sum_j exp(s_ij) v_j / D_i and LSE_i = log D_i with
@@ -13,7 +14,7 @@ with O_i = 0 and LSE_i = log(exp(sink)) or -inf when no key is visible.
 import math
 
 
-def brute_head(q, k, v, scale, softcap=0.0, wl=-1, wr=-1, dv=None, sink_size=0, sink=None):
+def brute_head(q, k, v, scale, softcap=0.0, wl=-1, wr=-1, dv=None, sink_size=0, sink=None, bias=None):
     lq, lk = len(q), len(k)
     if dv is None:
         dv = len(v[0]) if lk else len(q[0])
@@ -31,6 +32,8 @@ def brute_head(q, k, v, scale, softcap=0.0, wl=-1, wr=-1, dv=None, sink_size=0, 
             s *= scale
             if softcap > 0:
                 s = softcap * math.tanh(s / softcap)
+            if bias is not None:
+                s += bias[i][j]
             logits.append((j, s))
         if not logits:
             out.append([0.0] * dv)

@@ -400,3 +400,73 @@ def test_sink_keys_visible_set():
     for i in range(10):
         want = sorted({j for j in (0, 1) if j <= i} | set(range(max(0, i - 2), i + 1)))
         assert [j for j in range(10) if p[i, j] > 0] == want
+
+
+# ---------------------------------------------------------------------------
+# Additive bias (elementwise) and ALiBi.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(20))
+def test_bias_and_alibi_match_brute_force(seed):
+    rng = np.random.default_rng(2000 + seed)
+    Hkv, ratio, B = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    Hq = Hkv * ratio
+    sq, sk, d = int(rng.integers(1, 9)), int(rng.integers(1, 11)), int(rng.integers(1, 6))
+    q, k, v = _rand_case(rng, B, Hq, Hkv, sq, sk, d)
+    scale = float(rng.uniform(0.2, 1.5))
+    softcap = float(rng.choice([0.0, 2.5]))
+    wl, wr = int(rng.choice([-1, 2])), int(rng.choice([-1, 0]))
+    bias = rng.standard_normal((B, Hq, sq, sk)) if seed % 2 == 0 else None
+    slopes = rng.uniform(0.01, 1.0, size=(B, Hq)) if seed % 3 != 0 else None
+    o, lse = oracle.attention_batch(q, k, v, scale, softcap, wl, wr, bias=bias, alibi_slopes=slopes)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // ratio
+            tot = [[0.0] * sk for _ in range(sq)]
+            for i in range(sq):
+                for j in range(sk):
+                    if bias is not None:
+                        tot[i][j] += float(bias[b, h, i, j])
+                    if slopes is not None:
+                        tot[i][j] -= float(slopes[b, h]) * abs(i + sk - sq - j)
+            bo, bl = brute_head(q[b, h].tolist(), k[b, g].tolist(), v[b, g].tolist(), scale, softcap, wl, wr,
+                                bias=tot)
+            np.testing.assert_allclose(o[b, h], np.array(bo).reshape(sq, d), atol=1e-12, rtol=0)
+            fin = np.isfinite(bl)
+            np.testing.assert_array_equal(np.isinf(lse[b, h]), ~fin)
+            np.testing.assert_allclose(lse[b, h][fin], np.array(bl)[fin], atol=1e-12, rtol=0)
+
+
+def test_alibi_closed_form_causal():
+    """Q = 0, causal, square: row i sees keys 0..i with logits -a (i - j), so
+    LSE_i = ln sum_{t=0}^{i} e^{-a t} = ln((1 - e^{-a (i+1)}) / (1 - e^{-a})) and
+    O_i = sum_j e^{-a (i - j)} V_j / e^{LSE_i}."""
+    rng = np.random.default_rng(31)
+    n, a = 9, 0.37
+    q = np.zeros((1, 1, n, 4))
+    k = rng.standard_normal((1, 1, n, 4))
+    v = rng.standard_normal((1, 1, n, 4))
+    o, lse = oracle.attention_batch(q, k, v, 1.0, 0.0, -1, 0, alibi_slopes=np.array([a]))
+    for i in range(n):
+        want_lse = math.log((1 - math.exp(-a * (i + 1))) / (1 - math.exp(-a)))
+        assert abs(lse[0, 0, i] - want_lse) < 1e-12
+        w = np.array([math.exp(-a * (i - j)) for j in range(i + 1)])
+        np.testing.assert_allclose(o[0, 0, i], (w[:, None] * v[0, 0, :i + 1]).sum(0) / math.exp(want_lse),
+                                   atol=1e-12)
+
+
+def test_row_constant_bias_shifts_lse_only():
+    rng = np.random.default_rng(32)
+    q, k, v = _rand_case(rng, 1, 2, 2, 6, 8, 4)
+    base_o, base_l = oracle.attention_batch(q, k, v, 0.4, 0.0, -1, 0)
+    shift = rng.standard_normal((1, 2, 6, 1)) * np.ones((1, 1, 1, 8))
+    o, l = oracle.attention_batch(q, k, v, 0.4, 0.0, -1, 0, bias=shift)
+    np.testing.assert_allclose(o, base_o, atol=1e-12)
+    np.testing.assert_allclose(l, base_l + shift[..., 0], atol=1e-12)
+
+
+def test_alibi_bias_matrix():
+    b = A.alibi_bias(3, 5, 0.5)
+    for i in range(3):
+        for j in range(5):
+            assert b[i, j] == -0.5 * abs(i + 2 - j)
