@@ -69,6 +69,12 @@ typedef enum {
 } attn_dtype_t;
 
 typedef enum {
+  ATTN_BIAS_NONE = 0,
+  ATTN_BIAS_ELEMENTWISE = 1, /* per (batch, q-head, query, key) values */
+  ATTN_BIAS_ALIBI = 2        /* per (batch, q-head) slopes */
+} attn_bias_t;
+
+typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = 1,     /* bad argument: NULL pointer, bad size, stride, alignment */
   ATTN_ENOTSUP = 2,    /* valid but not implemented (head dim, dtype pair, mode) */
@@ -97,10 +103,22 @@ typedef struct {
                           exp(sink) to every row's softmax denominator with no value row, so
                           a row with no visible key gets O = 0, LSE = sink. Not capped.
                           BF16 / FP8 only (F32: ATTN_ENOTSUP), as is sink_size > 0. */
+  int bias_type;       /* attn_bias_t: an additive logit bias S'' = S' + Bias (the math
+                          contract of the Composable Kernel page), added after the scale and
+                          the soft-cap, before the mask. BF16 / FP8 only. */
+  const float* bias;   /* DEVICE fp32. ALIBI: the slope of (b, q-head h) at
+                          bias[b*bias_stride[0] + h] (bias_stride[0] = 0: one slope per head
+                          for every b); the bias of key j for query row i is
+                          -slope * |i + Lk - Lq - j| (bottom-right aligned). In varlen mode b
+                          is the sequence index. ELEMENTWISE: batch-mode prefill shapes only
+                          (attn_fwd with sq*Hq/Hkv > 16); the bias of (b, h, i, j) at
+                          bias[b*bias_stride[0] + h*bias_stride[1] + i*bias_stride[2] + j],
+                          16-byte aligned with bias_stride[2] a multiple of 4. */
+  int64_t bias_stride[3];
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
- * descales 1, automatic split size, no sinks. */
+ * descales 1, automatic split size, no sinks, no bias. */
 void attn_params_init(attn_params_t* p, float scale);
 
 /*

@@ -12,6 +12,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+ATTN_BIAS_NONE, ATTN_BIAS_ELEMENTWISE, ATTN_BIAS_ALIBI = 0, 1, 2
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_EINVAL", 2: "ATTN_ENOTSUP", 3: "ATTN_EWORKSPACE", 4: "ATTN_ELAUNCH"}
 
 
@@ -29,6 +30,9 @@ class AttnParams(ctypes.Structure):
         ("kv_split_tokens", ctypes.c_int),
         ("sink_size", ctypes.c_int),
         ("sink_logits", ctypes.c_void_p),
+        ("bias_type", ctypes.c_int),
+        ("bias", ctypes.c_void_p),
+        ("bias_stride", ctypes.c_int64 * 3),
     ]
 
 

@@ -20,7 +20,8 @@ _IN_TYPES = {torch.float32: _lib.ATTN_F32, torch.bfloat16: _lib.ATTN_BF16,
              torch.float8_e4m3fn: _lib.ATTN_FP8_E4M3}
 
 
-def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size=0, sink_logits=None):
+def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size=0, sink_logits=None,
+            bias=None, alibi_slopes=None):
     if dtype not in _IN_TYPES:
         raise TypeError(f"unsupported input dtype {dtype}")
     p = AttnParams()
@@ -39,6 +40,21 @@ def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, 
         if sink_logits.dtype != torch.float32 or not sink_logits.is_contiguous():
             raise TypeError("sink_logits must be a contiguous float32 tensor [Hq]")
         p.sink_logits = sink_logits.data_ptr()
+    if bias is not None and alibi_slopes is not None:
+        raise ValueError("pass either an elementwise bias or ALiBi slopes, not both")
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.dim() not in (1, 2) or alibi_slopes.stride(-1) != 1:
+            raise TypeError("alibi_slopes must be float32 [Hq] or [B, Hq] with unit stride over heads")
+        p.bias_type = _lib.ATTN_BIAS_ALIBI
+        p.bias = alibi_slopes.data_ptr()
+        p.bias_stride[0] = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.dim() != 4 or bias.stride(-1) != 1:
+            raise TypeError("bias must be float32 [B|1, Hq|1, sq, sk] with unit stride over keys")
+        p.bias_type = _lib.ATTN_BIAS_ELEMENTWISE
+        p.bias = bias.data_ptr()
+        for i in range(3):   # broadcast (size-1) dims read with stride 0
+            p.bias_stride[i] = 0 if bias.shape[i] == 1 else bias.stride(i)
     return p
 
 
@@ -82,12 +98,13 @@ def _workspace(nbytes, device, workspace):
 
 def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seqused_q=None,
              seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
-             kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None):
+             kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None, bias=None, alibi_slopes=None):
     """Batch mode. q [B, Hq, sq, d], k / v [B, Hkv, sk, d] (any strides, d
     contiguous). Returns (out [B, Hq, sq, d], lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
-    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
+                bias, alibi_slopes)
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:
@@ -103,13 +120,14 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
                     causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
-                    return_lse=True, sink_size=0, sink_logits=None):
+                    return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None):
     """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
     on the device. Returns (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
-    p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
+                alibi_slopes=alibi_slopes)
     if out is None:
         out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:
@@ -124,7 +142,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
                    softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
-                   workspace=None, sink_size=0, sink_logits=None):
+                   workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None):
     """Paged KV cache. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
     (any strides, d contiguous; K and V pools with equal strides);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
@@ -137,7 +155,8 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
     W = block_table.shape[1]
-    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits)
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
+                alibi_slopes=alibi_slopes)
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
     if lse is None and return_lse:

@@ -54,6 +54,20 @@ int n_splits_for(int split, int max_len) { return max_len > 0 ? (max_len + split
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Bias in the kernels' logit units: the kernels compare and exponentiate
+// x * c_exp2 in base 2, so a natural-log bias b enters as b * log2(e) / c_exp2.
+void set_bias(const attn_params_t* p, float c_exp2, attn::PrefillArgs* a) {
+  a->bias_type = p->bias_type;
+  a->bias = p->bias;
+  a->bias_sb = p->bias_stride[0]; a->bias_sh = p->bias_stride[1]; a->bias_sr = p->bias_stride[2];
+  a->bias_mul = 1.4426950408889634f / c_exp2;
+}
+void set_bias(const attn_params_t* p, float c_exp2, attn::DecodeArgs* a) {
+  a->alibi = p->bias_type == ATTN_BIAS_ALIBI ? p->bias : nullptr;
+  a->alibi_sb = p->bias_stride[0];
+  a->bias_mul = 1.4426950408889634f / c_exp2;
+}
+
 size_t decode_ws_bytes(int B, int Hkv, int n_splits, int m_rows, int d) {
   const size_t units = (size_t)B * Hkv * n_splits * m_rows;
   return align256(units * d * sizeof(float)) + align256(units * sizeof(float));
@@ -80,6 +94,17 @@ attn_status_t check_params(const attn_params_t* p, int d) {
   if (p->sink_logits && ((uintptr_t)p->sink_logits & 3u)) return fail(ATTN_EINVAL, "sink_logits is not 4-byte aligned");
   if (p->in_dtype == ATTN_F32 && (p->sink_size > 0 || p->sink_logits))
     return fail(ATTN_ENOTSUP, "attention sinks need bf16 or fp8 inputs");
+  if (p->bias_type < ATTN_BIAS_NONE || p->bias_type > ATTN_BIAS_ALIBI)
+    return fail(ATTN_EINVAL, "unknown bias_type %d", p->bias_type);
+  if (p->bias_type != ATTN_BIAS_NONE) {
+    if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "a logit bias needs bf16 or fp8 inputs");
+    if (!p->bias) return fail(ATTN_EINVAL, "bias is NULL");
+    if (p->bias_stride[0] < 0 || p->bias_stride[1] < 0 || p->bias_stride[2] < 0)
+      return fail(ATTN_EINVAL, "bias strides must be >= 0");
+    if ((uintptr_t)p->bias & 3u) return fail(ATTN_EINVAL, "bias is not 4-byte aligned");
+    if (p->bias_type == ATTN_BIAS_ELEMENTWISE && (((uintptr_t)p->bias & 15u) || p->bias_stride[2] % 4))
+      return fail(ATTN_EINVAL, "an elementwise bias needs a 16-byte aligned base and a row stride multiple of 4");
+  }
   return ATTN_OK;
 }
 
@@ -145,6 +170,9 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->kv_split_tokens = 0;
   p->sink_size = 0;
   p->sink_logits = nullptr;
+  p->bias_type = ATTN_BIAS_NONE;
+  p->bias = nullptr;
+  p->bias_stride[0] = p->bias_stride[1] = p->bias_stride[2] = 0;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -201,6 +229,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
 
   if (takes_decode_path(p->in_dtype, sq, ratio)) {
     if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "the decode path (sq*Hq/Hkv <= 16) supports bf16 only");
+    if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
+      return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
     if (seqused_q) return fail(ATTN_ENOTSUP, "seqused_q is not supported on the decode path (sq*Hq/Hkv <= 16)");
     const int split = plan_split_tokens(p, B, Hkv, sk);
     const int nsp = n_splits_for(split, sk);
@@ -220,6 +250,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size;
+    set_bias(p, c_exp2, &a);
     const size_t units = (size_t)B * Hkv * nsp * m_rows;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
@@ -248,6 +279,13 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
+  set_bias(p, c_exp2, &a);
+  if (p->bias_type == ATTN_BIAS_ELEMENTWISE) {
+    // bytes from one batch entry's bias base to its last element (32-bit offsets in the kernel)
+    const int64_t ext = ((int64_t)(Hq - 1) * p->bias_stride[1] + (int64_t)(sq - 1) * p->bias_stride[2] + sk) * 4;
+    if (ext >= ((int64_t)1 << 31)) return fail(ATTN_EINVAL, "elementwise bias spans more than 2 GiB per batch entry");
+    a.bias_bytes = (uint32_t)ext;
+  }
   return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillBatch, B, s));
 }
 
@@ -260,6 +298,8 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   (void)workspace_bytes;
   (void)max_seqlen_k;
   TRY(check_params(p, d));
+  if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
+    return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "fp32 inputs are supported in batch mode only");
   if (n < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0)
     return fail(ATTN_EINVAL, "bad sizes n=%d total_q=%d max_q=%d max_k=%d Hq=%d Hkv=%d", n, total_q, max_seqlen_q,
@@ -295,6 +335,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
+  set_bias(p, c_exp2, &a);
   return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillVarlen, n, (hipStream_t)stream));
 }
 
@@ -310,6 +351,8 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
   if (page_size <= 0 || page_size % 32) return fail(ATTN_ENOTSUP, "page_size %d is not a positive multiple of 32", page_size);
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "paged KV supports bf16 and fp8 inputs");
+  if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
+    return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   const int ratio = Hq / Hkv;
   const bool decode_shape = takes_decode_path(p->in_dtype, sq, ratio);
   if (decode_shape && p->in_dtype != ATTN_BF16)
@@ -352,6 +395,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
+    set_bias(p, c_exp2, &a);
     return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
   }
 
@@ -373,6 +417,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size;
+  set_bias(p, c_exp2, &a);
   const size_t units = (size_t)B * Hkv * nsp * m_rows;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));

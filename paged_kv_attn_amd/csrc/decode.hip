@@ -117,6 +117,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     t_lo = t0 + (max(0, t_lo - t0) / kGran) * kGran;  // keep granules aligned to the split
   }
 
+  // ALiBi slope of this lane's (request, q-head), in kernel logit units
+  const float alibi_k = a.alibi ? a.alibi[(int64_t)b * a.alibi_sb + hq] * a.bias_mul : 0.0f;
+
   // The split's page ids, one per lane (a split spans at most 64 pages).
   const int p_first = PAGED ? t0 / a.page_size : 0;
   int pg = 0;
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         float x = st[kb][r];
         if (SOFTCAP) x = a.softcap_post * tanh_fast(x * a.softcap_pre);
         const int j = gs + 16 * kb + 4 * j4 + r;
+        if (a.alibi) x = __builtin_fmaf(-alibi_k, __builtin_fabsf((float)(pos + off - j)), x);
         x = ((j >= lim_lo || j < a.sink_size) && j <= lim_hi) ? x : kNegInf;
         st[kb][r] = x;
         mt = __builtin_fmaxf(mt, x);

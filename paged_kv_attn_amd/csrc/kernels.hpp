@@ -11,6 +11,8 @@ enum InType : int { kInF32 = 0, kInBF16 = 1, kInFP8 = 2 };
 // prefill addressing modes: batch [B, H, S, d]; varlen (cu_seqlens); paged
 // (K/V rows through a block table, Lq = sq, Lk = seqlens_k)
 enum PrefillMode : int { kPrefillBatch = 0, kPrefillVarlen = 1, kPrefillPaged = 2 };
+// logit bias kinds (the values of attn_bias_t)
+enum BiasKind : int { kBiasNone = 0, kBiasElem = 1, kBiasAlibi = 2 };
 
 // Prefill (one workgroup = 128 packed query rows of one sequence and kv-head).
 struct PrefillArgs {
@@ -43,6 +45,11 @@ struct PrefillArgs {
   int wl, wr;                 // window (-1 = unbounded)
   int sink_size;              // keys j < sink_size ignore the left bound
   const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
+  int bias_type;              // attn_bias_t
+  const float* bias;          // ALiBi slopes or elementwise values (see attn.h)
+  int64_t bias_sb, bias_sh, bias_sr;
+  uint32_t bias_bytes;        // elementwise: bytes of one batch entry's bias (reads past it return 0)
+  float bias_mul;             // natural-log logit units -> the kernel's logit units
 };
 
 // Split-KV decode (one workgroup = one split of one request and kv-head).
@@ -64,6 +71,9 @@ struct DecodeArgs {
   float softcap_pre, softcap_post;
   int wl, wr;
   int sink_size;              // keys j < sink_size ignore the left bound
+  const float* alibi;         // nullable: ALiBi slope of (b, q-head) at alibi[b*alibi_sb + hq]
+  int64_t alibi_sb;
+  float bias_mul;             // natural-log logit units -> the kernel's logit units
   float* part_o;              // [B][hkv][n_splits][m_rows][d] fp32
   float* part_lse;            // [B][hkv][n_splits][m_rows]
 };

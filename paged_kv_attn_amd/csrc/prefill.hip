@@ -78,7 +78,7 @@ template <bool FP8> struct QFrag;
 template <> struct QFrag<false> { using T = U128; };
 template <> struct QFrag<true> { using T = U64; };
 
-template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP>
+template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Tr = Traits<D, FP8>;
   using QT = typename QFrag<FP8>::T;
@@ -172,6 +172,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     if (a.wr >= 0) lim_hi = min(Lk - 1, pos + off + a.wr);
     if (a.wl >= 0) lim_lo = pos + off - a.wl;
   }
+  // ALiBi slope of this row's (batch entry or sequence, q-head), in kernel logit units
+  const float alibi_k = BIAS == kBiasAlibi ? a.bias[(int64_t)z * a.bias_sb + hq] * a.bias_mul : 0.0f;
+  // elementwise bias: this row's values, addressed from the batch entry's base
+  const int bias_lane = BIAS == kBiasElem ? (int)((int64_t)hq * a.bias_sh + (int64_t)pos * a.bias_sr) * 4 : 0;
 
   // ---- Q fragment, resident in registers for the whole key loop ----
   // B operand of S^T = K Q^T: lane (row lane%32, half h) holds Q[row][16s + 8h .. +7].
@@ -324,6 +328,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[b][r] = a.softcap_post * tanh_fast(s[b][r] * a.softcap_pre);
+    }
+    // additive bias (after the soft-cap, before the mask); register r of block b
+    // is key j0 + 4h + 32b + 8(r/4) + r%4
+    if (BIAS == kBiasAlibi) {
+      const float dbase = (float)(pos + off - j0 - 4 * h);  // distance to key j0 + 4h
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float jr = (float)(32 * b + 8 * (r >> 2) + (r & 3));
+          s[b][r] = __builtin_fmaf(-alibi_k, __builtin_fabsf(dbase - jr), s[b][r]);
+        }
+    }
+    if (BIAS == kBiasElem) {
+      // 16-byte loads of 4 consecutive keys; reads past the bias tensor return 0
+      const __amdgpu_buffer_rsrc_t br =
+          make_rsrc((const char*)a.bias + (int64_t)z * a.bias_sb * 4, a.bias_bytes);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        U128 bv[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) bv[g4] = buf_load16(br, bias_lane + 4 * (j0 + 4 * h + 32 * b + 8 * g4));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t w = (&bv[r >> 2].x)[r & 3];
+          s[b][r] = __builtin_fmaf(__builtin_bit_cast(float, w), a.bias_mul, s[b][r]);
+        }
+      }
     }
     if (kMasked) {
       const int hi = lim_hi - j0 - 4 * h;
@@ -504,20 +536,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP>
+template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
   const int64_t n_units = (int64_t)a.hkv * nz;
   const int64_t grid = (n_units + kXcds - 1) / kXcds * kXcds * a.n_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, MODE, MASK, SOFTCAP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, MODE, MASK, SOFTCAP, BIAS>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, b);
   return hipGetLastError();
+}
+
+template <int D, bool FP8, int MODE, int BIAS>
+hipError_t launch_b(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
+  if (mask)
+    return softcap ? launch_t<D, FP8, MODE, true, true, BIAS>(a, nz, s) : launch_t<D, FP8, MODE, true, false, BIAS>(a, nz, s);
+  return softcap ? launch_t<D, FP8, MODE, false, true, BIAS>(a, nz, s) : launch_t<D, FP8, MODE, false, false, BIAS>(a, nz, s);
 }
 
 template <int D, bool FP8, int MODE>
 hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (mask) return softcap ? launch_t<D, FP8, MODE, true, true>(a, nz, s) : launch_t<D, FP8, MODE, true, false>(a, nz, s);
-  return softcap ? launch_t<D, FP8, MODE, false, true>(a, nz, s) : launch_t<D, FP8, MODE, false, false>(a, nz, s);
+  if (a.bias_type == kBiasAlibi) return launch_b<D, FP8, MODE, kBiasAlibi>(a, nz, mask, softcap, s);
+  if (MODE == kPrefillBatch && a.bias_type == kBiasElem)
+    return launch_b<D, FP8, MODE, (MODE == kPrefillBatch ? kBiasElem : kBiasNone)>(a, nz, mask, softcap, s);
+  return launch_b<D, FP8, MODE, kBiasNone>(a, nz, mask, softcap, s);
 }
 
 template <int D, bool FP8>

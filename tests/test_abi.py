@@ -37,7 +37,7 @@ def test_params_struct_layout_matches_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct \{(.*?)\} attn_params_t;", text, re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
-    fields = re.findall(r"\b(int|float\s*\*?)\s*([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)\s*;", body)
+    fields = re.findall(r"\b(int64_t|int|float\s*\*?)\s*([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)(?:\[\d+\])?\s*;", body)
     names = [n.strip() for _, group in fields for n in group.split(",")]
     assert names == [f for f, _ in AttnParams._fields_]
 
@@ -191,3 +191,28 @@ def test_product_path_has_no_oracle_dependency():
                     if isinstance(node, (ast.Import, ast.ImportFrom)):
                         mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
                         assert not any(m.split(".")[0] in ("oracle", "tests", "synth") for m in mods), (f, mods)
+
+
+def test_bias_validation():
+    p = _params(bias_type=7)
+    assert _fwd(p) == 1 and "bias_type" in _err()
+    p = _params(bias_type=_lib.ATTN_BIAS_ALIBI)
+    assert _fwd(p) == 1 and "bias is NULL" in _err()
+    p = _params(bias_type=_lib.ATTN_BIAS_ELEMENTWISE, bias=0x10008)
+    assert _fwd(p) == 1 and "16-byte" in _err()
+    p = _params(bias_type=_lib.ATTN_BIAS_ELEMENTWISE, bias=0x10000)
+    p.bias_stride[2] = 6
+    assert _fwd(p) == 1 and "multiple of 4" in _err()
+    p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, bias_type=_lib.ATTN_BIAS_ALIBI, bias=0x10000)
+    assert _fwd(p) == 2 and "bf16 or fp8" in _err()
+    p = _params(bias_type=_lib.ATTN_BIAS_ELEMENTWISE, bias=0x10000)       # decode shape
+    assert _paged(p) == 2 and "batch-mode prefill" in _err()
+
+
+def test_sink_validation():
+    p = _params(sink_size=-1)
+    assert _fwd(p) == 1 and "sink_size" in _err()
+    p = _params(sink_logits=0x10002)
+    assert _fwd(p) == 1 and "sink_logits" in _err()
+    p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, sink_size=4)
+    assert _fwd(p) == 2 and "sinks" in _err()
