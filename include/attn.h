@@ -31,7 +31,8 @@
  *     contiguous (unit stride). Every tensor base pointer must be 16-byte
  *     aligned and every stride a multiple of 16 bytes.
  *   - Supported: d in {64, 128}; (in_dtype, out_dtype) in {(F32, F32),
- *     (BF16, BF16), (FP8_E4M3, BF16)}. F32 runs in batch mode only (a plain
+ *     (BF16, BF16), (BF16, FP8_E4M3), (FP8_E4M3, BF16), (FP8_E4M3, FP8_E4M3)}.
+ *     FP8 output is E4M3FN with a per-tensor scale (o_scale). F32 runs in batch mode only (a plain
  *     vector-ALU kernel). The split-KV decode path (sq * Hq / Hkv <= 16, and
  *     every attn_fwd_paged call) takes BF16 only. FP8 means OCP E4M3FN; the
  *     value of a stored byte x is e4m3(x) * descale of its tensor.
@@ -115,10 +116,13 @@ typedef struct {
                           bias[b*bias_stride[0] + h*bias_stride[1] + i*bias_stride[2] + j],
                           16-byte aligned with bias_stride[2] a multiple of 4. */
   int64_t bias_stride[3];
+  float o_scale;       /* FP8 output only: O is stored as the saturating E4M3FN conversion
+                          (round to nearest even, clamped to +-448) of O * o_scale, the
+                          page's scale_o with its saturating O conversion; else ignored */
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
- * descales 1, automatic split size, no sinks, no bias. */
+ * descales 1, automatic split size, no sinks, no bias, o_scale 1. */
 void attn_params_init(attn_params_t* p, float scale);
 
 /*

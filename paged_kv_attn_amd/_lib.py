@@ -33,6 +33,7 @@ class AttnParams(ctypes.Structure):
         ("bias_type", ctypes.c_int),
         ("bias", ctypes.c_void_p),
         ("bias_stride", ctypes.c_int64 * 3),
+        ("o_scale", ctypes.c_float),
     ]
 
 

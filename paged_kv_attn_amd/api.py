@@ -21,13 +21,14 @@ _IN_TYPES = {torch.float32: _lib.ATTN_F32, torch.bfloat16: _lib.ATTN_BF16,
 
 
 def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size=0, sink_logits=None,
-            bias=None, alibi_slopes=None):
+            bias=None, alibi_slopes=None, out_dtype=None, o_scale=1.0):
     if dtype not in _IN_TYPES:
         raise TypeError(f"unsupported input dtype {dtype}")
     p = AttnParams()
     lib().attn_params_init(ctypes.byref(p), float(scale if scale is not None else 1.0 / math.sqrt(d)))
     p.in_dtype = _IN_TYPES[dtype]
-    p.out_dtype = _lib.ATTN_F32 if dtype == torch.float32 else _lib.ATTN_BF16
+    p.out_dtype = _IN_TYPES[out_dtype_for(dtype, out_dtype)]
+    p.o_scale = float(o_scale)
     p.softcap = float(softcap)
     if window is not None:
         p.window_left, p.window_right = int(window[0]), int(window[1])
@@ -58,7 +59,12 @@ def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, 
     return p
 
 
-def out_dtype_for(dtype):
+def out_dtype_for(dtype, out_dtype=None):
+    """O's dtype: fp32 for fp32 inputs, else bf16 unless fp8 (E4M3FN) is asked for."""
+    if out_dtype is not None:
+        if out_dtype not in (torch.bfloat16, torch.float8_e4m3fn, torch.float32):
+            raise TypeError(f"unsupported output dtype {out_dtype}")
+        return out_dtype
     return torch.float32 if dtype == torch.float32 else torch.bfloat16
 
 
@@ -98,15 +104,16 @@ def _workspace(nbytes, device, workspace):
 
 def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seqused_q=None,
              seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
-             kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None, bias=None, alibi_slopes=None):
+             kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None, bias=None, alibi_slopes=None,
+             out_dtype=None, o_scale=1.0):
     """Batch mode. q [B, Hq, sq, d], k / v [B, Hkv, sk, d] (any strides, d
     contiguous). Returns (out [B, Hq, sq, d], lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
-                bias, alibi_slopes)
+                bias, alibi_slopes, out_dtype, o_scale)
     if out is None:
-        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
+        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
     ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, sk)
@@ -120,16 +127,17 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
                     causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
-                    return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None):
+                    return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None,
+                    o_scale=1.0):
     """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
     on the device. Returns (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
-                alibi_slopes=alibi_slopes)
+                alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     if out is None:
-        out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype), device=q.device)
+        out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     st = lambda t: i64_array(t.stride()[:2])  # noqa: E731
@@ -142,7 +150,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
                    softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
-                   workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None):
+                   workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None, o_scale=1.0):
     """Paged KV cache. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
     (any strides, d contiguous; K and V pools with equal strides);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
@@ -156,9 +164,9 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
         raise TypeError("block_table and seqlens_k must be int32")
     W = block_table.shape[1]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
-                alibi_slopes=alibi_slopes)
+                alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     if out is None:
-        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype), device=q.device)
+        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
     ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, W * page_size)

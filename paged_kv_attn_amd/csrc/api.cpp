@@ -54,6 +54,12 @@ int n_splits_for(int split, int max_len) { return max_len > 0 ? (max_len + split
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// factor applied to the normalised O before it is stored: the value descale of
+// fp8 inputs, times o_scale for fp8 output
+float out_mul(const attn_params_t* p) {
+  return (p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f) * (p->out_dtype == ATTN_FP8_E4M3 ? p->o_scale : 1.0f);
+}
+
 // Bias in the kernels' logit units: the kernels compare and exponentiate
 // x * c_exp2 in base 2, so a natural-log bias b enters as b * log2(e) / c_exp2.
 void set_bias(const attn_params_t* p, float c_exp2, attn::PrefillArgs* a) {
@@ -76,8 +82,8 @@ size_t decode_ws_bytes(int B, int Hkv, int n_splits, int m_rows, int d) {
 attn_status_t check_params(const attn_params_t* p, int d) {
   if (!p) return fail(ATTN_EINVAL, "params is NULL");
   const bool pair_ok = (p->in_dtype == ATTN_F32 && p->out_dtype == ATTN_F32) ||
-                       (p->in_dtype == ATTN_BF16 && p->out_dtype == ATTN_BF16) ||
-                       (p->in_dtype == ATTN_FP8_E4M3 && p->out_dtype == ATTN_BF16);
+                       ((p->in_dtype == ATTN_BF16 || p->in_dtype == ATTN_FP8_E4M3) &&
+                        (p->out_dtype == ATTN_BF16 || p->out_dtype == ATTN_FP8_E4M3));
   if (!pair_ok) return fail(ATTN_ENOTSUP, "unsupported (in_dtype, out_dtype) = (%d, %d)", p->in_dtype, p->out_dtype);
   if (d != 64 && d != 128) return fail(ATTN_ENOTSUP, "head dim %d not supported (64 or 128)", d);
   if (!(p->scale > 0.0f) || !std::isfinite(p->scale)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
@@ -90,6 +96,8 @@ attn_status_t check_params(const attn_params_t* p, int d) {
   }
   if (p->kv_split_tokens < 0 || p->kv_split_tokens % 64 != 0 || p->kv_split_tokens > 2048)
     return fail(ATTN_EINVAL, "kv_split_tokens must be 0 or a multiple of 64 in [64, 2048]");
+  if (p->out_dtype == ATTN_FP8_E4M3 && (!(p->o_scale > 0.0f) || !std::isfinite(p->o_scale)))
+    return fail(ATTN_EINVAL, "o_scale must be finite and > 0 for fp8 output");
   if (p->sink_size < 0) return fail(ATTN_EINVAL, "sink_size must be >= 0");
   if (p->sink_logits && ((uintptr_t)p->sink_logits & 3u)) return fail(ATTN_EINVAL, "sink_logits is not 4-byte aligned");
   if (p->in_dtype == ATTN_F32 && (p->sink_size > 0 || p->sink_logits))
@@ -173,6 +181,7 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->bias_type = ATTN_BIAS_NONE;
   p->bias = nullptr;
   p->bias_stride[0] = p->bias_stride[1] = p->bias_stride[2] = 0;
+  p->o_scale = 1.0f;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -259,7 +268,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
     c.seqlens_k = seqused_k; c.sk = sk;
     c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
-    c.split_tokens = split; c.n_splits = nsp; c.o_mul = 1.0f;
+    c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
+  c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
     c.sink_logits = p->sink_logits;
     return launched(attn::launch_decode(a, c, d, false, B, s));
   }
@@ -276,7 +286,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
   a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
-  a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
+  a.o_mul = out_mul(p);
+  a.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
@@ -332,7 +343,8 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
   a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + rows_tile - 1) / rows_tile);
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
-  a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
+  a.o_mul = out_mul(p);
+  a.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
@@ -368,7 +380,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   const int eb = elem_bytes(p->in_dtype);
   TRY(check_strides("q", q_stride, 3, eb));
   TRY(check_strides("kv", kv_stride, 3, eb));
-  TRY(check_strides("o", o_stride, 3, 2));
+  TRY(check_strides("o", o_stride, 3, elem_bytes(p->out_dtype)));
   if (B == 0 || sq == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
@@ -392,7 +404,8 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
     a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
-    a.o_mul = p->in_dtype == ATTN_FP8_E4M3 ? p->v_descale : 1.0f;
+    a.o_mul = out_mul(p);
+  a.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
     set_bias(p, c_exp2, &a);
@@ -426,7 +439,8 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
   c.seqlens_k = seqlens_k; c.sk = max_len;
   c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
-  c.split_tokens = split; c.n_splits = nsp; c.o_mul = 1.0f;
+  c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
+  c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
   c.sink_logits = p->sink_logits;
   return launched(attn::launch_decode(a, c, d, true, B, (hipStream_t)stream));
 }

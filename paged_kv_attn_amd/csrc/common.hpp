@@ -155,6 +155,19 @@ __device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_of
   return __builtin_bit_cast(U128, v);
 }
 
+// Four floats -> four OCP E4M3FN bytes (low byte = a), round to nearest even,
+// saturated to +-448 first (so finite inputs never become NaN).
+__device__ __forceinline__ uint32_t pack_fp8x4_sat(float a, float b, float c, float d) {
+  const float m = 448.0f;
+  a = __builtin_fminf(__builtin_fmaxf(a, -m), m);
+  b = __builtin_fminf(__builtin_fmaxf(b, -m), m);
+  c = __builtin_fminf(__builtin_fmaxf(c, -m), m);
+  d = __builtin_fminf(__builtin_fmaxf(d, -m), m);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
 // 8 fp8 bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
 __device__ __forceinline__ U128 fp8x8_to_bf16x8(U64 in) {
   U128 r;

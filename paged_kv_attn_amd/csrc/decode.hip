@@ -354,11 +354,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (sink > kNegInf) wsum += fast_exp2((sink - M) * kLog2e);
   }
   const float inv = (M == kNegInf) ? 0.0f : a.o_mul / wsum;
-  __bf16* op = (__bf16*)a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr;
-  if (kPer == 2) {
-    *(uint32_t*)(op + 2 * lane) = pack_bf16x2(o[0] * inv, o[1] * inv);
+  const int64_t o_elem = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr;
+  if (a.out_fp8) {  // saturated E4M3FN
+    uint8_t* op = (uint8_t*)a.o + o_elem;
+    const uint32_t w = pack_fp8x4_sat(o[0] * inv, kPer == 2 ? o[1] * inv : 0.0f, 0.0f, 0.0f);
+    if (kPer == 2) {
+      *(uint16_t*)(op + 2 * lane) = (uint16_t)w;
+    } else {
+      op[lane] = (uint8_t)w;
+    }
   } else {
-    op[lane] = (__bf16)(o[0] * inv);
+    __bf16* op = (__bf16*)a.o + o_elem;
+    if (kPer == 2) {
+      *(uint32_t*)(op + 2 * lane) = pack_bf16x2(o[0] * inv, o[1] * inv);
+    } else {
+      op[lane] = (__bf16)(o[0] * inv);
+    }
   }
   if (a.lse && lane == 0)
     a.lse[((int64_t)b * a.hq + hq) * a.sq + pos] = (M == kNegInf) ? kNegInf : M + __builtin_log2f(wsum) * kLn2;

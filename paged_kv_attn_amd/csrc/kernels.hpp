@@ -41,7 +41,8 @@ struct PrefillArgs {
   float c_exp2;               // multiplier taking the kernel's logit domain to log2 units
   float softcap_pre;          // softcap: raw dot * softcap_pre = (scaled logit) / cap
   float softcap_post;         // softcap: cap * log2(e)
-  float o_mul;                // value descale applied to O (1 unless FP8)
+  float o_mul;                // applied to the normalised O: fp8 value descale, fp8-output scale
+  int out_fp8;                // O stored as saturated E4M3FN (else bf16)
   int wl, wr;                 // window (-1 = unbounded)
   int sink_size;              // keys j < sink_size ignore the left bound
   const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
@@ -87,7 +88,8 @@ struct CombineArgs {
   const int32_t* seqlens_k;   // nullable (then sk)
   int sk;
   int B, sq, hq, hkv, ratio, m_rows, split_tokens, n_splits;
-  float o_mul;
+  float o_mul;                // applied to the normalised O (fp8-output scale)
+  int out_fp8;                // O stored as saturated E4M3FN (else bf16)
   const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
 };
 

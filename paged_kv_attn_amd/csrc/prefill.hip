@@ -520,16 +520,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    char* op = (char*)a.o + (o_off + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr) * 2;
+    const int ob = a.out_fp8 ? 1 : 2;  // bytes per stored O element
+    char* op = (char*)a.o + (o_off + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr) * ob;
 #pragma unroll
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * dblk + 8 * q4 + 4 * h;
-        U64 w;
-        w.x = pack_bf16x2(acc[dblk][4 * q4 + 0] * inv, acc[dblk][4 * q4 + 1] * inv);
-        w.y = pack_bf16x2(acc[dblk][4 * q4 + 2] * inv, acc[dblk][4 * q4 + 3] * inv);
-        *(U64*)(op + d * 2) = w;
+        const float o0 = acc[dblk][4 * q4 + 0] * inv, o1 = acc[dblk][4 * q4 + 1] * inv;
+        const float o2 = acc[dblk][4 * q4 + 2] * inv, o3 = acc[dblk][4 * q4 + 3] * inv;
+        if (a.out_fp8) {
+          *(uint32_t*)(op + d) = pack_fp8x4_sat(o0, o1, o2, o3);
+        } else {
+          U64 w;
+          w.x = pack_bf16x2(o0, o1);
+          w.y = pack_bf16x2(o2, o3);
+          *(U64*)(op + d * 2) = w;
+        }
       }
     }
     if (a.lse && h == 0) a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] = lse2 * kLn2;
