@@ -74,6 +74,14 @@ __device__ __forceinline__ int swz(int row, int nchunks) {
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
+// Workgroups resident on one XCD at a time: 32 CUs, two workgroups each.
+constexpr int kSlotsPerXcd = 64;
+// Units (sequence, kv-head) per dispatch group: as many as one group's query
+// tiles take to fill the XCD's slots (at least one).
+__host__ __device__ inline int group_units(int n_qtiles) {
+  return n_qtiles >= kSlotsPerXcd ? 1 : kSlotsPerXcd / n_qtiles;
+}
+
 template <bool FP8> struct QFrag;
 template <> struct QFrag<false> { using T = U128; };
 template <> struct QFrag<true> { using T = U64; };
@@ -96,17 +104,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // XCD-aware work order. Workgroups are dispatched round-robin over the 8
   // XCDs (hardware id w goes to XCD w % 8), each with its own L2. A unit is one
   // (sequence, kv-head): all its query tiles read the same K/V, so they run on
-  // one XCD and share its L2, one unit after another, heaviest (latest, under a
-  // causal mask) tile first. Units are dealt to the XCDs round-robin, so with
+  // one XCD and share its L2. Units are dealt to the XCDs round-robin, so with
   // sequences of different lengths every XCD still gets a similar share of the
   // work (with Hkv a multiple of 8, XCD x takes kv-heads x, x+8, ... of every
-  // sequence).
+  // sequence). Each XCD takes its units G at a time (G = group_units), G just
+  // large enough for one group's query tiles to fill the XCD's slots, so the
+  // K/V of only about one group is live in L2. Inside a group, tiles go out
+  // by rank across its units, heaviest (latest, under a causal mask) first:
+  // the next group's heavy tiles then land on the slots that the previous
+  // group's light tiles free first (longest-processing-time-first order),
+  // instead of the last unit's heavy tiles starting when most slots are done.
   const int n_units = a.hkv * a.nz;
   const int xcd = (int)(blockIdx.x % kXcds);
   const int k_x = (int)(blockIdx.x / kXcds);       // position in this XCD's list
-  const int unit = xcd + kXcds * (k_x / a.n_qtiles);
+  const int G = group_units(a.n_qtiles);
+  const int gsz = G * a.n_qtiles;
+  const int qt_i = (k_x % gsz) / G;                // rank: 0 = heaviest
+  const int unit = xcd + kXcds * ((k_x / gsz) * G + (k_x % gsz) % G);
   if (unit >= n_units) return;
-  const int qt_i = k_x % a.n_qtiles;
   const int g = unit % a.hkv;                      // kv-head
   const int z = unit / a.hkv;                      // batch entry or sequence
   const int qt = MASK ? a.n_qtiles - 1 - qt_i : qt_i;
@@ -548,7 +563,9 @@ hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
   const int64_t n_units = (int64_t)a.hkv * nz;
-  const int64_t grid = (n_units + kXcds - 1) / kXcds * kXcds * a.n_qtiles;
+  const int64_t units_x = (n_units + kXcds - 1) / kXcds;   // units per XCD
+  const int64_t G = group_units(a.n_qtiles);
+  const int64_t grid = kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
   hipLaunchKernelGGL((prefill_kernel<D, FP8, MODE, MASK, SOFTCAP, BIAS>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, b);
   return hipGetLastError();
