@@ -119,10 +119,22 @@ typedef struct {
   float o_scale;       /* FP8 output only: O is stored as the saturating E4M3FN conversion
                           (round to nearest even, clamped to +-448) of O * o_scale, the
                           page's scale_o with its saturating O conversion; else ignored */
+  const int32_t* cache_batch_idx; /* attn_fwd only (batch mode), nullable DEVICE int32 [B]: the
+                          K/V batch entry that batch entry b reads (the cache_batch_idx of the
+                          Composable Kernel page's batch-mode arguments), so K and V are
+                          [cache_batch_count, Hkv, sk, d] caches and Q, O, LSE, seqused_q/k
+                          and the bias keep index b. An index outside [0, cache_batch_count)
+                          gives entry b no keys (O = 0, LSE = -inf or its sink logit): it is
+                          never dereferenced. BF16 / FP8 only. */
+  int cache_batch_count; /* K/V batch entries when cache_batch_idx is set (>= 1) */
+  int min_seqlen_q;    /* attn_fwd_varlen only: a sequence with Lq <= min_seqlen_q is skipped
+                          and its O and LSE rows are left untouched (the page's min_seqlen_q
+                          of group mode); 0 skips only empty sequences, i.e. nothing. */
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
- * descales 1, automatic split size, no sinks, no bias, o_scale 1. */
+ * descales 1, automatic split size, no sinks, no bias, o_scale 1, no cache
+ * batch index, min_seqlen_q 0. */
 void attn_params_init(attn_params_t* p, float scale);
 
 /*

@@ -188,11 +188,16 @@ def _map_pool(fn, jobs, workers):
 
 def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1,
                     seqused_q=None, seqused_k=None, workers=1, sink_size=0, sink_logits=None,
-                    bias=None, alibi_slopes=None):
+                    bias=None, alibi_slopes=None, cache_batch_idx=None):
     """Batch mode: q [B, Hq, sq, d], k/v [B, Hkv, sk, d] (fp64).
 
     Per batch b the used lengths are Lq = seqused_q[b] (else sq) and
     Lk = seqused_k[b] (else sk); q-head h reads kv-head h // (Hq // Hkv).
+    ``cache_batch_idx`` ([B] or None): batch entry b takes its keys and values
+    from entry cache_batch_idx[b] of k / v (then [C, Hkv, sk, d]), the
+    ``cache_batch_idx`` of the Composable Kernel page's batch-mode arguments;
+    Lq, Lk, the bias and the outputs keep index b. An index outside [0, C),
+    which the page leaves undefined, is read here as "no keys" (Lk = 0).
     ``sink_size`` and ``sink_logits`` ([Hq] or None) as in head_attention.
     ``bias``: elementwise [B, Hq, sq, sk] (its top-left [Lq, Lk] block is used);
     ``alibi_slopes``: [B, Hq] or [Hq] (shared by every batch entry).
@@ -214,6 +219,9 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
         b, h = bh
         lq = sq if seqused_q is None else int(seqused_q[b])
         lk = k.shape[2] if seqused_k is None else int(seqused_k[b])
+        kb = b if cache_batch_idx is None else int(cache_batch_idx[b])
+        if not 0 <= kb < k.shape[0]:
+            kb, lk = 0, 0
         g = h // ratio
         sink = -np.inf if sink_logits is None else float(sink_logits[h])
         bh = None
@@ -223,7 +231,7 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
             sl = np.asarray(alibi_slopes, dtype=np.float64)
             ab = alibi_bias(lq, lk, sl[h] if sl.ndim == 1 else sl[b, h])
             bh = ab if bh is None else bh + ab
-        oh, lh = head_attention(q[b, h, :lq], k[b, g, :lk], v[b, g, :lk], scale, softcap,
+        oh, lh = head_attention(q[b, h, :lq], k[kb, g, :lk], v[kb, g, :lk], scale, softcap,
                                 window_left, window_right, sink_size=sink_size, sink_logit=sink, bias=bh)
         return b, h, lq, oh, lh
 
@@ -235,13 +243,15 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
                      window_left=-1, window_right=-1, workers=1, sink_size=0, sink_logits=None,
-                     alibi_slopes=None):
+                     alibi_slopes=None, min_seqlen_q=0):
     """Varlen / group mode: sequences packed along the token axis.
 
     q [Tq, Hq, d], k/v [Tk, Hkv, d]; sequence s owns query tokens
     cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and key tokens likewise (the
     ``seqstart_q/k`` offsets of the Composable Kernel page's group-mode
     arguments). Each sequence is sliced out and the batch definition applied.
+    A sequence with Lq <= ``min_seqlen_q`` is skipped (the page's group-mode
+    ``min_seqlen_q`` early exit): its rows stay NaN, i.e. not computed.
     Returns O [Tq, Hq, dv] and LSE [Hq, Tq].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -253,6 +263,8 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
     o = np.full((tq, hq, v.shape[2]), np.nan)
     lse = np.full((hq, tq), np.nan)
     for s in range(len(cq) - 1):
+        if cq[s + 1] - cq[s] <= min_seqlen_q:
+            continue
         qs = q[cq[s]:cq[s + 1]].transpose(1, 0, 2)[None]
         ks = k[ck[s]:ck[s + 1]].transpose(1, 0, 2)[None]
         vs = v[ck[s]:ck[s + 1]].transpose(1, 0, 2)[None]

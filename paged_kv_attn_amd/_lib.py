@@ -34,6 +34,9 @@ class AttnParams(ctypes.Structure):
         ("bias", ctypes.c_void_p),
         ("bias_stride", ctypes.c_int64 * 3),
         ("o_scale", ctypes.c_float),
+        ("cache_batch_idx", ctypes.c_void_p),
+        ("cache_batch_count", ctypes.c_int),
+        ("min_seqlen_q", ctypes.c_int),
     ]
 
 

@@ -105,13 +105,21 @@ def _workspace(nbytes, device, workspace):
 def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seqused_q=None,
              seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
              kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None, bias=None, alibi_slopes=None,
-             out_dtype=None, o_scale=1.0):
+             out_dtype=None, o_scale=1.0, cache_batch_idx=None):
     """Batch mode. q [B, Hq, sq, d], k / v [B, Hkv, sk, d] (any strides, d
-    contiguous). Returns (out [B, Hq, sq, d], lse [B, Hq, sq] or None)."""
+    contiguous). With ``cache_batch_idx`` (int32 [B] on the device) k / v are
+    [C, Hkv, sk, d] caches and batch entry b reads entry cache_batch_idx[b]
+    (an index outside [0, C) reads no keys). Returns (out [B, Hq, sq, d],
+    lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 bias, alibi_slopes, out_dtype, o_scale)
+    if cache_batch_idx is not None:
+        if cache_batch_idx.dtype != torch.int32 or cache_batch_idx.numel() < B or not cache_batch_idx.is_contiguous():
+            raise TypeError("cache_batch_idx must be a contiguous int32 tensor with B entries")
+        p.cache_batch_idx = cache_batch_idx.data_ptr()
+        p.cache_batch_count = k.shape[0]
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
@@ -128,14 +136,17 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
                     causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
                     return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None,
-                    o_scale=1.0):
+                    o_scale=1.0, min_seqlen_q=0):
     """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
-    on the device. Returns (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
+    on the device. Sequences with at most ``min_seqlen_q`` query tokens are
+    skipped: their rows of out / lse are left as they were. Returns
+    (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
+    p.min_seqlen_q = int(min_seqlen_q)
     if out is None:
         out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:

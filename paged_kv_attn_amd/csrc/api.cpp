@@ -113,6 +113,20 @@ attn_status_t check_params(const attn_params_t* p, int d) {
     if (p->bias_type == ATTN_BIAS_ELEMENTWISE && (((uintptr_t)p->bias & 15u) || p->bias_stride[2] % 4))
       return fail(ATTN_EINVAL, "an elementwise bias needs a 16-byte aligned base and a row stride multiple of 4");
   }
+  if (p->min_seqlen_q < 0) return fail(ATTN_EINVAL, "min_seqlen_q must be >= 0");
+  return ATTN_OK;
+}
+
+// The cache batch index (batch mode only) and min_seqlen_q (varlen only).
+attn_status_t check_mode_fields(const attn_params_t* p, bool batch_mode, bool varlen_mode) {
+  if (p->cache_batch_idx) {
+    if (!batch_mode) return fail(ATTN_EINVAL, "cache_batch_idx applies to attn_fwd (batch mode) only");
+    if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "cache_batch_idx needs bf16 or fp8 inputs");
+    if ((uintptr_t)p->cache_batch_idx & 3u) return fail(ATTN_EINVAL, "cache_batch_idx is not 4-byte aligned");
+    if (p->cache_batch_count < 1) return fail(ATTN_EINVAL, "cache_batch_count must be >= 1 with cache_batch_idx");
+  }
+  if (p->min_seqlen_q != 0 && !varlen_mode)
+    return fail(ATTN_EINVAL, "min_seqlen_q applies to attn_fwd_varlen only");
   return ATTN_OK;
 }
 
@@ -182,6 +196,9 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->bias = nullptr;
   p->bias_stride[0] = p->bias_stride[1] = p->bias_stride[2] = 0;
   p->o_scale = 1.0f;
+  p->cache_batch_idx = nullptr;
+  p->cache_batch_count = 0;
+  p->min_seqlen_q = 0;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -204,6 +221,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
                        const int32_t* seqused_q, const int32_t* seqused_k, void* workspace,
                        size_t workspace_bytes, void* stream) {
   TRY(check_params(p, d));
+  TRY(check_mode_fields(p, true, false));
   if (B < 0 || Hq <= 0 || Hkv <= 0 || sq < 0 || sk < 0) return fail(ATTN_EINVAL, "bad sizes B=%d Hq=%d Hkv=%d sq=%d sk=%d", B, Hq, Hkv, sq, sk);
   if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
   const int eb = elem_bytes(p->in_dtype), ob = elem_bytes(p->out_dtype);
@@ -259,6 +277,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size;
+    a.cache_idx = p->cache_batch_idx; a.cache_count = p->cache_batch_count;
     set_bias(p, c_exp2, &a);
     const size_t units = (size_t)B * Hkv * nsp * m_rows;
     a.part_o = (float*)workspace;
@@ -267,6 +286,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
     c.seqlens_k = seqused_k; c.sk = sk;
+    c.cache_idx = p->cache_batch_idx; c.cache_count = p->cache_batch_count;
     c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
     c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
   c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
@@ -282,6 +302,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_sr = o_stride[2];
   a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
   a.seqused_q = seqused_q; a.seqused_k = seqused_k;
+  a.cache_idx = p->cache_batch_idx; a.cache_count = p->cache_batch_count;
   a.sq = sq; a.sk = sk; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
   const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
   a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);
@@ -309,6 +330,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   (void)workspace_bytes;
   (void)max_seqlen_k;
   TRY(check_params(p, d));
+  TRY(check_mode_fields(p, false, true));
   if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
     return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "fp32 inputs are supported in batch mode only");
@@ -339,6 +361,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.o_sb = 0; a.o_sh = o_stride[1]; a.o_sr = o_stride[0];
   a.lse_sb = 0; a.lse_sh = total_q;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.min_seqlen_q = p->min_seqlen_q;
   a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
   const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
   a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + rows_tile - 1) / rows_tile);
@@ -357,6 +380,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
                              int num_pages, const int64_t q_stride[3], const int64_t kv_stride[3],
                              const int64_t o_stride[3], void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_params(p, d));
+  TRY(check_mode_fields(p, false, false));
   if (B < 0 || sq < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
     return fail(ATTN_EINVAL, "bad sizes B=%d sq=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", B, sq, Hq, Hkv,
                 block_table_stride, num_pages);

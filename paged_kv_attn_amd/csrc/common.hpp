@@ -186,6 +186,14 @@ __device__ __forceinline__ U128 fp8x8_to_bf16x8(U64 in) {
   return r;
 }
 
+// K/V batch entry read by batch entry b: idx[b] with a cache batch index, else
+// b; -1 (no keys) for an index outside [0, count).
+__device__ __forceinline__ int kv_entry(const int32_t* idx, int count, int b) {
+  if (!idx) return b;
+  const int e = idx[b];
+  return (e >= 0 && e < count) ? e : -1;
+}
+
 // tanh for the logit soft-cap, from exp: tanh(x) = sign(x) (1 - e) / (1 + e),
 // e = exp(-2|x|). Relative error a few ulp of fp32 away from 0; near 0 the
 // absolute error is ~1e-7, far below the bf16 rounding of P.

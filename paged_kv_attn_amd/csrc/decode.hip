@@ -89,7 +89,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int g = blockIdx.x;      // kv-heads fastest: the units running together read the
   const int split = blockIdx.y;  // same token rows (shared DRAM pages in a [page, slot, head] pool)
   const int b = blockIdx.z;
-  const int Lk = a.seqlens_k ? a.seqlens_k[b] : a.sk;
+  // K/V batch entry of contiguous K/V (cache batch index; out of range: no keys)
+  const int kb = PAGED ? b : kv_entry(a.cache_idx, a.cache_count, b);
+  const int Lk = kb < 0 ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
   const int t0 = split * a.split_tokens;
   if (t0 >= Lk) return;  // empty split: the combine reads only ceil(Lk / split_tokens) partials
   const int t1 = min(Lk, t0 + a.split_tokens);
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       const int page = __builtin_amdgcn_readlane(pg, gs / a.page_size - p_first);
       return (const char*)pool + ((int64_t)page * sb + (int64_t)g * sh + (int64_t)(gs % a.page_size) * sr) * 2;
     }
-    return (const char*)pool + ((int64_t)b * sb + (int64_t)g * sh + (int64_t)gs * sr) * 2;
+    return (const char*)pool + ((int64_t)kb * sb + (int64_t)g * sh + (int64_t)gs * sr) * 2;
   };
   // issue the loads of granule gs into the LDS buffers kb / vb (whole rows,
   // non-temporal: every K and V row is read once). A granule at or past t_hi is
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int b = (int)(row / ((int64_t)a.sq * a.hq));
   const int g = hq / a.ratio;
   const int r = pos * a.ratio + hq % a.ratio;  // packed row
-  const int Lk = a.seqlens_k ? a.seqlens_k[b] : a.sk;
+  const int Lk = kv_entry(a.cache_idx, a.cache_count, b) < 0 ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
   const int n = Lk > 0 ? (Lk + a.split_tokens - 1) / a.split_tokens : 0;
   const int64_t unit0 = ((int64_t)b * a.hkv + g) * a.n_splits;
   const float* lse_p = a.part_lse + unit0 * a.m_rows + r;   // split s at lse_p[s * m_rows]

@@ -51,6 +51,9 @@ struct PrefillArgs {
   int64_t bias_sb, bias_sh, bias_sr;
   uint32_t bias_bytes;        // elementwise: bytes of one batch entry's bias (reads past it return 0)
   float bias_mul;             // natural-log logit units -> the kernel's logit units
+  const int32_t* cache_idx;   // batch mode, nullable: K/V batch entry of each batch entry
+  int cache_count;            // K/V batch entries (indices outside [0, cache_count) read no keys)
+  int min_seqlen_q;           // varlen mode: sequences with Lq <= min_seqlen_q are skipped
 };
 
 // Split-KV decode (one workgroup = one split of one request and kv-head).
@@ -77,6 +80,8 @@ struct DecodeArgs {
   float bias_mul;             // natural-log logit units -> the kernel's logit units
   float* part_o;              // [B][hkv][n_splits][m_rows][d] fp32
   float* part_lse;            // [B][hkv][n_splits][m_rows]
+  const int32_t* cache_idx;   // contiguous K/V only, nullable: K/V batch entry of each request
+  int cache_count;
 };
 
 struct CombineArgs {
@@ -91,6 +96,8 @@ struct CombineArgs {
   float o_mul;                // applied to the normalised O (fp8-output scale)
   int out_fp8;                // O stored as saturated E4M3FN (else bf16)
   const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
+  const int32_t* cache_idx;   // as DecodeArgs (an out-of-range entry has no keys)
+  int cache_count;
 };
 
 // fp32 path (batch mode).

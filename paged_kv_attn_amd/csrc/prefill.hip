@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int q0 = a.cu_q[z], k0 = a.cu_k[z];
     Lq = a.cu_q[z + 1] - q0;
     Lk = a.cu_k[z + 1] - k0;
+    if (Lq <= a.min_seqlen_q) return;  // skipped sequence: its rows stay untouched
     q_off = (int64_t)q0 * a.q_sr;
     k_off = (int64_t)k0 * a.k_sr;
     v_off = (int64_t)k0 * a.v_sr;
@@ -152,9 +153,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   } else {
     Lq = a.seqused_q ? a.seqused_q[z] : a.sq;
     Lk = a.seqused_k ? a.seqused_k[z] : a.sk;
+    // K/V batch entry (cache batch index); an out-of-range index reads no keys
+    int kz = kv_entry(a.cache_idx, a.cache_count, z);
+    if (kz < 0) {
+      kz = 0;
+      Lk = 0;
+    }
     q_off = (int64_t)z * a.q_sb;
-    k_off = (int64_t)z * a.k_sb;
-    v_off = (int64_t)z * a.v_sb;
+    k_off = (int64_t)kz * a.k_sb;
+    v_off = (int64_t)kz * a.v_sb;
     o_off = (int64_t)z * a.o_sb;
     lse_off = (int64_t)z * a.lse_sb;
   }

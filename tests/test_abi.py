@@ -37,7 +37,8 @@ def test_params_struct_layout_matches_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct \{(.*?)\} attn_params_t;", text, re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
-    fields = re.findall(r"\b(int64_t|int|float\s*\*?)\s*([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)(?:\[\d+\])?\s*;", body)
+    fields = re.findall(r"\b(int64_t|int32_t\s*\*|int|float\s*\*?)\s*([a-z_0-9]+(?:\s*,\s*[a-z_0-9]+)*)(?:\[\d+\])?\s*;",
+                        body)
     names = [n.strip() for _, group in fields for n in group.split(",")]
     assert names == [f for f, _ in AttnParams._fields_]
 
@@ -216,3 +217,29 @@ def test_sink_validation():
     assert _fwd(p) == 1 and "sink_logits" in _err()
     p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, sink_size=4)
     assert _fwd(p) == 2 and "sinks" in _err()
+
+
+def test_cache_batch_idx_and_min_seqlen_q_validation():
+    p = _params(cache_batch_idx=0x10000, cache_batch_count=0)
+    assert _fwd(p) == 1 and "cache_batch_count" in _err()
+    p = _params(cache_batch_idx=0x10002, cache_batch_count=2)
+    assert _fwd(p) == 1 and "4-byte" in _err()
+    p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, cache_batch_idx=0x10000, cache_batch_count=2)
+    assert _fwd(p) == 2 and "cache_batch_idx" in _err()
+    p = _params(cache_batch_idx=0x10000, cache_batch_count=2)
+    assert _paged(p) == 1 and "batch mode" in _err()
+    p = _params(min_seqlen_q=3)
+    assert _fwd(p) == 1 and "attn_fwd_varlen only" in _err()
+    assert _paged(p) == 1 and "attn_fwd_varlen only" in _err()
+    p = _params(min_seqlen_q=-1)
+    assert _fwd(p) == 1 and "min_seqlen_q" in _err()
+    p = _params(cache_batch_idx=0x10000, cache_batch_count=2)
+    st = [2 * 128, 128]
+    r = lib().attn_fwd_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 2, 10, 5, 5, 2, 2, 128,
+                              i64_array(st), i64_array(st), i64_array(st), i64_array(st), NULL, 0, NULL)
+    assert r == 1 and "batch mode" in _err()
+
+
+def test_params_init_new_fields():
+    p = _params()
+    assert p.cache_batch_idx is None and p.cache_batch_count == 0 and p.min_seqlen_q == 0

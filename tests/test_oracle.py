@@ -470,3 +470,63 @@ def test_alibi_bias_matrix():
     for i in range(3):
         for j in range(5):
             assert b[i, j] == -0.5 * abs(i + 2 - j)
+
+
+# ---------------------------------------------------------------------------
+# KV-cache addressing extras: the cache batch index of batch mode and the
+# min_seqlen_q skip of group (varlen) mode.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cache_batch_idx_matches_brute_force(seed):
+    rng = np.random.default_rng(2000 + seed)
+    B, C, Hkv, ratio = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 3)), 2
+    Hq = Hkv * ratio
+    sq, sk, d = int(rng.integers(1, 7)), int(rng.integers(1, 9)), int(rng.integers(1, 5))
+    q = rng.standard_normal((B, Hq, sq, d))
+    k = rng.standard_normal((C, Hkv, sk, d))
+    v = rng.standard_normal((C, Hkv, sk, d))
+    idx = rng.integers(-1, C + 1, size=B)            # includes out-of-range entries
+    used_k = rng.integers(0, sk + 1, size=B)
+    o, lse = oracle.attention_batch(q, k, v, 0.7, 0.0, -1, 0, seqused_k=used_k, cache_batch_idx=idx)
+    for b in range(B):
+        kb = int(idx[b])
+        lk = int(used_k[b]) if 0 <= kb < C else 0
+        for h in range(Hq):
+            g = h // ratio
+            kk = k[kb, g, :lk].tolist() if lk else []
+            vv = v[kb, g, :lk].tolist() if lk else []
+            bo, bl = brute_head(q[b, h].tolist(), kk, vv, 0.7, 0.0, -1, 0, dv=d)
+            np.testing.assert_allclose(o[b, h], np.array(bo).reshape(sq, d), atol=1e-12, rtol=0)
+            np.testing.assert_array_equal(np.isneginf(lse[b, h]), np.isneginf(bl))
+            fin = np.isfinite(bl)
+            np.testing.assert_allclose(lse[b, h][fin], np.array(bl)[fin], atol=1e-12, rtol=0)
+
+
+def test_cache_batch_idx_out_of_range_reads_no_keys():
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((2, 2, 3, 4)), rng.standard_normal((1, 2, 5, 4)), rng.standard_normal((1, 2, 5, 4))
+    o, lse = oracle.attention_batch(q, k, v, 0.5, cache_batch_idx=np.array([3, -2]))
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+    o, lse = oracle.attention_batch(q, k, v, 0.5, cache_batch_idx=np.array([3, -2]), sink_logits=np.array([0.5, -1]))
+    assert np.all(o == 0.0) and np.all(lse[:, 0] == 0.5) and np.all(lse[:, 1] == -1.0)
+
+
+def test_min_seqlen_q_skips_short_sequences():
+    rng = np.random.default_rng(6)
+    lens_q, lens_k = [3, 1, 5, 2, 0], [4, 2, 5, 6, 3]
+    cq, ck = np.concatenate([[0], np.cumsum(lens_q)]), np.concatenate([[0], np.cumsum(lens_k)])
+    q = rng.standard_normal((cq[-1], 4, 3))
+    k = rng.standard_normal((ck[-1], 2, 3))
+    v = rng.standard_normal((ck[-1], 2, 3))
+    o, lse = oracle.attention_varlen(q, k, v, cq, ck, 0.8, 0.0, -1, 0, min_seqlen_q=2)
+    for s, (lq, lk) in enumerate(zip(lens_q, lens_k)):
+        rows = slice(cq[s], cq[s + 1])
+        if lq <= 2:
+            assert np.all(np.isnan(o[rows])) and np.all(np.isnan(lse[:, rows]))
+            continue
+        for h in range(4):
+            bo, bl = brute_head(q[rows, h].tolist(), k[ck[s]:ck[s + 1], h // 2].tolist(),
+                                v[ck[s]:ck[s + 1], h // 2].tolist(), 0.8, 0.0, -1, 0)
+            np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)
