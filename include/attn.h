@@ -130,11 +130,15 @@ typedef struct {
   int min_seqlen_q;    /* attn_fwd_varlen only: a sequence with Lq <= min_seqlen_q is skipped
                           and its O and LSE rows are left untouched (the page's min_seqlen_q
                           of group mode); 0 skips only empty sequences, i.e. nothing. */
+  int head_dim_v;      /* head dim of V and O (the page's hdim_v); 0 = the d argument (hdim_q).
+                          64 or 128. A value different from d is supported by attn_fwd on
+                          prefill shapes (sq*Hq/Hkv > 16) and by attn_fwd_varlen, BF16 / FP8 only;
+                          V's rows then have head_dim_v elements and O's rows too. */
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
  * descales 1, automatic split size, no sinks, no bias, o_scale 1, no cache
- * batch index, min_seqlen_q 0. */
+ * batch index, min_seqlen_q 0, head_dim_v 0 (= d). */
 void attn_params_init(attn_params_t* p, float scale);
 
 /*

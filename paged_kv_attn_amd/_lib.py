@@ -37,6 +37,7 @@ class AttnParams(ctypes.Structure):
         ("cache_batch_idx", ctypes.c_void_p),
         ("cache_batch_count", ctypes.c_int),
         ("min_seqlen_q", ctypes.c_int),
+        ("head_dim_v", ctypes.c_int),
     ]
 
 

@@ -106,22 +106,25 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
              seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
              kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None, bias=None, alibi_slopes=None,
              out_dtype=None, o_scale=1.0, cache_batch_idx=None):
-    """Batch mode. q [B, Hq, sq, d], k / v [B, Hkv, sk, d] (any strides, d
+    """Batch mode. q [B, Hq, sq, d], k [B, Hkv, sk, d], v [B, Hkv, sk, dv] (any strides, d
     contiguous). With ``cache_batch_idx`` (int32 [B] on the device) k / v are
     [C, Hkv, sk, d] caches and batch entry b reads entry cache_batch_idx[b]
-    (an index outside [0, C) reads no keys). Returns (out [B, Hq, sq, d],
+    (an index outside [0, C) reads no keys). Returns (out [B, Hq, sq, dv],
     lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
+    dv = v.shape[3]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 bias, alibi_slopes, out_dtype, o_scale)
+    if dv != d:
+        p.head_dim_v = dv
     if cache_batch_idx is not None:
         if cache_batch_idx.dtype != torch.int32 or cache_batch_idx.numel() < B or not cache_batch_idx.is_contiguous():
             raise TypeError("cache_batch_idx must be a contiguous int32 tensor with B entries")
         p.cache_batch_idx = cache_batch_idx.data_ptr()
         p.cache_batch_count = k.shape[0]
     if out is None:
-        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((B, Hq, sq, dv), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
     ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, sk)
@@ -147,8 +150,11 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     p.min_seqlen_q = int(min_seqlen_q)
+    dv = v.shape[2]
+    if dv != d:
+        p.head_dim_v = dv
     if out is None:
-        out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((Tq, Hq, dv), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     st = lambda t: i64_array(t.stride()[:2])  # noqa: E731
@@ -176,6 +182,8 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     W = block_table.shape[1]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
+    if v_pool.shape[3] != d:
+        p.head_dim_v = v_pool.shape[3]     # rejected by the library (equal dims only in paged mode)
     if out is None:
         out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:

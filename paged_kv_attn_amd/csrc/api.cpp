@@ -114,8 +114,15 @@ attn_status_t check_params(const attn_params_t* p, int d) {
       return fail(ATTN_EINVAL, "an elementwise bias needs a 16-byte aligned base and a row stride multiple of 4");
   }
   if (p->min_seqlen_q < 0) return fail(ATTN_EINVAL, "min_seqlen_q must be >= 0");
+  if (p->head_dim_v != 0 && p->head_dim_v != 64 && p->head_dim_v != 128)
+    return fail(ATTN_ENOTSUP, "head_dim_v %d not supported (0, 64 or 128)", p->head_dim_v);
+  if (p->head_dim_v != 0 && p->head_dim_v != d && p->in_dtype == ATTN_F32)
+    return fail(ATTN_ENOTSUP, "head_dim_v != d needs bf16 or fp8 inputs");
   return ATTN_OK;
 }
+
+// head dim of V and O
+int dim_v(const attn_params_t* p, int d) { return p->head_dim_v ? p->head_dim_v : d; }
 
 // The cache batch index (batch mode only) and min_seqlen_q (varlen only).
 attn_status_t check_mode_fields(const attn_params_t* p, bool batch_mode, bool varlen_mode) {
@@ -199,6 +206,7 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->cache_batch_idx = nullptr;
   p->cache_batch_count = 0;
   p->min_seqlen_q = 0;
+  p->head_dim_v = 0;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -259,6 +267,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
       return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
     if (seqused_q) return fail(ATTN_ENOTSUP, "seqused_q is not supported on the decode path (sq*Hq/Hkv <= 16)");
+    if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "head_dim_v != d is not supported on the decode path (sq*Hq/Hkv <= 16)");
     const int split = plan_split_tokens(p, B, Hkv, sk);
     const int nsp = n_splits_for(split, sk);
     const int m_rows = sq * ratio;
@@ -318,7 +327,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     if (ext >= ((int64_t)1 << 31)) return fail(ATTN_EINVAL, "elementwise bias spans more than 2 GiB per batch entry");
     a.bias_bytes = (uint32_t)ext;
   }
-  return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillBatch, B, s));
+  return launched(attn::launch_prefill(a, d, dim_v(p, d), p->in_dtype, attn::kPrefillBatch, B, s));
 }
 
 attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
@@ -371,7 +380,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
-  return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillVarlen, n, (hipStream_t)stream));
+  return launched(attn::launch_prefill(a, d, dim_v(p, d), p->in_dtype, attn::kPrefillVarlen, n, (hipStream_t)stream));
 }
 
 attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* k_pool, const void* v_pool, void* o,
@@ -381,6 +390,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
                              const int64_t o_stride[3], void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_params(p, d));
   TRY(check_mode_fields(p, false, false));
+  if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "head_dim_v != d is not supported in paged mode (one stride set for both pools)");
   if (B < 0 || sq < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
     return fail(ATTN_EINVAL, "bad sizes B=%d sq=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", B, sq, Hq, Hkv,
                 block_table_stride, num_pages);
@@ -433,7 +443,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
     set_bias(p, c_exp2, &a);
-    return launched(attn::launch_prefill(a, d, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
+    return launched(attn::launch_prefill(a, d, d, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
   }
 
   const int split = plan_split_tokens(p, B, Hkv, max_len);

@@ -119,7 +119,8 @@ struct F32Args {
 };
 
 int prefill_rows_per_tile(int in_type);  // packed query rows per prefill workgroup
-hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, int mode, int batch_or_seqs,
+// d: head dim of Q and K; dv: head dim of V and O ({64, 128} each; paged mode: dv == d)
+hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int batch_or_seqs,
                           hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, bool paged, int B,
                          hipStream_t stream);

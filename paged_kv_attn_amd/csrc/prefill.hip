@@ -44,14 +44,15 @@ constexpr int kBlockN = 64;
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;         // accelerator complex dies on MI355X
 
-template <int D, bool FP8>
+// D: head dim of Q and K; DV: head dim of V and O
+template <int D, int DV, bool FP8>
 struct Traits {
   static constexpr int kElem = FP8 ? 1 : 2;              // stored bytes per Q/K/V element
   static constexpr int kQkSteps = D / 16;                // k-steps of S^T = K Q^T
-  static constexpr int kDBlocks = D / 32;                // 32-row blocks of O^T
+  static constexpr int kDBlocks = DV / 32;               // 32-row blocks of O^T
   static constexpr int kKRow = D * kElem;                // bytes per K row in LDS (no padding)
   static constexpr int kKCh = kKRow / 16;                // 16-byte chunks per K row
-  static constexpr int kVRow = D * 2;                    // bytes per V row in LDS (bf16)
+  static constexpr int kVRow = DV * 2;                   // bytes per V row in LDS (bf16)
   static constexpr int kVCh = kVRow / 16;
   static constexpr int kKTile = kBlockN * kKRow;
   static constexpr int kVTile = kBlockN * kVRow;
@@ -59,7 +60,7 @@ struct Traits {
   static constexpr int kVInstr = kVTile / 1024 / 4;
   static constexpr int kSmem = 2 * kKTile + 2 * kVTile;
   // fp8 V goes through registers (to widen to bf16): 16-byte fp8 chunks per thread
-  static constexpr int kV8Ch = D / 16;
+  static constexpr int kV8Ch = DV / 16;
   static constexpr int kV8Loads = kBlockN * kV8Ch / kThreads;
   static_assert(kKInstr >= 1 && kVInstr >= 1, "tile too small for 4 waves");
   static_assert(!FP8 || kV8Loads >= 1, "fp8 V staging needs >= 1 chunk per thread");
@@ -86,9 +87,9 @@ template <bool FP8> struct QFrag;
 template <> struct QFrag<false> { using T = U128; };
 template <> struct QFrag<true> { using T = U64; };
 
-template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
+template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  using Tr = Traits<D, FP8>;
+  using Tr = Traits<D, DV, FP8>;
   using QT = typename QFrag<FP8>::T;
   // Separate LDS objects per slot: the compiler can then prove that reads of
   // one slot do not alias the HBM->LDS loads in flight into the other, and
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
+template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
@@ -573,49 +574,57 @@ hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   const int64_t units_x = (n_units + kXcds - 1) / kXcds;   // units per XCD
   const int64_t G = group_units(a.n_qtiles);
   const int64_t grid = kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, MODE, MASK, SOFTCAP, BIAS>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MASK, SOFTCAP, BIAS>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, b);
   return hipGetLastError();
 }
 
-template <int D, bool FP8, int MODE, int BIAS>
+template <int D, int DV, bool FP8, int MODE, int BIAS>
 hipError_t launch_b(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
   if (mask)
-    return softcap ? launch_t<D, FP8, MODE, true, true, BIAS>(a, nz, s) : launch_t<D, FP8, MODE, true, false, BIAS>(a, nz, s);
-  return softcap ? launch_t<D, FP8, MODE, false, true, BIAS>(a, nz, s) : launch_t<D, FP8, MODE, false, false, BIAS>(a, nz, s);
+    return softcap ? launch_t<D, DV, FP8, MODE, true, true, BIAS>(a, nz, s) : launch_t<D, DV, FP8, MODE, true, false, BIAS>(a, nz, s);
+  return softcap ? launch_t<D, DV, FP8, MODE, false, true, BIAS>(a, nz, s) : launch_t<D, DV, FP8, MODE, false, false, BIAS>(a, nz, s);
 }
 
-template <int D, bool FP8, int MODE>
+template <int D, int DV, bool FP8, int MODE>
 hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (a.bias_type == kBiasAlibi) return launch_b<D, FP8, MODE, kBiasAlibi>(a, nz, mask, softcap, s);
+  if (a.bias_type == kBiasAlibi) return launch_b<D, DV, FP8, MODE, kBiasAlibi>(a, nz, mask, softcap, s);
   if (MODE == kPrefillBatch && a.bias_type == kBiasElem)
-    return launch_b<D, FP8, MODE, (MODE == kPrefillBatch ? kBiasElem : kBiasNone)>(a, nz, mask, softcap, s);
-  return launch_b<D, FP8, MODE, kBiasNone>(a, nz, mask, softcap, s);
+    return launch_b<D, DV, FP8, MODE, (MODE == kPrefillBatch ? kBiasElem : kBiasNone)>(a, nz, mask, softcap, s);
+  return launch_b<D, DV, FP8, MODE, kBiasNone>(a, nz, mask, softcap, s);
 }
 
-template <int D, bool FP8>
+template <int D, int DV, bool FP8>
 hipError_t launch_f(const PrefillArgs& a, int mode, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (mode == kPrefillVarlen) return launch_m<D, FP8, kPrefillVarlen>(a, nz, mask, softcap, s);
-  if (mode == kPrefillPaged) return launch_m<D, FP8, kPrefillPaged>(a, nz, mask, softcap, s);
-  return launch_m<D, FP8, kPrefillBatch>(a, nz, mask, softcap, s);
+  if (mode == kPrefillVarlen) return launch_m<D, DV, FP8, kPrefillVarlen>(a, nz, mask, softcap, s);
+  if constexpr (D == DV) {
+    if (mode == kPrefillPaged) return launch_m<D, DV, FP8, kPrefillPaged>(a, nz, mask, softcap, s);
+  } else {
+    if (mode == kPrefillPaged) return hipErrorInvalidValue;  // one stride set for both pools: equal dims only
+  }
+  return launch_m<D, DV, FP8, kPrefillBatch>(a, nz, mask, softcap, s);
 }
 
-template <int D>
+template <int D, int DV>
 hipError_t launch_d(const PrefillArgs& a, int in_type, int mode, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (in_type == kInFP8) return launch_f<D, true>(a, mode, nz, mask, softcap, s);
-  return launch_f<D, false>(a, mode, nz, mask, softcap, s);
+  if (in_type == kInFP8) return launch_f<D, DV, true>(a, mode, nz, mask, softcap, s);
+  return launch_f<D, DV, false>(a, mode, nz, mask, softcap, s);
 }
 
 }  // namespace
 
 int prefill_rows_per_tile(int) { return kBlockM; }
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, int in_type, int mode, int nz, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int nz, hipStream_t stream) {
   const bool mask = a.wl >= 0 || a.wr >= 0;
   const bool softcap = a.softcap_pre != 0.0f;
   if (a.n_qtiles <= 0 || nz <= 0 || a.hkv <= 0) return hipSuccess;
-  if (d == 128) return launch_d<128>(a, in_type, mode, nz, mask, softcap, stream);
-  return launch_d<64>(a, in_type, mode, nz, mask, softcap, stream);
+  if (d == 128) {
+    if (dv == 64) return launch_d<128, 64>(a, in_type, mode, nz, mask, softcap, stream);
+    return launch_d<128, 128>(a, in_type, mode, nz, mask, softcap, stream);
+  }
+  if (dv == 128) return launch_d<64, 128>(a, in_type, mode, nz, mask, softcap, stream);
+  return launch_d<64, 64>(a, in_type, mode, nz, mask, softcap, stream);
 }
 
 }  // namespace attn

@@ -243,3 +243,17 @@ def test_cache_batch_idx_and_min_seqlen_q_validation():
 def test_params_init_new_fields():
     p = _params()
     assert p.cache_batch_idx is None and p.cache_batch_count == 0 and p.min_seqlen_q == 0
+
+
+def test_head_dim_v_validation():
+    p = _params(head_dim_v=96)
+    assert _fwd(p) == 2 and "head_dim_v" in _err()
+    p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, head_dim_v=64)
+    assert _fwd(p, d=128) == 2 and "head_dim_v" in _err()
+    p = _params(head_dim_v=64)                               # decode shape (sq=1, ratio 4)
+    assert _paged(p) == 2 and "paged" in _err()
+    st = [32 * 128, 128, 128]
+    kst = [8 * 4096 * 128, 4096 * 128, 128]
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
+                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
+    assert r == 2 and "decode path" in _err()

@@ -1,0 +1,57 @@
+"""GPU parity of hdim_q != hdim_v (V and O with their own head dim, 64 or
+128) on batch-mode prefill and varlen, bf16 and fp8, against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import _cases as C
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dense(B, Hq, Hkv, sq, sk, d, dv, dtype, seed, **kw):
+    c = synth.dense_case(B, Hq, Hkv, sq, sk, d, dtype, seed=seed, device=DEV, **kw)
+    cv = synth.dense_case(B, Hq, Hkv, sq, sk, dv, dtype, seed=seed + 1, device=DEV, **kw)
+    c.t["v"] = cv.t["v"]
+    c.descale["v"] = cv.descale["v"]
+    return c
+
+
+@pytest.mark.parametrize("d,dv,dtype,B,Hq,Hkv,sq,sk,kw", [
+    (128, 64, "bf16", 2, 8, 2, 300, 500, dict(causal=True)),                   # GQA, causal, sq < sk
+    (64, 128, "bf16", 1, 4, 4, 257, 257, dict(window=(100, 0), softcap=30.0)),  # window + soft-cap, ragged tile
+    (128, 64, "fp8", 1, 8, 2, 400, 400, dict(causal=True)),                     # fp8 QK, bf16 PV
+    (64, 128, "fp8", 2, 4, 1, 200, 333, dict(causal=False)),                    # no mask, GQA 4
+])
+def test_prefill_head_dim_v(d, dv, dtype, B, Hq, Hkv, sq, sk, kw):
+    case = _dense(B, Hq, Hkv, sq, sk, d, dv, dtype, seed=sq + d, **kw)
+    out, lse = C.run_dense(case)
+    assert out.shape == (B, Hq, sq, dv)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, dtype, f"head_dim_v d={d} dv={dv} {dtype}")
+
+
+def test_prefill_head_dim_v_sinks_alibi():
+    case = _dense(2, 8, 2, 300, 300, 128, 64, "bf16", 41, window=(64, 0))
+    rng = np.random.default_rng(3)
+    sinks = rng.uniform(-2, 2, size=8)
+    slopes = rng.uniform(0.0, 0.1, size=(2, 8))
+    out, lse = C.run_dense(case, sink_size=4, sink_logits=torch.tensor(sinks, dtype=torch.float32, device=DEV),
+                           alibi_slopes=torch.tensor(slopes, dtype=torch.float32, device=DEV))
+    O, LSE = C.oracle_dense(case, sink_size=4, sink_logits=sinks, alibi_slopes=slopes)
+    C.assert_parity(out, lse, O, LSE, "bf16", "head_dim_v with sinks and ALiBi")
+
+
+@pytest.mark.parametrize("d,dv", [(128, 64), (64, 128)])
+def test_varlen_head_dim_v(d, dv):
+    lens_q, lens_k = [300, 0, 77, 640], [300, 5, 77, 700]
+    c = synth.varlen_case(lens_q, lens_k, 8, 2, d, "bf16", seed=d + 5, device=DEV)
+    cv = synth.varlen_case(lens_q, lens_k, 8, 2, dv, "bf16", seed=d + 6, device=DEV)
+    c.t["v"] = cv.t["v"]
+    out, lse = C.run_varlen(c)
+    assert out.shape[-1] == dv
+    O, LSE = C.oracle_varlen(c)
+    C.assert_parity(out, lse.T, O, LSE.T, "bf16", f"varlen head_dim_v d={d} dv={dv}")

@@ -530,3 +530,28 @@ def test_min_seqlen_q_skips_short_sequences():
                                 v[ck[s]:ck[s + 1], h // 2].tolist(), 0.8, 0.0, -1, 0)
             np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
             np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# hdim_q != hdim_v: V (and O) with their own head dim.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(10))
+def test_value_head_dim_matches_brute_force(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B, Hkv, ratio = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    Hq = Hkv * ratio
+    sq, sk = int(rng.integers(1, 8)), int(rng.integers(1, 9))
+    d, dv = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    q = rng.standard_normal((B, Hq, sq, d))
+    k = rng.standard_normal((B, Hkv, sk, d))
+    v = rng.standard_normal((B, Hkv, sk, dv))
+    wl, wr = int(rng.choice([-1, 1, 3])), int(rng.choice([-1, 0]))
+    o, lse = oracle.attention_batch(q, k, v, 0.6, 0.0, wl, wr)
+    assert o.shape == (B, Hq, sq, dv)
+    for b in range(B):
+        for h in range(Hq):
+            bo, bl = brute_head(q[b, h].tolist(), k[b, h // ratio].tolist(), v[b, h // ratio].tolist(), 0.6, 0.0,
+                                wl, wr, dv=dv)
+            np.testing.assert_allclose(o[b, h], np.array(bo).reshape(sq, dv), atol=1e-12, rtol=0)
+            np.testing.assert_array_equal(np.isneginf(lse[b, h]), np.isneginf(bl))
