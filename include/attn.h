@@ -75,6 +75,13 @@ typedef enum {
   ATTN_BIAS_ALIBI = 2        /* per (batch, q-head) slopes */
 } attn_bias_t;
 
+/* Layout of V (the page's VLayout: row-major [.., seqlen_k, hdim_v] or
+ * column-major [.., hdim_v, seqlen_k]). */
+typedef enum {
+  ATTN_V_ROW_MAJOR = 0,      /* V[b, h, j, c] at b*stride[0] + h*stride[1] + j*stride[2] + c */
+  ATTN_V_COL_MAJOR = 1       /* V[b, h, j, c] at b*stride[0] + h*stride[1] + c*stride[2] + j */
+} attn_v_layout_t;
+
 typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = 1,     /* bad argument: NULL pointer, bad size, stride, alignment */
@@ -134,11 +141,16 @@ typedef struct {
                           64 or 128. A value different from d is supported by attn_fwd on
                           prefill shapes (sq*Hq/Hkv > 16) and by attn_fwd_varlen, BF16 / FP8 only;
                           V's rows then have head_dim_v elements and O's rows too. */
+  int v_layout;        /* attn_v_layout_t. ATTN_V_COL_MAJOR (keys contiguous, v_stride[2] the
+                          stride between head-dim rows) is supported by attn_fwd on prefill
+                          shapes with BF16 inputs and head_dim_v = d; sk must be a multiple of 8
+                          and (head_dim_v - 1) * v_stride[2] * 2 + 128 < 2^31. Keys past
+                          seqused_k may hold any bits: they are never used. */
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
  * descales 1, automatic split size, no sinks, no bias, o_scale 1, no cache
- * batch index, min_seqlen_q 0, head_dim_v 0 (= d). */
+ * batch index, min_seqlen_q 0, head_dim_v 0 (= d), row-major V. */
 void attn_params_init(attn_params_t* p, float scale);
 
 /*

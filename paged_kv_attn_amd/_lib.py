@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
 ATTN_BIAS_NONE, ATTN_BIAS_ELEMENTWISE, ATTN_BIAS_ALIBI = 0, 1, 2
+ATTN_V_ROW_MAJOR, ATTN_V_COL_MAJOR = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_EINVAL", 2: "ATTN_ENOTSUP", 3: "ATTN_EWORKSPACE", 4: "ATTN_ELAUNCH"}
 
 
@@ -38,6 +39,7 @@ class AttnParams(ctypes.Structure):
         ("cache_batch_count", ctypes.c_int),
         ("min_seqlen_q", ctypes.c_int),
         ("head_dim_v", ctypes.c_int),
+        ("v_layout", ctypes.c_int),
     ]
 
 

@@ -105,19 +105,24 @@ def _workspace(nbytes, device, workspace):
 def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seqused_q=None,
              seqused_k=None, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
              kv_split_tokens=0, workspace=None, sink_size=0, sink_logits=None, bias=None, alibi_slopes=None,
-             out_dtype=None, o_scale=1.0, cache_batch_idx=None):
+             out_dtype=None, o_scale=1.0, cache_batch_idx=None, v_colmajor=False):
     """Batch mode. q [B, Hq, sq, d], k [B, Hkv, sk, d], v [B, Hkv, sk, dv] (any strides, d
     contiguous). With ``cache_batch_idx`` (int32 [B] on the device) k / v are
     [C, Hkv, sk, d] caches and batch entry b reads entry cache_batch_idx[b]
-    (an index outside [0, C) reads no keys). Returns (out [B, Hq, sq, dv],
-    lse [B, Hq, sq] or None)."""
+    (an index outside [0, C) reads no keys). With ``v_colmajor`` v is
+    [B, Hkv, dv, sk] with keys contiguous (bf16 prefill shapes, dv = d).
+    Returns (out [B, Hq, sq, dv], lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
-    dv = v.shape[3]
+    dv = v.shape[2] if v_colmajor else v.shape[3]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 bias, alibi_slopes, out_dtype, o_scale)
     if dv != d:
         p.head_dim_v = dv
+    if v_colmajor:
+        if v.shape[3] != sk or v.stride(3) != 1:
+            raise ValueError("column-major v must be [B, Hkv, dv, sk] with unit stride over keys")
+        p.v_layout = _lib.ATTN_V_COL_MAJOR
     if cache_batch_idx is not None:
         if cache_batch_idx.dtype != torch.int32 or cache_batch_idx.numel() < B or not cache_batch_idx.is_contiguous():
             raise TypeError("cache_batch_idx must be a contiguous int32 tensor with B entries")

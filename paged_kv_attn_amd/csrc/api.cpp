@@ -118,6 +118,8 @@ attn_status_t check_params(const attn_params_t* p, int d) {
     return fail(ATTN_ENOTSUP, "head_dim_v %d not supported (0, 64 or 128)", p->head_dim_v);
   if (p->head_dim_v != 0 && p->head_dim_v != d && p->in_dtype == ATTN_F32)
     return fail(ATTN_ENOTSUP, "head_dim_v != d needs bf16 or fp8 inputs");
+  if (p->v_layout != ATTN_V_ROW_MAJOR && p->v_layout != ATTN_V_COL_MAJOR)
+    return fail(ATTN_EINVAL, "unknown v_layout %d", p->v_layout);
   return ATTN_OK;
 }
 
@@ -134,6 +136,8 @@ attn_status_t check_mode_fields(const attn_params_t* p, bool batch_mode, bool va
   }
   if (p->min_seqlen_q != 0 && !varlen_mode)
     return fail(ATTN_EINVAL, "min_seqlen_q applies to attn_fwd_varlen only");
+  if (p->v_layout == ATTN_V_COL_MAJOR && !batch_mode)
+    return fail(ATTN_ENOTSUP, "column-major V is supported by attn_fwd (batch mode) only");
   return ATTN_OK;
 }
 
@@ -207,6 +211,7 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->cache_batch_count = 0;
   p->min_seqlen_q = 0;
   p->head_dim_v = 0;
+  p->v_layout = ATTN_V_ROW_MAJOR;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -242,6 +247,15 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   TRY(check_strides("k", k_stride, 3, eb));
   TRY(check_strides("v", v_stride, 3, eb));
   TRY(check_strides("o", o_stride, 3, ob));
+  if (p->v_layout == ATTN_V_COL_MAJOR) {
+    if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "column-major V needs bf16 inputs");
+    if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "column-major V needs head_dim_v = d");
+    if (takes_decode_path(p->in_dtype, sq, Hq / Hkv))
+      return fail(ATTN_ENOTSUP, "column-major V is not supported on the decode path (sq*Hq/Hkv <= 16)");
+    if (sk % 8) return fail(ATTN_EINVAL, "column-major V needs sk a multiple of 8 (got %d)", sk);
+    if ((int64_t)(d - 1) * v_stride[2] * 2 + 128 >= ((int64_t)1 << 31))
+      return fail(ATTN_EINVAL, "column-major V: head-dim row stride too large");
+  }
   if (B == 0 || sq == 0) return ATTN_OK;
   const int ratio = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
@@ -312,6 +326,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
   a.seqused_q = seqused_q; a.seqused_k = seqused_k;
   a.cache_idx = p->cache_batch_idx; a.cache_count = p->cache_batch_count;
+  a.v_colmajor = p->v_layout == ATTN_V_COL_MAJOR;
   a.sq = sq; a.sk = sk; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
   const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
   a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);

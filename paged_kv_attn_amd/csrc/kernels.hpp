@@ -54,6 +54,7 @@ struct PrefillArgs {
   const int32_t* cache_idx;   // batch mode, nullable: K/V batch entry of each batch entry
   int cache_count;            // K/V batch entries (indices outside [0, cache_count) read no keys)
   int min_seqlen_q;           // varlen mode: sequences with Lq <= min_seqlen_q are skipped
+  int v_colmajor;             // batch mode, bf16, equal head dims: V keys contiguous, v_sr = head-dim row stride
 };
 
 // Split-KV decode (one workgroup = one split of one request and kv-head).

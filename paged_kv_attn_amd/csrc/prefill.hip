@@ -75,6 +75,18 @@ __device__ __forceinline__ int swz(int row, int nchunks) {
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
+// Column-major V (keys contiguous in memory): the V^T tile sits in LDS as DV
+// rows of 64 keys (128 B), 16-byte chunk c of row R in slot c ^ vt_swz(R), so
+// the 32 rows x 2 chunks that one operand read touches fall in distinct banks.
+__device__ __forceinline__ int vt_swz(int row) { return (row >> 1) & 7; }
+// With column-major V the K tile's rows are loaded permuted within each 16-key
+// block (rows 4-7 <-> 8-11), so that the 8 P values a lane feeds to one PV
+// product belong to 8 consecutive keys, i.e. one 16-byte chunk of a V^T row.
+__device__ __forceinline__ int k_row_perm(int r) {
+  const int y = r & 15;
+  return (r & ~15) | ((y >= 4 && y < 12) ? (y ^ 12) : y);
+}
+
 // Workgroups resident on one XCD at a time: 32 CUs, two workgroups each.
 constexpr int kSlotsPerXcd = 64;
 // Units (sequence, kv-head) per dispatch group: as many as one group's query
@@ -87,8 +99,9 @@ template <bool FP8> struct QFrag;
 template <> struct QFrag<false> { using T = U128; };
 template <> struct QFrag<true> { using T = U64; };
 
-template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
+template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+  static_assert(!VT || (!FP8 && D == DV), "column-major V: bf16 with equal head dims");
   using Tr = Traits<D, DV, FP8>;
   using QT = typename QFrag<FP8>::T;
   // Separate LDS objects per slot: the compiler can then prove that reads of
@@ -241,13 +254,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   for (int i = 0; i < Tr::kKInstr; ++i) {
     const int B = 1024 * (wave + 4 * i) + 16 * lane;
     const int R = B / Tr::kKRow, sl = (B % Tr::kKRow) / 16;
-    koff[i] = (int)(R * krow) + 16 * (sl ^ swz(R, Tr::kKCh));
+    koff[i] = (int)((VT ? k_row_perm(R) : R) * krow) + 16 * (sl ^ swz(R, Tr::kKCh));
   }
 #pragma unroll
   for (int i = 0; i < Tr::kVInstr; ++i) {
     const int B = 1024 * (wave + 4 * i) + 16 * lane;
     const int R = B / Tr::kVRow, sl = (B % Tr::kVRow) / 16;
     voff[i] = (int)(R * vrow) + 16 * (sl ^ swz(R, Tr::kVCh));
+  }
+  // column-major V: lane l of block q fetches row R = 8 q + l / 8 (a head-dim
+  // index), global chunk kc = (l % 8) ^ vt_swz(R) (keys 8 kc .. 8 kc + 7 of the tile)
+  int vt_kc[VT ? Tr::kVInstr : 1];
+#pragma unroll
+  for (int i = 0; i < (VT ? Tr::kVInstr : 0); ++i) {
+    const int R = 8 * (wave + 4 * i) + (lane >> 3);
+    vt_kc[i] = (lane & 7) ^ vt_swz(R);
+    voff[i] = (int)(R * vrow) + 16 * vt_kc[i];
   }
   auto load_k = [&](int t, int slot) {
     const int j0 = t * kBlockN;
@@ -261,6 +283,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int v8ch = threadIdx.x % Tr::kV8Ch, v8row = threadIdx.x / Tr::kV8Ch;
   auto load_v = [&](int t, int slot) {
     const int j0 = t * kBlockN;
+    if (VT) {
+      // rows are head-dim indices (row stride vrow); chunks of keys at or past Lk
+      // get an offset beyond the range and arrive as zeros
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + 2 * j0, (uint32_t)((DV - 1) * vrow + 2 * kBlockN));
+      lds_char* base = vslot(slot);
+#pragma unroll
+      for (int i = 0; i < Tr::kVInstr; ++i)
+        buf_load16_lds(r, base + 1024 * (wave + 4 * i), j0 + 8 * vt_kc[i] < Lk ? voff[i] : 0x7FFFFFF0);
+      return;
+    }
     const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(vh, a.v_sb, vrow, j0), (uint32_t)(min(kBlockN, Lk - j0) * vrow));
     if (FP8) {
 #pragma unroll
@@ -342,6 +374,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // Softmax of tile t's scores (s0, s1) into bf16 P, with the lazy rescale of O.
   // Register r of block b is key j0 + 32b + 8(r/4) + 4h + r%4 of this lane's row.
+  // Score register r of block b in lane half h is key j0 + kHStep h + key_rel(b, r)
+  // (the S^T row of the register, through the K row permutation with column-major V).
+  constexpr int kHStep = VT ? 8 : 4;
+  auto key_rel = [](int b, int r) -> int {
+    return VT ? 32 * b + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3) : 32 * b + 8 * (r >> 2) + (r & 3);
+  };
   auto softmax = [&](auto masked_tag, int t, f32x16 s0, f32x16 s1, uint32_t (&pk)[2][8]) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     const int j0 = t * kBlockN;
@@ -355,12 +393,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // additive bias (after the soft-cap, before the mask); register r of block b
     // is key j0 + 4h + 32b + 8(r/4) + r%4
     if (BIAS == kBiasAlibi) {
-      const float dbase = (float)(pos + off - j0 - 4 * h);  // distance to key j0 + 4h
+      const float dbase = (float)(pos + off - j0 - kHStep * h);  // distance to key j0 + kHStep h
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float jr = (float)(32 * b + 8 * (r >> 2) + (r & 3));
+          const float jr = (float)key_rel(b, r);
           s[b][r] = __builtin_fmaf(-alibi_k, __builtin_fabsf(dbase - jr), s[b][r]);
         }
     }
@@ -372,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int b = 0; b < 2; ++b) {
         U128 bv[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) bv[g4] = buf_load16(br, bias_lane + 4 * (j0 + 4 * h + 32 * b + 8 * g4));
+        for (int g4 = 0; g4 < 4; ++g4) bv[g4] = buf_load16(br, bias_lane + 4 * (j0 + kHStep * h + key_rel(b, 4 * g4)));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t w = (&bv[r >> 2].x)[r & 3];
@@ -381,15 +419,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
     if (kMasked) {
-      const int hi = lim_hi - j0 - 4 * h;
-      const int lo = lim_lo - j0 - 4 * h;
-      const int sk = a.sink_size - j0 - 4 * h;  // sink keys ignore the left bound
+      const int hi = lim_hi - j0 - kHStep * h;
+      const int lo = lim_lo - j0 - kHStep * h;
+      const int sk = a.sink_size - j0 - kHStep * h;  // sink keys ignore the left bound
       const bool two_sided = MASK && a.wl >= 0;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int jr = 32 * b + 8 * (r >> 2) + (r & 3);
+          const int jr = key_rel(b, r);
           const bool vis = (jr <= hi) && (!two_sided || jr >= lo || jr < sk);
           s[b][r] = vis ? s[b][r] : kNegInf;
         }
@@ -452,9 +490,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int kb = 32 * b + 16 * gm;
 #pragma unroll
         for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
-          const U64 v0 = lds_read_tr16(vt + v_addr(kb, 0, dblk));
-          const U64 v1 = lds_read_tr16(vt + v_addr(kb, 1, dblk));
-          acc[dblk] = mfma32_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
+          if (VT) {  // keys kb + 8h .. +7 of head-dim row 32 dblk + lane % 32: one chunk
+            const int R = 32 * dblk + (lane & 31);
+            const U128 vv = lds_load16(vt + R * (2 * kBlockN) + 16 * (((kb >> 3) + h) ^ vt_swz(R)));
+            acc[dblk] = mfma32_bf16(as_bf16x8(vv), pb, acc[dblk]);
+          } else {
+            const U64 v0 = lds_read_tr16(vt + v_addr(kb, 0, dblk));
+            const U64 v1 = lds_read_tr16(vt + v_addr(kb, 1, dblk));
+            acc[dblk] = mfma32_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
+          }
         }
       }
     }
@@ -495,6 +539,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     auto step = [&](auto parity_tag, int t) {
       constexpr int P = decltype(parity_tag)::value ? 1 : 0;
       const bool has1 = t + 1 < t_end;
+      if (VT && !has1) {
+        // the chunk holding key Lk - 1 also brought keys Lk .. (past the used
+        // length, possibly not finite): zero them before any product reads them
+        const int rem = Lk - t * kBlockN;
+        if (rem > 0 && rem < kBlockN && (rem & 7)) {
+          if ((int)threadIdx.x < DV) {
+            const int R = threadIdx.x;
+            lds_char* row = vslot(P) + R * (2 * kBlockN) + 16 * ((rem >> 3) ^ vt_swz(R));
+            for (int e = rem & 7; e < 8; ++e) *(__attribute__((address_space(3))) uint16_t*)(row + 2 * e) = 0;
+          }
+          __syncthreads();
+        }
+      }
       if (has1) {
         load_k(t + 1, 1 - P);
         load_v(t + 1, 1 - P);
@@ -566,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS>
+template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
@@ -574,24 +631,34 @@ hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   const int64_t units_x = (n_units + kXcds - 1) / kXcds;   // units per XCD
   const int64_t G = group_units(a.n_qtiles);
   const int64_t grid = kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MASK, SOFTCAP, BIAS>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MASK, SOFTCAP, BIAS, VT>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, b);
   return hipGetLastError();
 }
 
-template <int D, int DV, bool FP8, int MODE, int BIAS>
+template <int D, int DV, bool FP8, int MODE, int BIAS, bool VT>
 hipError_t launch_b(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
   if (mask)
-    return softcap ? launch_t<D, DV, FP8, MODE, true, true, BIAS>(a, nz, s) : launch_t<D, DV, FP8, MODE, true, false, BIAS>(a, nz, s);
-  return softcap ? launch_t<D, DV, FP8, MODE, false, true, BIAS>(a, nz, s) : launch_t<D, DV, FP8, MODE, false, false, BIAS>(a, nz, s);
+    return softcap ? launch_t<D, DV, FP8, MODE, true, true, BIAS, VT>(a, nz, s) : launch_t<D, DV, FP8, MODE, true, false, BIAS, VT>(a, nz, s);
+  return softcap ? launch_t<D, DV, FP8, MODE, false, true, BIAS, VT>(a, nz, s) : launch_t<D, DV, FP8, MODE, false, false, BIAS, VT>(a, nz, s);
+}
+
+template <int D, int DV, bool FP8, int MODE, bool VT>
+hipError_t launch_v(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
+  if (a.bias_type == kBiasAlibi) return launch_b<D, DV, FP8, MODE, kBiasAlibi, VT>(a, nz, mask, softcap, s);
+  if (MODE == kPrefillBatch && a.bias_type == kBiasElem)
+    return launch_b<D, DV, FP8, MODE, (MODE == kPrefillBatch ? kBiasElem : kBiasNone), VT>(a, nz, mask, softcap, s);
+  return launch_b<D, DV, FP8, MODE, kBiasNone, VT>(a, nz, mask, softcap, s);
 }
 
 template <int D, int DV, bool FP8, int MODE>
 hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (a.bias_type == kBiasAlibi) return launch_b<D, DV, FP8, MODE, kBiasAlibi>(a, nz, mask, softcap, s);
-  if (MODE == kPrefillBatch && a.bias_type == kBiasElem)
-    return launch_b<D, DV, FP8, MODE, (MODE == kPrefillBatch ? kBiasElem : kBiasNone)>(a, nz, mask, softcap, s);
-  return launch_b<D, DV, FP8, MODE, kBiasNone>(a, nz, mask, softcap, s);
+  if constexpr (MODE == kPrefillBatch && !FP8 && D == DV) {
+    if (a.v_colmajor) return launch_v<D, DV, FP8, MODE, true>(a, nz, mask, softcap, s);
+  } else {
+    if (a.v_colmajor) return hipErrorInvalidValue;  // batch-mode bf16 with equal head dims only
+  }
+  return launch_v<D, DV, FP8, MODE, false>(a, nz, mask, softcap, s);
 }
 
 template <int D, int DV, bool FP8>

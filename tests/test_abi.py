@@ -257,3 +257,21 @@ def test_head_dim_v_validation():
     r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
                        i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
     assert r == 2 and "decode path" in _err()
+
+
+def test_v_layout_validation():
+    p = _params(v_layout=5)
+    assert _fwd(p) == 1 and "v_layout" in _err()
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)
+    assert _fwd(p, sk=60) == 1 and "multiple of 8" in _err()
+    assert _paged(p) == 2 and "batch mode" in _err()
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, in_dtype=_lib.ATTN_FP8_E4M3, out_dtype=_lib.ATTN_BF16)
+    assert _fwd(p) == 2 and "bf16" in _err()
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, head_dim_v=64)
+    assert _fwd(p) == 2 and "head_dim_v" in _err()
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)
+    st = [32 * 128, 128, 128]
+    kst = [8 * 4096 * 128, 4096 * 128, 128]
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
+                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
+    assert r == 2 and "decode path" in _err()
