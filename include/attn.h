@@ -220,6 +220,36 @@ attn_status_t attn_fwd_paged(const attn_params_t* p,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Group (varlen) mode over a paged KV cache, with optional per-sequence key
+ * offsets ("gappy" group mode of the Composable Kernel page: with is_gappy,
+ * seqstart_k[b] is the logical position of the sequence's first key in its
+ * page list, kv_l2p_offset, and seqlen_k_ptr[b] its key count).
+ * Q [total_q, Hq, d] and O [total_q, Hq, d] as in attn_fwd_varlen, sequence s
+ * owning query tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1; lse (nullable)
+ * fp32 [Hq, total_q]. The pools are addressed as in attn_fwd_paged. Sequence s
+ * has Lk = seqlens_k[s] keys; key j is token kv_start[s] + j of block table row
+ * s (kv_start NULL: 0), i.e. slot (kv_start[s] + j) % page_size of page
+ * block_table[s*block_table_stride + (kv_start[s] + j) / page_size];
+ * kv_start[s] + Lk <= block_table_stride * page_size. Bottom-right aligned mask
+ * per sequence. page_size must be a multiple of 64 and every kv_start[s] a
+ * multiple of 64 (each 64-key tile then lies in one page); a sequence whose
+ * kv_start is negative or not a multiple of 64 is not computed: its O and LSE
+ * rows are set to NaN and no key of it is read. BF16 or FP8_E4M3 inputs, the
+ * prefill kernel for every query length; no workspace. Not supported with
+ * cache_batch_idx, column-major V or head_dim_v != d.
+ */
+attn_status_t attn_fwd_varlen_paged(const attn_params_t* p,
+                                    const void* q, const void* k_pool, const void* v_pool,
+                                    void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                    const int32_t* kv_start,
+                                    const int32_t* block_table, int block_table_stride,
+                                    int n, int total_q, int max_seqlen_q,
+                                    int Hq, int Hkv, int d, int page_size, int num_pages,
+                                    const int64_t q_stride[2], const int64_t kv_stride[3],
+                                    const int64_t o_stride[2], void* stream);
+
+/*
  * Workspace bytes needed by attn_fwd / attn_fwd_paged for this shape (0 when
  * the shape takes the prefill path). max_seqlen_k is sk for attn_fwd and
  * block_table_stride * page_size for attn_fwd_paged. Returns 0 for invalid

@@ -23,6 +23,7 @@ from .attention import (  # noqa: F401
     attention_batch,
     attention_paged,
     attention_varlen,
+    attention_varlen_paged,
     bf16_bits_to_f64,
     e4m3fn_bits_to_f64,
     e4m3fn_value,

@@ -280,17 +280,18 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
     return o, lse
 
 
-def gather_paged(pool, block_table_row, seqlen):
+def gather_paged(pool, block_table_row, seqlen, start=0):
     """Contiguous [Hkv, L, d] copy of one request's keys (or values).
 
     pool is [num_pages, page_size, Hkv, d]; token t lives in physical page
     block_table_row[t // page_size] at slot t % page_size (the page-block
     navigator of the Composable Kernel page: one block-table row per batch,
-    ``page_block_size`` tokens per page).
+    ``page_block_size`` tokens per page). Key j is token ``start + j`` (the
+    page's ``kv_l2p_offset`` of gappy group mode; 0 otherwise).
     """
     pool = np.asarray(pool)
     page_size = pool.shape[1]
-    t = np.arange(int(seqlen))
+    t = int(start) + np.arange(int(seqlen))
     pages = np.asarray(block_table_row)[t // page_size]
     rows = pool[pages, t % page_size]          # [L, Hkv, d]
     return rows.transpose(1, 0, 2)
@@ -331,3 +332,32 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
         o[b] = ob[0]
         lse[b] = lb[0]
     return o, lse
+
+
+def attention_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, scale, softcap=0.0,
+                           window_left=-1, window_right=-1, kv_start=None, workers=1, decode=None, sink_size=0,
+                           sink_logits=None, alibi_slopes=None, min_seqlen_q=0):
+    """Group mode over a paged KV cache (the group-mode page-block navigator of
+    the Composable Kernel page, with ``is_gappy``: ``seqstart_k[b]`` then holds
+    the logical position ``kv_l2p_offset`` of sequence b's first key in its page
+    list). q [Tq, Hq, d] packed by cu_seqlens_q; sequence s reads seqlens_k[s]
+    keys starting at token kv_start[s] (None: 0) of block table row s. Each
+    sequence's keys are gathered into a contiguous copy and the varlen
+    definition applied. Returns O [Tq, Hq, dv] and LSE [Hq, Tq]."""
+    n = len(cu_seqlens_q) - 1
+    dec_k, dec_v = (decode, decode) if not isinstance(decode, tuple) else decode
+    ks, vs, ck = [], [], [0]
+    for s in range(n):
+        st = 0 if kv_start is None else int(kv_start[s])
+        kk = gather_paged(k_pool, block_table[s], seqlens_k[s], st)   # [Hkv, L, d]
+        vv = gather_paged(v_pool, block_table[s], seqlens_k[s], st)
+        if dec_k is not None:
+            kk, vv = dec_k(kk), dec_v(vv)
+        ks.append(np.asarray(kk, dtype=np.float64).transpose(1, 0, 2))
+        vs.append(np.asarray(vv, dtype=np.float64).transpose(1, 0, 2))
+        ck.append(ck[-1] + int(seqlens_k[s]))
+    k = np.concatenate(ks, 0) if ks else np.zeros((0,) + np.asarray(k_pool).shape[2:])
+    v = np.concatenate(vs, 0) if vs else np.zeros((0,) + np.asarray(v_pool).shape[2:])
+    return attention_varlen(q, k, v, cu_seqlens_q, np.array(ck), scale, softcap, window_left, window_right,
+                            workers=workers, sink_size=sink_size, sink_logits=sink_logits,
+                            alibi_slopes=alibi_slopes, min_seqlen_q=min_seqlen_q)

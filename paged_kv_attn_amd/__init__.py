@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     attn_fwd,
     attn_fwd_paged,
     attn_fwd_varlen,
+    attn_fwd_varlen_paged,
     attn_last_error,
     attn_num_splits,
     attn_params,

@@ -202,3 +202,38 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
                                B, sq, Hq, Hkv, d, page_size, num_pages, st(q), kv_stride, st(out),
                                _ptr(ws), ws_bytes, _stream(q)))
     return out, lse
+
+
+def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q, *, kv_start=None,
+                          scale=None, causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None,
+                          lse=None, return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None,
+                          out_dtype=None, o_scale=1.0, min_seqlen_q=0):
+    """Varlen queries over a paged KV cache. q [Tq, Hq, d] with cu_seqlens_q
+    int32 [n+1]; pools [num_pages, page_size, Hkv, d] (equal strides);
+    block_table int32 [n, W]; seqlens_k int32 [n]; kv_start (int32 [n] or
+    None): logical position of each sequence's first key in its page list, a
+    multiple of 64 (else that sequence's rows come back NaN). Returns
+    (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
+    Tq, Hq, d = q.shape
+    num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same strides")
+    for name, t in (("block_table", block_table), ("seqlens_k", seqlens_k), ("cu_seqlens_q", cu_seqlens_q),
+                    ("kv_start", kv_start)):
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    n = cu_seqlens_q.numel() - 1
+    p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
+                alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
+    p.min_seqlen_q = int(min_seqlen_q)
+    if out is None:
+        out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    kv_stride = i64_array([k_pool.stride(0), k_pool.stride(2), k_pool.stride(1)])
+    st = lambda t: i64_array(t.stride()[:2])  # noqa: E731
+    check(lib().attn_fwd_varlen_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
+                                      _ptr(cu_seqlens_q), _ptr(seqlens_k), _ptr(kv_start), _ptr(block_table),
+                                      int(block_table.stride(0)), n, Tq, int(max_seqlen_q), Hq, Hkv, d, page_size,
+                                      num_pages, st(q), kv_stride, st(out), _stream(q)))
+    return out, lse

@@ -494,4 +494,63 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   return launched(attn::launch_decode(a, c, d, true, B, (hipStream_t)stream));
 }
 
+attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const void* k_pool, const void* v_pool,
+                                    void* o, float* lse, const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                    const int32_t* kv_start, const int32_t* block_table, int block_table_stride,
+                                    int n, int total_q, int max_seqlen_q, int Hq, int Hkv, int d, int page_size,
+                                    int num_pages, const int64_t q_stride[2], const int64_t kv_stride[3],
+                                    const int64_t o_stride[2], void* stream) {
+  TRY(check_params(p, d));
+  TRY(check_mode_fields(p, false, true));
+  if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "head_dim_v != d is not supported in paged mode (one stride set for both pools)");
+  if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "paged KV supports bf16 and fp8 inputs");
+  if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
+    return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
+  if (n < 0 || total_q < 0 || max_seqlen_q < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
+    return fail(ATTN_EINVAL, "bad sizes n=%d total_q=%d max_q=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", n,
+                total_q, max_seqlen_q, Hq, Hkv, block_table_stride, num_pages);
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  if (page_size <= 0 || page_size % 64)
+    return fail(ATTN_ENOTSUP, "page_size %d is not a positive multiple of 64", page_size);
+  if (!cu_seqlens_q || !seqlens_k || !block_table)
+    return fail(ATTN_EINVAL, "cu_seqlens_q / seqlens_k / block_table is NULL");
+  if (kv_start && ((uintptr_t)kv_start & 3u)) return fail(ATTN_EINVAL, "kv_start is not 4-byte aligned");
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("k_pool", k_pool));
+  TRY(check_ptr("v_pool", v_pool));
+  TRY(check_ptr("o", o));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
+  const int eb = elem_bytes(p->in_dtype);
+  TRY(check_strides("q", q_stride, 2, eb));
+  TRY(check_strides("kv", kv_stride, 3, eb));
+  TRY(check_strides("o", o_stride, 2, elem_bytes(p->out_dtype)));
+  if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
+  const int64_t max_len64 = (int64_t)block_table_stride * page_size;
+  if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
+  float c_exp2, pre, post;
+  logit_consts(p, &c_exp2, &pre, &post);
+  const int ratio = Hq / Hkv;
+  attn::PrefillArgs a{};
+  a.q = q; a.k = k_pool; a.v = v_pool; a.o = o; a.lse = lse;
+  a.q_sb = 0; a.q_sh = q_stride[1]; a.q_sr = q_stride[0];
+  a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
+  a.v_sb = kv_stride[0]; a.v_sh = kv_stride[1]; a.v_sr = kv_stride[2];
+  a.o_sb = 0; a.o_sh = o_stride[1]; a.o_sr = o_stride[0];
+  a.lse_sb = 0; a.lse_sh = total_q;
+  a.cu_q = cu_seqlens_q; a.cu_k = nullptr;
+  a.seqused_q = nullptr; a.seqused_k = seqlens_k; a.kv_start = kv_start;
+  a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
+  a.min_seqlen_q = p->min_seqlen_q;
+  a.sq = 0; a.sk = (int)max_len64; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
+  const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
+  a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + rows_tile - 1) / rows_tile);
+  a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
+  a.o_mul = out_mul(p);
+  a.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
+  a.wl = p->window_left; a.wr = p->window_right;
+  a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
+  set_bias(p, c_exp2, &a);
+  return launched(attn::launch_prefill(a, d, d, p->in_dtype, attn::kPrefillVarlenPaged, n, (hipStream_t)stream));
+}
+
 }  // extern "C"

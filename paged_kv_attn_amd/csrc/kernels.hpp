@@ -10,7 +10,7 @@ namespace attn {
 enum InType : int { kInF32 = 0, kInBF16 = 1, kInFP8 = 2 };
 // prefill addressing modes: batch [B, H, S, d]; varlen (cu_seqlens); paged
 // (K/V rows through a block table, Lq = sq, Lk = seqlens_k)
-enum PrefillMode : int { kPrefillBatch = 0, kPrefillVarlen = 1, kPrefillPaged = 2 };
+enum PrefillMode : int { kPrefillBatch = 0, kPrefillVarlen = 1, kPrefillPaged = 2, kPrefillVarlenPaged = 3 };
 // logit bias kinds (the values of attn_bias_t)
 enum BiasKind : int { kBiasNone = 0, kBiasElem = 1, kBiasAlibi = 2 };
 
@@ -55,6 +55,7 @@ struct PrefillArgs {
   int cache_count;            // K/V batch entries (indices outside [0, cache_count) read no keys)
   int min_seqlen_q;           // varlen mode: sequences with Lq <= min_seqlen_q are skipped
   int v_colmajor;             // batch mode, bf16, equal head dims: V keys contiguous, v_sr = head-dim row stride
+  const int32_t* kv_start;    // varlen-paged mode, nullable: logical position of each sequence's first key
 };
 
 // Split-KV decode (one workgroup = one split of one request and kv-head).

@@ -143,9 +143,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // ---- sequence geometry (batch: seqused; varlen: cumulative offsets; paged:
   // Lq = sq, Lk = seqlens_k, K/V rows found through the block table) ----
   constexpr bool VARLEN = MODE == kPrefillVarlen;
-  constexpr bool PAGED = MODE == kPrefillPaged;
+  constexpr bool VPAGED = MODE == kPrefillVarlenPaged;        // varlen queries over a paged pool
+  constexpr bool PAGED = MODE == kPrefillPaged || VPAGED;     // K/V rows through the block table
   int Lq, Lk;
   int64_t q_off, k_off, v_off, o_off, lse_off;
+  int kv0 = 0;       // logical position of key 0 in the sequence's page list
+  bool bad = false;  // varlen-paged: a start that is not tile-aligned -> NaN rows, nothing read
   if (VARLEN) {
     const int q0 = a.cu_q[z], k0 = a.cu_k[z];
     Lq = a.cu_q[z + 1] - q0;
@@ -154,6 +157,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     q_off = (int64_t)q0 * a.q_sr;
     k_off = (int64_t)k0 * a.k_sr;
     v_off = (int64_t)k0 * a.v_sr;
+    o_off = (int64_t)q0 * a.o_sr;
+    lse_off = q0;
+  } else if (VPAGED) {
+    const int q0 = a.cu_q[z];
+    Lq = a.cu_q[z + 1] - q0;
+    Lk = a.seqused_k[z];
+    if (Lq <= a.min_seqlen_q) return;  // skipped sequence: its rows stay untouched
+    kv0 = a.kv_start ? a.kv_start[z] : 0;
+    if (kv0 < 0 || (kv0 & (kBlockN - 1))) {
+      bad = true;
+      kv0 = 0;
+      Lk = 0;
+    }
+    q_off = (int64_t)q0 * a.q_sr;
+    k_off = 0;  // pool base; pages are found per tile
+    v_off = 0;
     o_off = (int64_t)q0 * a.o_sr;
     lse_off = q0;
   } else if (PAGED) {
@@ -233,8 +252,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // in-page offset, as in the page-block navigator of the Composable Kernel page
   auto tile_rows = [&](const char* head_base, int64_t page_stride, int64_t row_bytes, int j0) -> const char* {
     if (PAGED) {
-      const int page = a.block_table[(int64_t)z * a.bt_stride + j0 / a.page_size];
-      return head_base + (int64_t)page * page_stride * Tr::kElem + (int64_t)(j0 % a.page_size) * row_bytes;
+      const int jl = kv0 + j0;  // logical token position in the page list
+      const int page = a.block_table[(int64_t)z * a.bt_stride + jl / a.page_size];
+      return head_base + (int64_t)page * page_stride * Tr::kElem + (int64_t)(jl % a.page_size) * row_bytes;
     }
     return head_base + j0 * row_bytes;
   };
@@ -609,7 +629,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int d = 32 * dblk + 8 * q4 + 4 * h;
         const float o0 = acc[dblk][4 * q4 + 0] * inv, o1 = acc[dblk][4 * q4 + 1] * inv;
         const float o2 = acc[dblk][4 * q4 + 2] * inv, o3 = acc[dblk][4 * q4 + 3] * inv;
-        if (a.out_fp8) {
+        if (VPAGED && bad) {  // NaN bit patterns (E4M3FN 0x7F, bf16 0x7FC0)
+          if (a.out_fp8) *(uint32_t*)(op + d) = 0x7F7F7F7Fu;
+          else *(U64*)(op + d * 2) = U64{0x7FC07FC0u, 0x7FC07FC0u};
+        } else if (a.out_fp8) {
           *(uint32_t*)(op + d) = pack_fp8x4_sat(o0, o1, o2, o3);
         } else {
           U64 w;
@@ -619,6 +642,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
+    if (VPAGED && bad) lse2 = __builtin_nanf("");
     if (a.lse && h == 0) a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] = lse2 * kLn2;
   }
 }
@@ -666,8 +690,10 @@ hipError_t launch_f(const PrefillArgs& a, int mode, int nz, bool mask, bool soft
   if (mode == kPrefillVarlen) return launch_m<D, DV, FP8, kPrefillVarlen>(a, nz, mask, softcap, s);
   if constexpr (D == DV) {
     if (mode == kPrefillPaged) return launch_m<D, DV, FP8, kPrefillPaged>(a, nz, mask, softcap, s);
+    if (mode == kPrefillVarlenPaged) return launch_m<D, DV, FP8, kPrefillVarlenPaged>(a, nz, mask, softcap, s);
   } else {
-    if (mode == kPrefillPaged) return hipErrorInvalidValue;  // one stride set for both pools: equal dims only
+    if (mode == kPrefillPaged || mode == kPrefillVarlenPaged)
+      return hipErrorInvalidValue;  // one stride set for both pools: equal dims only
   }
   return launch_m<D, DV, FP8, kPrefillBatch>(a, nz, mask, softcap, s);
 }

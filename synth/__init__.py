@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     dense_case,
     paged_case,
     varlen_case,
+    varlen_paged_case,
     workload,
     WORKLOADS,
 )

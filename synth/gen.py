@@ -178,6 +178,60 @@ def paged_case(lens_k, sq, Hq, Hkv, d, page_size=128, dtype="bf16", seed=0, caus
                      lens_k=lens_k, table_width=W, seed=seed))
 
 
+def varlen_paged_case(lens_q, lens_k, starts, Hq, Hkv, d, page_size=64, dtype="bf16", seed=0, causal=True,
+                      softcap=0.0, window=None, scale=None, device="cpu") -> Case:
+    """Group mode over a paged pool: Q [Tq, Hq, d] packed by cu_seqlens_q;
+    sequence s reads lens_k[s] keys starting at logical token starts[s] of its
+    block-table row (kv_start). Request s owns ceil((starts[s] + lens_k[s]) / P)
+    pages dealt from a seeded permutation; every slot outside
+    [starts[s], starts[s] + lens_k[s]) and a guard page (the last id, filling
+    unused table entries) are NaN (bf16 only)."""
+    lens_q = [int(x) for x in lens_q]
+    lens_k = [int(x) for x in lens_k]
+    starts = [int(x) for x in starts]
+    n = len(lens_q)
+    P = page_size
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_pages = [max(1, -(-(st + L) // P)) for st, L in zip(starts, lens_k)]
+    W = max(n_pages) if n_pages else 1
+    n_real = sum(n_pages)
+    N = n_real + 1
+    guard = N - 1
+    ids = rng.permutation(n_real)
+    table = np.full((n, W), guard, dtype=np.int32)
+    off = 0
+    for r, m in enumerate(n_pages):
+        table[r, :m] = ids[off:off + m]
+        off += m
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    g = _torch_gen(seed, device)
+    q, dq = to_stored(normal((int(cu_q[-1]), Hq, d), g, device), dtype)
+    kp, dk = _pool(N, P, Hkv, d, g, device, dtype)
+    vp, dv = _pool(N, P, Hkv, d, g, device, dtype)
+    if dtype != "fp8":
+        kp[guard] = float("nan")
+        vp[guard] = float("nan")
+        for r in range(n):
+            for t0 in range(0, n_pages[r] * P, P):   # page by page, slots outside the used range
+                page = int(table[r, t0 // P])
+                lo = min(P, max(0, starts[r] - t0))
+                hi = min(P, max(0, starts[r] + lens_k[r] - t0))
+                for a_, b_ in ((0, lo), (max(lo, hi), P)):
+                    if b_ > a_:
+                        kp[page, a_:b_] = float("nan")
+                        vp[page, a_:b_] = float("nan")
+    t = {"q": q, "k_pool": kp, "v_pool": vp,
+         "block_table": torch.from_numpy(table).to(device),
+         "seqlens_k": torch.tensor(lens_k, dtype=torch.int32, device=device),
+         "kv_start": torch.tensor(starts, dtype=torch.int32, device=device),
+         "cu_seqlens_q": torch.from_numpy(cu_q).to(device)}
+    wl, wr = _mask_args(causal, window)
+    return Case("varlen_paged", dtype, t, {"q": dq, "k": dk, "v": dv},
+                scale if scale is not None else 1.0 / math.sqrt(d), softcap, wl, wr,
+                dict(n=n, Hq=Hq, Hkv=Hkv, d=d, page_size=P, num_pages=N, lens_q=lens_q, lens_k=lens_k,
+                     starts=starts, table_width=W, max_q=max(lens_q) if lens_q else 0, seed=seed))
+
+
 def _pool(N, P, Hkv, d, g, device, dtype):
     """One page pool, drawn page-chunk by page-chunk to bound temporaries."""
     out_dtype = {"f32": torch.float32, "bf16": torch.bfloat16}.get(dtype)

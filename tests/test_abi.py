@@ -275,3 +275,22 @@ def test_v_layout_validation():
     r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
                        i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
     assert r == 2 and "decode path" in _err()
+
+
+def _vpaged(p, page=64, kv_start=NULL, table=FAKE, d=128):
+    st = [2 * 128, 128]
+    kv = [page * 2 * 128, 128, 2 * 128]
+    return lib().attn_fwd_varlen_paged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, kv_start, table,
+                                       4, 2, 10, 8, 2, 2, d, page, 16, i64_array(st), i64_array(kv), i64_array(st),
+                                       NULL)
+
+
+def test_varlen_paged_rejects_bad_arguments():
+    p = _params()
+    assert _vpaged(p, page=32) == 2 and "multiple of 64" in _err()
+    assert _vpaged(p, kv_start=ctypes.c_void_p(0x10002)) == 1 and "kv_start" in _err()
+    assert _vpaged(p, table=NULL) == 1 and "block_table" in _err()
+    assert _vpaged(_params(cache_batch_idx=0x10000, cache_batch_count=1)) == 1 and "batch mode" in _err()
+    assert _vpaged(_params(head_dim_v=64)) == 2 and "head_dim_v" in _err()
+    assert _vpaged(_params(v_layout=_lib.ATTN_V_COL_MAJOR)) == 2 and "column-major" in _err()
+    assert _vpaged(_params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)) == 2

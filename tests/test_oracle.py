@@ -555,3 +555,29 @@ def test_value_head_dim_matches_brute_force(seed):
                                 wl, wr, dv=dv)
             np.testing.assert_allclose(o[b, h], np.array(bo).reshape(sq, dv), atol=1e-12, rtol=0)
             np.testing.assert_array_equal(np.isneginf(lse[b, h]), np.isneginf(bl))
+
+
+# ---------------------------------------------------------------------------
+# Group mode over a paged KV cache with per-sequence key offsets (gappy).
+# ---------------------------------------------------------------------------
+
+def test_varlen_paged_equals_varlen_on_the_keys_it_addresses():
+    rng = np.random.default_rng(41)
+    P, n_pages, Hq, Hkv, d = 4, 20, 4, 2, 3
+    k_pool = rng.standard_normal((n_pages, P, Hkv, d))
+    v_pool = rng.standard_normal((n_pages, P, Hkv, d))
+    lens_q, lens_k, starts = [3, 5, 2], [6, 9, 1], [4, 2, 7]
+    table = np.stack([rng.permutation(n_pages)[:5] for _ in range(3)])
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    q = rng.standard_normal((cq[-1], Hq, d))
+    o, lse = oracle.attention_varlen_paged(q, k_pool, v_pool, cq, lens_k, table, 0.7, 0.0, -1, 0, kv_start=starts)
+    # the same keys written out by hand: token t of row s is pool[table[s, t // P], t % P]
+    for s in range(3):
+        keys = np.stack([k_pool[table[s, (starts[s] + j) // P], (starts[s] + j) % P] for j in range(lens_k[s])])
+        vals = np.stack([v_pool[table[s, (starts[s] + j) // P], (starts[s] + j) % P] for j in range(lens_k[s])])
+        rows = slice(cq[s], cq[s + 1])
+        for h in range(Hq):
+            bo, bl = brute_head(q[rows, h].tolist(), keys[:, h // 2].tolist(), vals[:, h // 2].tolist(), 0.7, 0.0,
+                                -1, 0)
+            np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)
