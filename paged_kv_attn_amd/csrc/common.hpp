@@ -66,6 +66,11 @@ __device__ __forceinline__ U64 lds_load8(const lds_char* p) {
   const u32x2 v = *(const __attribute__((address_space(3))) u32x2*)p;
   return __builtin_bit_cast(U64, v);
 }
+// 8 bytes to LDS (ds_write_b64).
+__device__ __forceinline__ void lds_store8(lds_char* p, const U64& x) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  *(__attribute__((address_space(3))) u32x2*)p = __builtin_bit_cast(u32x2, x);
+}
 // 16 bytes to LDS (ds_write_b128).
 __device__ __forceinline__ void lds_store16(lds_char* p, const U128& x) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -595,56 +595,85 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- epilogue: normalise, LSE, predicated stores (rows < Lq only) ----
+  // ---- epilogue: normalise, LSE, stores (rows < Lq only) ----
   const float l_tot = sum_across_halves(l_run);
-  if (row_ok) {
-    const bool empty = !(l_tot > 0.0f);  // no visible key: O = 0, LSE = -inf (or the sink logit)
-    float inv = empty ? 0.0f : a.o_mul / l_tot;
-    float lse2 = empty ? kNegInf : m_run * c + __builtin_log2f(l_tot);  // log2 units
-    if (a.sink_logits) {
-      // one more denominator term 2^sk2 (the sink logit in log2 units), no value row
-      const float sk2 = a.sink_logits[hq] * kLog2e;
-      if (empty) {
-        lse2 = sk2;
-      } else if (sk2 > kNegInf) {
-        const float mc = m_run * c;
-        if (sk2 <= mc) {
-          const float l2 = l_tot + fast_exp2(sk2 - mc);
-          inv = a.o_mul / l2;
-          lse2 = mc + __builtin_log2f(l2);
-        } else {  // scale by 2^(mc - sk2) <= 1 so nothing overflows
-          const float f = fast_exp2(mc - sk2);
-          const float l2 = l_tot * f + 1.0f;
-          inv = a.o_mul * f / l2;
-          lse2 = sk2 + __builtin_log2f(l2);
-        }
+  const bool empty = !(l_tot > 0.0f);  // no visible key: O = 0, LSE = -inf (or the sink logit)
+  float inv = empty ? 0.0f : a.o_mul / l_tot;
+  float lse2 = empty ? kNegInf : m_run * c + __builtin_log2f(l_tot);  // log2 units
+  if (a.sink_logits) {
+    // one more denominator term 2^sk2 (the sink logit in log2 units), no value row
+    const float sk2 = a.sink_logits[hq] * kLog2e;
+    if (empty) {
+      lse2 = sk2;
+    } else if (sk2 > kNegInf) {
+      const float mc = m_run * c;
+      if (sk2 <= mc) {
+        const float l2 = l_tot + fast_exp2(sk2 - mc);
+        inv = a.o_mul / l2;
+        lse2 = mc + __builtin_log2f(l2);
+      } else {  // scale by 2^(mc - sk2) <= 1 so nothing overflows
+        const float f = fast_exp2(mc - sk2);
+        const float l2 = l_tot * f + 1.0f;
+        inv = a.o_mul * f / l2;
+        lse2 = sk2 + __builtin_log2f(l2);
       }
     }
-    const int ob = a.out_fp8 ? 1 : 2;  // bytes per stored O element
-    char* op = (char*)a.o + (o_off + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr) * ob;
+  }
+  if (VPAGED && bad) {  // not computed: NaN rows
+    inv = __builtin_nanf("");
+    lse2 = __builtin_nanf("");
+  }
+  if (!a.out_fp8) {
+    // bf16 O through LDS: each lane holds 4-element pieces of its own row, so
+    // direct stores would touch 64 rows per instruction. The wave stages its
+    // 32 x DV tile (row-major, 16-byte chunks XOR-swizzled by row) in a slice of
+    // the V buffers, which no wave reads after the key loop's last barrier,
+    // and writes it back 16 bytes per lane, whole rows per instruction.
+    constexpr int kPitch = DV * 2;            // bytes per staged row
+    constexpr int kNch = DV / 8;              // 16-byte chunks per row
+    constexpr int kRowsPer = 64 / kNch;       // rows per wave store
+    lds_char* const st = (wave < 2 ? vl0 : vl1) + (wave & 1) * 32 * kPitch;
+    const int ri = lane & 31;
+#pragma unroll
+    for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        U64 w;
+        w.x = pack_bf16x2(acc[dblk][4 * q4 + 0] * inv, acc[dblk][4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(acc[dblk][4 * q4 + 2] * inv, acc[dblk][4 * q4 + 3] * inv);
+        const int ch = 4 * dblk + q4;  // columns 8 ch .. 8 ch + 7; this lane's half at + 4 h
+        lds_store8(st + ri * kPitch + 16 * (ch ^ (ri & (kNch - 1))) + 8 * h, w);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 32 / kRowsPer; ++k) {
+      const int r = k * kRowsPer + lane / kNch;
+      const int cc = lane % kNch;
+      const U128 v = lds_load16(st + r * kPitch + 16 * (cc ^ (r & (kNch - 1))));
+      const int grow = wr0 + r;
+      if (grow < rows_total) {
+        const int pr = grow / ratio;
+        const int hr = g * ratio + grow % ratio;
+        *(U128*)((char*)a.o + (o_off + (int64_t)hr * a.o_sh + (int64_t)pr * a.o_sr) * 2 + 16 * cc) = v;
+      }
+    }
+  } else if (row_ok) {
+    char* op = (char*)a.o + (o_off + (int64_t)hq * a.o_sh + (int64_t)pos * a.o_sr);
 #pragma unroll
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * dblk + 8 * q4 + 4 * h;
-        const float o0 = acc[dblk][4 * q4 + 0] * inv, o1 = acc[dblk][4 * q4 + 1] * inv;
-        const float o2 = acc[dblk][4 * q4 + 2] * inv, o3 = acc[dblk][4 * q4 + 3] * inv;
-        if (VPAGED && bad) {  // NaN bit patterns (E4M3FN 0x7F, bf16 0x7FC0)
-          if (a.out_fp8) *(uint32_t*)(op + d) = 0x7F7F7F7Fu;
-          else *(U64*)(op + d * 2) = U64{0x7FC07FC0u, 0x7FC07FC0u};
-        } else if (a.out_fp8) {
-          *(uint32_t*)(op + d) = pack_fp8x4_sat(o0, o1, o2, o3);
+        if (VPAGED && bad) {  // the E4M3FN NaN byte
+          *(uint32_t*)(op + d) = 0x7F7F7F7Fu;
         } else {
-          U64 w;
-          w.x = pack_bf16x2(o0, o1);
-          w.y = pack_bf16x2(o2, o3);
-          *(U64*)(op + d * 2) = w;
+          *(uint32_t*)(op + d) = pack_fp8x4_sat(acc[dblk][4 * q4 + 0] * inv, acc[dblk][4 * q4 + 1] * inv,
+                                                acc[dblk][4 * q4 + 2] * inv, acc[dblk][4 * q4 + 3] * inv);
         }
       }
     }
-    if (VPAGED && bad) lse2 = __builtin_nanf("");
-    if (a.lse && h == 0) a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] = lse2 * kLn2;
   }
+  if (row_ok && a.lse && h == 0) a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] = lse2 * kLn2;
 }
 
 template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
