@@ -2,8 +2,11 @@
  * attn.h - C ABI of the MI355X (gfx950) fused attention forward library
  * (libattn.so).
  *
- * One operation, three addressing modes. For every query row i of sequence b
- * and q-head h, with kv-head g = h / (Hq / Hkv) and used lengths Lq, Lk:
+ * One operation, four entry points: batch (attn_fwd), packed sequences
+ * (attn_fwd_varlen), a paged KV cache (attn_fwd_paged) and packed sequences
+ * over a paged KV cache (attn_fwd_varlen_paged). For every query row i of
+ * sequence b and q-head h, with kv-head g = h / (Hq / Hkv) and used lengths
+ * Lq, Lk:
  *
  *     S[i,j]   = scale * dot(Q[b,h,i,:], K[b,g,j,:])            (0 <= j < Lk)
  *     S[i,j]   = softcap * tanh(S[i,j] / softcap)               if softcap > 0
@@ -30,12 +33,14 @@
  *   - Strides are in ELEMENTS of the stored type; the head dimension d is
  *     contiguous (unit stride). Every tensor base pointer must be 16-byte
  *     aligned and every stride a multiple of 16 bytes.
- *   - Supported: d in {64, 128}; (in_dtype, out_dtype) in {(F32, F32),
+ *   - Supported: d (the head dim of Q and K) in {64, 128}, head_dim_v (of V
+ *     and O; attn_params_t) in {64, 128}; (in_dtype, out_dtype) in {(F32, F32),
  *     (BF16, BF16), (BF16, FP8_E4M3), (FP8_E4M3, BF16), (FP8_E4M3, FP8_E4M3)}.
- *     FP8 output is E4M3FN with a per-tensor scale (o_scale). F32 runs in batch mode only (a plain
- *     vector-ALU kernel). The split-KV decode path (sq * Hq / Hkv <= 16, and
- *     every attn_fwd_paged call) takes BF16 only. FP8 means OCP E4M3FN; the
- *     value of a stored byte x is e4m3(x) * descale of its tensor.
+ *     FP8 output is E4M3FN with a per-tensor scale (o_scale). F32 runs in batch
+ *     mode only (a plain vector-ALU kernel). The split-KV decode path (short
+ *     query blocks: sq * Hq / Hkv <= 16 in attn_fwd and attn_fwd_paged) takes
+ *     BF16 only. FP8 means OCP E4M3FN; the value of a stored byte x is
+ *     e4m3(x) * descale of its tensor.
  *   - lse may be NULL (not stored). LSE is fp32, natural log.
  *   - Rows at or beyond a sequence's used query length are never written, in O
  *     or LSE (the predicated stores of the flash-attention epilogue page).
