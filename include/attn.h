@@ -39,7 +39,8 @@
  *     FP8 output is E4M3FN with a per-tensor scale (o_scale). F32 runs in batch
  *     mode only (a plain vector-ALU kernel). The split-KV decode path (short
  *     query blocks: sq * Hq / Hkv <= 16 in attn_fwd and attn_fwd_paged) takes
- *     BF16 only. FP8 means OCP E4M3FN; the value of a stored byte x is
+ *     BF16 or FP8_E4M3 (FP8: Q K^T on fp8 matrix cores, V widened exactly to
+ *     bf16 for P V). FP8 means OCP E4M3FN; the value of a stored byte x is
  *     e4m3(x) * descale of its tensor.
  *   - lse may be NULL (not stored). LSE is fp32, natural log.
  *   - Rows at or beyond a sequence's used query length are never written, in O
@@ -206,7 +207,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p,
  * page_block_size). seqlens_k (int32 [B], device) gives Lk per request;
  * Lq = sq (bottom-right aligned mask). block_table_stride * page_size bounds
  * every Lk. lse (nullable) is fp32 [B, Hq, sq].
- *   - Decode shapes (sq * Hq / Hkv <= 16): BF16 only, page_size a multiple of
+ *   - Decode shapes (sq * Hq / Hkv <= 16): BF16 or FP8_E4M3, page_size a multiple of
  *     32, split-KV kernel + combine; needs a workspace of attn_workspace_bytes()
  *     bytes with max_seqlen_k = block_table_stride * page_size.
  *   - Longer query blocks (paged prefill, e.g. chunked prefill into a cache):

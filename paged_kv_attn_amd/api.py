@@ -176,7 +176,7 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     """Paged KV cache. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
     (any strides, d contiguous; K and V pools with equal strides);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
-    (sq * Hq / Hkv <= 16, bf16) run the split-KV decode kernel; longer ones
+    (sq * Hq / Hkv <= 16, bf16 or fp8) run the split-KV decode kernel; longer ones
     (bf16 or fp8, page_size a multiple of 64) the prefill kernel. Returns (out, lse)."""
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]

@@ -277,7 +277,6 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   }
 
   if (takes_decode_path(p->in_dtype, sq, ratio)) {
-    if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "the decode path (sq*Hq/Hkv <= 16) supports bf16 only");
     if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
       return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
     if (seqused_q) return fail(ATTN_ENOTSUP, "seqused_q is not supported on the decode path (sq*Hq/Hkv <= 16)");
@@ -300,6 +299,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size;
+    a.fp8 = p->in_dtype == ATTN_FP8_E4M3;
     a.cache_idx = p->cache_batch_idx; a.cache_count = p->cache_batch_count;
     set_bias(p, c_exp2, &a);
     const size_t units = (size_t)B * Hkv * nsp * m_rows;
@@ -416,8 +416,6 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   const int ratio = Hq / Hkv;
   const bool decode_shape = takes_decode_path(p->in_dtype, sq, ratio);
-  if (decode_shape && p->in_dtype != ATTN_BF16)
-    return fail(ATTN_ENOTSUP, "the paged decode path (sq*Hq/Hkv <= 16) supports bf16 only");
   if (!decode_shape && page_size % 64)
     return fail(ATTN_ENOTSUP, "paged prefill (sq*Hq/Hkv > 16) needs page_size a multiple of 64 (got %d)", page_size);
   if (!block_table || !seqlens_k) return fail(ATTN_EINVAL, "block_table / seqlens_k is NULL");
@@ -479,6 +477,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size;
+  a.fp8 = p->in_dtype == ATTN_FP8_E4M3;
   set_bias(p, c_exp2, &a);
   const size_t units = (size_t)B * Hkv * nsp * m_rows;
   a.part_o = (float*)workspace;

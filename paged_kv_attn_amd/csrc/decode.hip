@@ -37,17 +37,26 @@ namespace {
 
 constexpr int kGran = 32;  // keys per pipeline step
 
-template <int D>
+// K rows sit in LDS in their stored type (bf16 or fp8); V rows always as bf16
+// (fp8 V is widened on its way through registers, so P V stays a bf16 product).
+template <int D, bool FP8>
 struct DTr {
-  static constexpr int kSteps = D / 32;        // k-steps of S^T = K Q^T (32 d each)
-  static constexpr int kDBlocks = D / 16;      // 16-row blocks of O^T
-  static constexpr int kRow = D * 2;           // bytes per K/V row
-  static constexpr int kCh = kRow / 16;        // 16-byte chunks per row
-  static constexpr int kBuf = kGran * kRow;    // one K or V granule in LDS
-  static constexpr int kBlocks = kBuf / 1024;  // direct-to-LDS loads per granule per tensor
-  static constexpr int kOps = 2 * kBlocks;     // vector-memory ops per granule
+  static constexpr int kElem = FP8 ? 1 : 2;      // stored bytes per Q/K/V element
+  static constexpr int kSteps = D / 32;          // k-steps of S^T = K Q^T (32 d each)
+  static constexpr int kDBlocks = D / 16;        // 16-row blocks of O^T
+  static constexpr int kRow = D * kElem;         // bytes per K row in LDS
+  static constexpr int kCh = kRow / 16;          // 16-byte chunks per K row
+  static constexpr int kBuf = kGran * kRow;      // one K granule in LDS
+  static constexpr int kBlocks = kBuf / 1024;    // direct-to-LDS loads per K granule
   static constexpr int kRowsPer256 = 256 / kRow;
-  static_assert(kBlocks >= 1, "granule smaller than one direct-to-LDS block");
+  static constexpr int kVRow = D * 2;            // bytes per V row in LDS (bf16)
+  static constexpr int kVCh = kVRow / 16;
+  static constexpr int kVBuf = kGran * kVRow;
+  static constexpr int kVBlocks = kVBuf / 1024;  // direct-to-LDS loads per V granule (bf16)
+  static constexpr int kVRowsPer256 = 256 / kVRow;
+  static constexpr int kV8 = kGran * D / 16 / 64;  // fp8 V: 16-byte register loads per lane per granule
+  static constexpr int kOps = kBlocks + (FP8 ? kV8 : kVBlocks);  // vector-memory ops per granule
+  static_assert(kBlocks >= 1 && kVBlocks >= 1 && (!FP8 || kV8 >= 1), "granule too small");
 };
 
 // Chunk swizzles of the LDS rows (chunk c of row R lives in slot c ^ swz(R));
@@ -57,13 +66,18 @@ struct DTr {
 // transpose read (ds_read_b64_tr_b16) of two 16-lane groups takes 8
 // consecutive rows x 2 adjacent chunks; the swizzle (bit 0 clear, so the pair
 // stays adjacent) gives the 8 rows 8 different chunk pairs.
-template <int D>
+template <int D, bool FP8>
 __device__ __forceinline__ int kswz(int row) {
-  return (row / DTr<D>::kRowsPer256) & (DTr<D>::kCh - 1);
+  return (row / DTr<D, FP8>::kRowsPer256) & (DTr<D, FP8>::kCh - 1);
 }
 template <int D>
 __device__ __forceinline__ int vswz(int row) {
-  return ((row / DTr<D>::kRowsPer256) & (DTr<D>::kCh / 2 - 1)) << 1;
+  return ((row / DTr<D, false>::kVRowsPer256) & (DTr<D, false>::kVCh / 2 - 1)) << 1;
+}
+
+__device__ __forceinline__ f32x4 mfma16_fp8(const U64& a, const U64& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), c, 0,
+                                                    0, 0);
 }
 
 __device__ __forceinline__ float xor_shfl(float x, int mask) {
@@ -71,15 +85,15 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ mask) << 2), __builtin_bit_cast(int, x)));
 }
 
-template <int D, bool PAGED, bool MASK, bool SOFTCAP>
+template <int D, bool PAGED, bool MASK, bool SOFTCAP, bool FP8>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  using Tr = DTr<D>;
+  using Tr = DTr<D, FP8>;
   // One LDS object per pipeline buffer, so the compiler can tell the
   // HBM->LDS copies into one buffer from the reads of the other.
   __shared__ __attribute__((aligned(1024))) char kbuf0[Tr::kBuf];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[Tr::kBuf];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[Tr::kVBuf];
   __shared__ __attribute__((aligned(1024))) char kbuf1[Tr::kBuf];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[Tr::kBuf];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[Tr::kVBuf];
   lds_char* const k0 = (lds_char*)kbuf0;
   lds_char* const v0 = (lds_char*)vbuf0;
   lds_char* const k1 = (lds_char*)kbuf1;
@@ -131,51 +145,76 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
 
   // Q^T as the B operand: lane (column qc, group j4) holds Q[qc][32s + 8 j4 .. +7]
-  U128 qf[Tr::kSteps];
+  // (16 bytes of bf16, or 8 bytes of fp8)
+  U128 qf[FP8 ? 1 : Tr::kSteps];
+  U64 qf8[FP8 ? Tr::kSteps : 1];
   {
-    const char* qp = (const char*)a.q + ((int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)pos * a.q_sr) * 2;
+    const char* qp =
+        (const char*)a.q + ((int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)pos * a.q_sr) * Tr::kElem;
 #pragma unroll
-    for (int s = 0; s < Tr::kSteps; ++s) qf[s] = row_ok ? *(const U128*)(qp + (32 * s + 8 * j4) * 2) : U128{0, 0, 0, 0};
+    for (int s = 0; s < Tr::kSteps; ++s) {
+      if (FP8) qf8[s] = row_ok ? *(const U64*)(qp + 32 * s + 8 * j4) : U64{0, 0};
+      else qf[s] = row_ok ? *(const U128*)(qp + (32 * s + 8 * j4) * 2) : U128{0, 0, 0, 0};
+    }
   }
 
-  const int64_t krow = a.k_sr * 2, vrow = a.v_sr * 2;   // bytes per key row
+  const int64_t krow = a.k_sr * Tr::kElem, vrow = a.v_sr * Tr::kElem;   // bytes per key row
   const int L = lane & 15;
   // K and V granules -> LDS, whole rows per load: block q, lane l covers LDS
   // bytes 1024 q + 16 l = (row R, slot sl) and fetches chunk sl ^ swz(R) of row R.
-  int koff[Tr::kBlocks], voff[Tr::kBlocks];
+  int koff[Tr::kBlocks], voff[FP8 ? Tr::kV8 : Tr::kVBlocks];
 #pragma unroll
   for (int q = 0; q < Tr::kBlocks; ++q) {
     const int B = 1024 * q + 16 * lane;
     const int R = B / Tr::kRow, sl = (B % Tr::kRow) / 16;
-    koff[q] = (int)(R * krow) + 16 * (sl ^ kswz<D>(R));
-    voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz<D>(R));
+    koff[q] = (int)(R * krow) + 16 * (sl ^ kswz<D, FP8>(R));
+  }
+  // V: bf16 rows straight to LDS; fp8 rows as 16-byte chunks into registers
+  // (load i of lane l: chunk 64 i + l = row R, fp8 chunk c8 of the row)
+#pragma unroll
+  for (int q = 0; q < (FP8 ? Tr::kV8 : Tr::kVBlocks); ++q) {
+    if (FP8) {
+      const int ch = 64 * q + lane, R = ch / (D / 16), c8 = ch % (D / 16);
+      voff[q] = (int)(R * vrow) + 16 * c8;
+    } else {
+      const int B = 1024 * q + 16 * lane;
+      const int R = B / Tr::kVRow, sl = (B % Tr::kVRow) / 16;
+      voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz<D>(R));
+    }
   }
   // K A-operand reads: lane (key 16 kb + L, group j4) takes K[key][32 st + 8 j4 .. +7],
   // chunk 4 st + j4 of row 16 kb + L, whose swizzle kswz(16 kb + L) = kswz(L) = ksw:
   // slot (4 st + j4) ^ ksw = ((4 st) ^ (ksw & ~3)) + ((j4 ^ ksw) & 3).
-  const int ksw = kswz<D>(L);
+  const int ksw = kswz<D, FP8>(L);
   const int k_lane0 = L * Tr::kRow + 16 * ((j4 ^ ksw) & 3);
   const int k_hi = 16 * (ksw & ~3);
+  // fp8 K: the 8 bytes K[key][32 st + 8 j4 ..] are half h8 = j4 & 1 of chunk 2 st + j4 / 2
+  // of row 16 kb + L, whose swizzle is kswz(L) for both kb
+  auto k8_addr = [&](int kb, int st) -> int {
+    return (16 * kb + L) * Tr::kRow + 16 * ((2 * st + (j4 >> 1)) ^ ksw) + 8 * (j4 & 1);
+  };
   // transpose reads: group j4 (16 lanes) reads rows 16 kb + 4 j4 + L / 4, bf16
   // columns 16 dblk + 4 (L & 3) .. +3 = byte 8 (L & 1) of chunk 2 dblk + (L & 3) / 2;
   // those rows' swizzle vs = vswz(4 j4 + L / 4) has bit 0 clear, so the slot is
   // (2 dblk ^ vs) + (L & 3) / 2.
   const int v_sw = vswz<D>(4 * j4 + (L >> 2));
-  const int v_base0 = (4 * j4 + (L >> 2)) * Tr::kRow + 16 * ((L & 3) >> 1) + 8 * (L & 1);
+  const int v_base0 = (4 * j4 + (L >> 2)) * Tr::kVRow + 16 * ((L & 3) >> 1) + 8 * (L & 1);
   const int v_swhi = 16 * v_sw;
 
   // base of the 32 keys starting at key gs (64-bit page base + in-page offset)
   auto rows_base = [&](int gs, const void* pool, int64_t sb, int64_t sh, int64_t sr) -> const char* {
     if (PAGED) {
       const int page = __builtin_amdgcn_readlane(pg, gs / a.page_size - p_first);
-      return (const char*)pool + ((int64_t)page * sb + (int64_t)g * sh + (int64_t)(gs % a.page_size) * sr) * 2;
+      return (const char*)pool +
+             ((int64_t)page * sb + (int64_t)g * sh + (int64_t)(gs % a.page_size) * sr) * Tr::kElem;
     }
-    return (const char*)pool + ((int64_t)kb * sb + (int64_t)g * sh + (int64_t)gs * sr) * 2;
+    return (const char*)pool + ((int64_t)kb * sb + (int64_t)g * sh + (int64_t)gs * sr) * Tr::kElem;
   };
   // issue the loads of granule gs into the LDS buffers kb / vb (whole rows,
   // non-temporal: every K and V row is read once). A granule at or past t_hi is
   // issued with an empty range: no memory traffic, zeros everywhere.
-  auto issue = [&](int gs, lds_char* kb, lds_char* vb) {
+  U128 v8a[FP8 ? Tr::kV8 : 1], v8b[FP8 ? Tr::kV8 : 1];  // fp8 V of the two pipeline stages
+  auto issue = [&](int gs, lds_char* kb, lds_char* vb, U128 (&v8)[FP8 ? Tr::kV8 : 1]) {
     // readfirstlane keeps the clamp (a vector med3) from making the
     // descriptor look divergent
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kGran, t_hi - gs)));
@@ -186,8 +225,22 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         make_rsrc(rows_base(gp, a.v, a.v_sb, a.v_sh, a.v_sr), (uint32_t)(rows * vrow));
 #pragma unroll
     for (int q = 0; q < Tr::kBlocks; ++q) buf_load16_lds_stream(kr, kb + 1024 * q, koff[q]);
+    if (FP8) {
 #pragma unroll
-    for (int q = 0; q < Tr::kBlocks; ++q) buf_load16_lds_stream(vr, vb + 1024 * q, voff[q]);
+      for (int q = 0; q < Tr::kV8; ++q) v8[q] = buf_load16(vr, voff[q]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < Tr::kVBlocks; ++q) buf_load16_lds_stream(vr, vb + 1024 * q, voff[q]);
+    }
+  };
+  // fp8 V of one granule: widen (exactly) to bf16 into the LDS layout of bf16 V
+  auto store_v8 = [&](lds_char* vb, const U128 (&v8)[FP8 ? Tr::kV8 : 1]) {
+#pragma unroll
+    for (int q = 0; q < (FP8 ? Tr::kV8 : 0); ++q) {
+      const int ch = 64 * q + lane, R = ch / (D / 16), c0 = 2 * (ch % (D / 16));
+      lds_store16(vb + R * Tr::kVRow + 16 * (c0 ^ vswz<D>(R)), fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}));
+      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1) ^ vswz<D>(R)), fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w}));
+    }
   };
 
   const float c = a.c_exp2;
@@ -204,13 +257,21 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     asm volatile("" : "+v"(k_lane), "+v"(k_x));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      U128 kf[Tr::kSteps];
-#pragma unroll
-      for (int s = 0; s < Tr::kSteps; ++s)
-        kf[s] = lds_load16(kbuf + k_lane + 16 * kb * Tr::kRow + ((64 * s) ^ k_x));
       st[kb] = f32x4{};
+      if (FP8) {
+        U64 kf[Tr::kSteps];
 #pragma unroll
-      for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st[kb]);
+        for (int s = 0; s < Tr::kSteps; ++s) kf[s] = lds_load8(kbuf + k8_addr(kb, s));
+#pragma unroll
+        for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_fp8(kf[s], qf8[s], st[kb]);
+      } else {
+        U128 kf[Tr::kSteps];
+#pragma unroll
+        for (int s = 0; s < Tr::kSteps; ++s)
+          kf[s] = lds_load16(kbuf + k_lane + 16 * kb * Tr::kRow + ((64 * s) ^ k_x));
+#pragma unroll
+        for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st[kb]);
+      }
     }
     // lane (column qc, group j4) holds keys gs + 16 kb + 4 j4 + r
     float mt = kNegInf;
@@ -255,22 +316,24 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
       const lds_char* vp = vb + v_base + ((32 * dblk) ^ v_hi);
       const U64 v0 = lds_read_tr16(vp);
-      const U64 v1 = lds_read_tr16(vp + 16 * Tr::kRow);
+      const U64 v1 = lds_read_tr16(vp + 16 * Tr::kVRow);
       acc[dblk] = mfma16_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
     }
   };
 
   int gs = t_lo;
   if (gs < t_hi) {
-    issue(gs, k0, v0);
+    issue(gs, k0, v0, v8a);
     for (;;) {
-      issue(gs + kGran, k1, v1);
+      issue(gs + kGran, k1, v1, v8b);
       wait_vmem_le<Tr::kOps>();
+      if (FP8) store_v8(v0, v8a);
       compute(gs, k0, v0);
       gs += kGran;
       if (gs >= t_hi) break;
-      issue(gs + kGran, k0, v0);
+      issue(gs + kGran, k0, v0, v8a);
       wait_vmem_le<Tr::kOps>();
+      if (FP8) store_v8(v1, v8b);
       compute(gs, k1, v1);
       gs += kGran;
       if (gs >= t_hi) break;
@@ -380,7 +443,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 template <int D, bool PAGED, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_t s) {
   dim3 grid(a.hkv, a.n_splits, B);
-  hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP>), grid, dim3(64), 0, s, a);
+  if (a.fp8) hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP, true>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP, false>), grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)B * c.hq * c.sq;

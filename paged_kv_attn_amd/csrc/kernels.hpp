@@ -82,6 +82,7 @@ struct DecodeArgs {
   float bias_mul;             // natural-log logit units -> the kernel's logit units
   float* part_o;              // [B][hkv][n_splits][m_rows][d] fp32
   float* part_lse;            // [B][hkv][n_splits][m_rows]
+  int fp8;                    // Q/K/V stored as E4M3FN (descales folded into c_exp2 and the combine)
   const int32_t* cache_idx;   // contiguous K/V only, nullable: K/V batch entry of each request
   int cache_count;
 };

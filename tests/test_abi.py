@@ -157,8 +157,6 @@ def test_attn_fwd_paged_rejects_bad_arguments(kw, status, msg):
 
 
 def test_paged_rejects_unsupported_types():
-    p = _params(in_dtype=_lib.ATTN_FP8_E4M3, out_dtype=_lib.ATTN_BF16)
-    assert _paged(p) == 2 and "bf16 only" in _err()           # fp8 decode shape
     p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)
     assert _paged(p, sq=64) == 2 and "bf16 and fp8" in _err()
 
