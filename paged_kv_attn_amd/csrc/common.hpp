@@ -209,4 +209,14 @@ __device__ __forceinline__ float tanh_fast(float x) {
   return copysignf(t, x);
 }
 
+// Soft-capped logit cap * tanh(y), y = x * pre, in the kernels' log2 units
+// (post = cap * log2 e), from the identity tanh(y) = 1 - 2 / (1 + e^(2y)):
+// one exp, one reciprocal, an add and an FMA; k2 = 2 log2(e) * pre.
+// y -> +inf: e^(2y) = inf, reciprocal 0, result post; y -> -inf: result -post.
+// Absolute error ~ post * 2^-23 (the cancellation in 1 - 2r near y = 0).
+__device__ __forceinline__ float softcap_logit(float x, float k2, float post) {
+  const float r = fast_rcp(1.0f + fast_exp2(x * k2));
+  return __builtin_fmaf(r, -2.0f * post, post);
+}
+
 }  // namespace attn

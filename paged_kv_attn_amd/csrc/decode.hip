@@ -280,7 +280,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = st[kb][r];
-        if (SOFTCAP) x = a.softcap_post * tanh_fast(x * a.softcap_pre);
+        if (SOFTCAP) x = softcap_logit(x, 2.0f * kLog2e * a.softcap_pre, a.softcap_post);
         const int j = gs + 16 * kb + 4 * j4 + r;
         if (a.alibi) x = __builtin_fmaf(-alibi_k, __builtin_fabsf((float)(pos + off - j)), x);
         x = ((j >= lim_lo || j < a.sink_size) && j <= lim_hi) ? x : kNegInf;

@@ -356,7 +356,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   const float c = a.c_exp2;
-  float m_run = kNegInf;   // reference max (raised lazily, see below)
+  // Soft-capped logits without an additive bias never exceed post = cap log2(e)
+  // (kernel units, where c = 1). For caps up to ~41 (2 post <= 120) the fixed
+  // reference m = post then needs no row max and no rescale: every p =
+  // 2^(s' - post) lies in [2^-(2 post), 1], far from fp32 and bf16 underflow.
+  const bool capped = SOFTCAP && BIAS == kBiasNone && a.softcap_post <= 60.0f;
+  float m_run = capped ? a.softcap_post : kNegInf;   // reference max (raised lazily, see below)
   float l_run = 0.0f;      // this lane's partial row sum (its half of the keys)
   f32x16 acc[Tr::kDBlocks];
 #pragma unroll
@@ -406,11 +411,38 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     const int j0 = t * kBlockN;
     f32x16 s[2] = {s0, s1};
+    if (SOFTCAP && BIAS == kBiasNone && capped) {
+      // p = 2^(s' - post) with s' = post (1 - 2 r), r = 1 / (1 + e^(2y)): p = 2^(-2 post r)
+      const float k2 = 2.0f * kLog2e * a.softcap_pre, q2 = -2.0f * a.softcap_post;
+      const int hi = lim_hi - j0 - kHStep * h;
+      const int lo = lim_lo - j0 - kHStep * h;
+      const int sk = a.sink_size - j0 - kHStep * h;
+      const bool two_sided = MASK && a.wl >= 0;
+      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float e0 = q2 * fast_rcp(1.0f + fast_exp2(s[b][r] * k2));
+          float e1 = q2 * fast_rcp(1.0f + fast_exp2(s[b][r + 1] * k2));
+          if (kMasked) {
+            const int j0r = key_rel(b, r), j1r = key_rel(b, r + 1);
+            e0 = ((j0r <= hi) && (!two_sided || j0r >= lo || j0r < sk)) ? e0 : kNegInf;
+            e1 = ((j1r <= hi) && (!two_sided || j1r >= lo || j1r < sk)) ? e1 : kNegInf;
+          }
+          const float p0 = fast_exp2(e0), p1 = fast_exp2(e1);
+          ls[(r >> 1) & 3] += p0 + p1;
+          pk[b][r >> 1] = pack_bf16x2(p0, p1);
+        }
+      }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      return 1.0f;
+    }
     if (SOFTCAP) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[b][r] = a.softcap_post * tanh_fast(s[b][r] * a.softcap_pre);
+        for (int r = 0; r < 16; ++r) s[b][r] = softcap_logit(s[b][r], 2.0f * kLog2e * a.softcap_pre, a.softcap_post);
     }
     // additive bias (after the soft-cap, before the mask); register r of block b
     // is key j0 + 4h + 32b + 8(r/4) + r%4
