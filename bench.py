@@ -7,7 +7,8 @@ One step = the whole hot path over one batch of synthetic input:
     128-token pages in a randomly permuted pool, Hq=32, Hkv=8, d=128 (split-KV
     kernel + combine) -> HBM GB/s.
 Inputs are generated on the GPU and resident in HBM before timing. Each launch
-is bracketed by HIP events on the stream the library enqueues on; values are
+is bracketed by HIP events (device-scope release) on the stream the library
+enqueues on; values are
 algorithmic work / mean launch duration:
   prefill flops = 4 d * (visible query-key pairs) per q-head,
   decode bytes  = K + V of every valid token and kv-head, + Q + O + LSE + the
@@ -89,6 +90,43 @@ def measured_traffic(kind: str):
     if fields.get("kernel_sources_sha256") != sources_sha256(kind) or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+class HipEvents:
+    """HIP events recorded on a given stream, created with hipEventReleaseToDevice:
+    a device-scope release when each event is recorded, so no system-scope cache
+    writeback is counted into the interval between two events (the flag HIP
+    documents for precise timing of the commands between events)."""
+
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self, n: int, stream_handle: int):
+        import ctypes
+        self._ct = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._stream = ctypes.c_void_p(stream_handle)
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.RELEASE_TO_DEVICE)))
+            self.ev.append(e)
+
+    def _check(self, rc: int):
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed with hipError {rc}")
+
+    def record(self, i: int):
+        self._check(self._hip.hipEventRecord(self.ev[i], self._stream))
+
+    def ms(self, i: int, j: int) -> float:
+        x = self._ct.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._ct.byref(x), self.ev[i], self.ev[j]))
+        return x.value
+
+    def close(self):
+        for e in self.ev:
+            self._hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def copy_calibration(mib: int) -> None:
@@ -189,20 +227,22 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # HIP events on the stream the library enqueues on (torch's current stream)
+    ev = HipEvents(4 * args.steps, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record()
+        ev.record(4 * i)
         run_prefill()
-        ev[i][1].record()
-        ev[i][2].record()
+        ev.record(4 * i + 1)
+        ev.record(4 * i + 2)
         run_decode()
-        ev[i][3].record()
+        ev.record(4 * i + 3)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    t_pre = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    t_dec = sorted(e[2].elapsed_time(e[3]) for e in ev)
+    t_pre = sorted(ev.ms(4 * i, 4 * i + 1) for i in range(args.steps))
+    t_dec = sorted(ev.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps))
+    ev.close()
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pre_ms, dec_ms = mean(t_pre), mean(t_dec)
     flops = prefill_flops(pre)
