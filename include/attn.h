@@ -144,9 +144,10 @@ typedef struct {
                           and its O and LSE rows are left untouched (the page's min_seqlen_q
                           of group mode); 0 skips only empty sequences, i.e. nothing. */
   int head_dim_v;      /* head dim of V and O (the page's hdim_v); 0 = the d argument (hdim_q).
-                          64 or 128. A value different from d is supported by attn_fwd on
-                          prefill shapes (sq*Hq/Hkv > 16) and by attn_fwd_varlen, BF16 / FP8 only;
-                          V's rows then have head_dim_v elements and O's rows too. */
+                          64 or 128. A value different from d is supported by attn_fwd (prefill
+                          and split-KV decode shapes alike) and by attn_fwd_varlen, BF16 / FP8
+                          only; V's rows then have head_dim_v elements and O's rows too. The
+                          paged entry points take one stride set for both pools: head_dim_v = d. */
   int v_layout;        /* attn_v_layout_t. ATTN_V_COL_MAJOR (keys contiguous, v_stride[2] the
                           stride between head-dim rows) is supported by attn_fwd on prefill
                           shapes with BF16 inputs and head_dim_v = d; sk must be a multiple of 8

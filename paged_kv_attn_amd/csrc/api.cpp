@@ -219,7 +219,7 @@ size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int 
   const int ratio = Hq / Hkv;
   if (!takes_decode_path(p->in_dtype, sq, ratio)) return 0;
   const int split = plan_split_tokens(p, B, Hkv, max_seqlen_k);
-  return decode_ws_bytes(B, Hkv, n_splits_for(split, max_seqlen_k), sq * ratio, d);
+  return decode_ws_bytes(B, Hkv, n_splits_for(split, max_seqlen_k), sq * ratio, dim_v(p, d));
 }
 
 int attn_num_splits(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int max_seqlen_k) {
@@ -280,11 +280,11 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
       return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
     if (seqused_q) return fail(ATTN_ENOTSUP, "seqused_q is not supported on the decode path (sq*Hq/Hkv <= 16)");
-    if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "head_dim_v != d is not supported on the decode path (sq*Hq/Hkv <= 16)");
+    const int dv = dim_v(p, d);
     const int split = plan_split_tokens(p, B, Hkv, sk);
     const int nsp = n_splits_for(split, sk);
     const int m_rows = sq * ratio;
-    const size_t need = decode_ws_bytes(B, Hkv, nsp, m_rows, d);
+    const size_t need = decode_ws_bytes(B, Hkv, nsp, m_rows, dv);
     if (!workspace || workspace_bytes < need)
       return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
     TRY(check_ptr("workspace", workspace));
@@ -304,7 +304,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     set_bias(p, c_exp2, &a);
     const size_t units = (size_t)B * Hkv * nsp * m_rows;
     a.part_o = (float*)workspace;
-    a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
+    a.part_lse = (float*)((char*)workspace + align256(units * dv * sizeof(float)));
     attn::CombineArgs c{};
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
@@ -314,7 +314,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
   c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
     c.sink_logits = p->sink_logits;
-    return launched(attn::launch_decode(a, c, d, false, B, s));
+    return launched(attn::launch_decode(a, c, d, dv, false, B, s));
   }
 
   attn::PrefillArgs a{};
@@ -490,7 +490,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
   c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
   c.sink_logits = p->sink_logits;
-  return launched(attn::launch_decode(a, c, d, true, B, (hipStream_t)stream));
+  return launched(attn::launch_decode(a, c, d, d, true, B, (hipStream_t)stream));
 }
 
 attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const void* k_pool, const void* v_pool,

@@ -39,22 +39,23 @@ constexpr int kGran = 32;  // keys per pipeline step
 
 // K rows sit in LDS in their stored type (bf16 or fp8); V rows always as bf16
 // (fp8 V is widened on its way through registers, so P V stays a bf16 product).
-template <int D, bool FP8>
+// D: head dim of Q and K; DV: head dim of V and O.
+template <int D, int DV, bool FP8>
 struct DTr {
   static constexpr int kElem = FP8 ? 1 : 2;      // stored bytes per Q/K/V element
   static constexpr int kSteps = D / 32;          // k-steps of S^T = K Q^T (32 d each)
-  static constexpr int kDBlocks = D / 16;        // 16-row blocks of O^T
+  static constexpr int kDBlocks = DV / 16;       // 16-row blocks of O^T
   static constexpr int kRow = D * kElem;         // bytes per K row in LDS
   static constexpr int kCh = kRow / 16;          // 16-byte chunks per K row
   static constexpr int kBuf = kGran * kRow;      // one K granule in LDS
   static constexpr int kBlocks = kBuf / 1024;    // direct-to-LDS loads per K granule
   static constexpr int kRowsPer256 = 256 / kRow;
-  static constexpr int kVRow = D * 2;            // bytes per V row in LDS (bf16)
+  static constexpr int kVRow = DV * 2;           // bytes per V row in LDS (bf16)
   static constexpr int kVCh = kVRow / 16;
   static constexpr int kVBuf = kGran * kVRow;
   static constexpr int kVBlocks = kVBuf / 1024;  // direct-to-LDS loads per V granule (bf16)
   static constexpr int kVRowsPer256 = 256 / kVRow;
-  static constexpr int kV8 = kGran * D / 16 / 64;  // fp8 V: 16-byte register loads per lane per granule
+  static constexpr int kV8 = kGran * DV / 16 / 64;  // fp8 V: 16-byte register loads per lane per granule
   static constexpr int kOps = kBlocks + (FP8 ? kV8 : kVBlocks);  // vector-memory ops per granule
   static_assert(kBlocks >= 1 && kVBlocks >= 1 && (!FP8 || kV8 >= 1), "granule too small");
 };
@@ -68,11 +69,11 @@ struct DTr {
 // stays adjacent) gives the 8 rows 8 different chunk pairs.
 template <int D, bool FP8>
 __device__ __forceinline__ int kswz(int row) {
-  return (row / DTr<D, FP8>::kRowsPer256) & (DTr<D, FP8>::kCh - 1);
+  return (row / DTr<D, D, FP8>::kRowsPer256) & (DTr<D, D, FP8>::kCh - 1);
 }
-template <int D>
+template <int DV>
 __device__ __forceinline__ int vswz(int row) {
-  return ((row / DTr<D, false>::kVRowsPer256) & (DTr<D, false>::kVCh / 2 - 1)) << 1;
+  return ((row / DTr<DV, DV, false>::kVRowsPer256) & (DTr<DV, DV, false>::kVCh / 2 - 1)) << 1;
 }
 
 __device__ __forceinline__ f32x4 mfma16_fp8(const U64& a, const U64& b, const f32x4& c) {
@@ -85,9 +86,9 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ mask) << 2), __builtin_bit_cast(int, x)));
 }
 
-template <int D, bool PAGED, bool MASK, bool SOFTCAP, bool FP8>
+template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP, bool FP8>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  using Tr = DTr<D, FP8>;
+  using Tr = DTr<D, DV, FP8>;
   // One LDS object per pipeline buffer, so the compiler can tell the
   // HBM->LDS copies into one buffer from the reads of the other.
   __shared__ __attribute__((aligned(1024))) char kbuf0[Tr::kBuf];
@@ -174,12 +175,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int q = 0; q < (FP8 ? Tr::kV8 : Tr::kVBlocks); ++q) {
     if (FP8) {
-      const int ch = 64 * q + lane, R = ch / (D / 16), c8 = ch % (D / 16);
+      const int ch = 64 * q + lane, R = ch / (DV / 16), c8 = ch % (DV / 16);
       voff[q] = (int)(R * vrow) + 16 * c8;
     } else {
       const int B = 1024 * q + 16 * lane;
       const int R = B / Tr::kVRow, sl = (B % Tr::kVRow) / 16;
-      voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz<D>(R));
+      voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz<DV>(R));
     }
   }
   // K A-operand reads: lane (key 16 kb + L, group j4) takes K[key][32 st + 8 j4 .. +7],
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   // columns 16 dblk + 4 (L & 3) .. +3 = byte 8 (L & 1) of chunk 2 dblk + (L & 3) / 2;
   // those rows' swizzle vs = vswz(4 j4 + L / 4) has bit 0 clear, so the slot is
   // (2 dblk ^ vs) + (L & 3) / 2.
-  const int v_sw = vswz<D>(4 * j4 + (L >> 2));
+  const int v_sw = vswz<DV>(4 * j4 + (L >> 2));
   const int v_base0 = (4 * j4 + (L >> 2)) * Tr::kVRow + 16 * ((L & 3) >> 1) + 8 * (L & 1);
   const int v_swhi = 16 * v_sw;
 
@@ -237,9 +238,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   auto store_v8 = [&](lds_char* vb, const U128 (&v8)[FP8 ? Tr::kV8 : 1]) {
 #pragma unroll
     for (int q = 0; q < (FP8 ? Tr::kV8 : 0); ++q) {
-      const int ch = 64 * q + lane, R = ch / (D / 16), c0 = 2 * (ch % (D / 16));
-      lds_store16(vb + R * Tr::kVRow + 16 * (c0 ^ vswz<D>(R)), fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}));
-      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1) ^ vswz<D>(R)), fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w}));
+      const int ch = 64 * q + lane, R = ch / (DV / 16), c0 = 2 * (ch % (DV / 16));
+      lds_store16(vb + R * Tr::kVRow + 16 * (c0 ^ vswz<DV>(R)), fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}));
+      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1) ^ vswz<DV>(R)), fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w}));
     }
   };
 
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   if (row_ok) {
     const bool live = m_run != kNegInf;
     const float inv = live ? 1.0f / l_run : 0.0f;
-    float* po = a.part_o + (unit * a.m_rows + qc) * D + 4 * j4;
+    float* po = a.part_o + (unit * a.m_rows + qc) * DV + 4 * j4;
 #pragma unroll
     for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) *(f32x4*)(po + 16 * dblk) = acc[dblk] * inv;
     if (j4 == 0) a.part_lse[unit * a.m_rows + qc] = live ? (m_run * c + __builtin_log2f(l_run)) * kLn2 : kNegInf;
@@ -440,32 +441,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     a.lse[((int64_t)b * a.hq + hq) * a.sq + pos] = (M == kNegInf) ? kNegInf : M + __builtin_log2f(wsum) * kLn2;
 }
 
-template <int D, bool PAGED, bool MASK, bool SOFTCAP>
+template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_t s) {
   dim3 grid(a.hkv, a.n_splits, B);
-  if (a.fp8) hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP, true>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<D, PAGED, MASK, SOFTCAP, false>), grid, dim3(64), 0, s, a);
+  if (a.fp8) hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false>), grid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)B * c.hq * c.sq;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, c);
+  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, c);
   return hipGetLastError();
 }
 
-template <int D, bool PAGED>
+template <int D, int DV, bool PAGED>
 hipError_t launch_p(const DecodeArgs& a, const CombineArgs& c, int B, bool mask, bool softcap, hipStream_t s) {
-  if (mask) return softcap ? launch_t<D, PAGED, true, true>(a, c, B, s) : launch_t<D, PAGED, true, false>(a, c, B, s);
-  return softcap ? launch_t<D, PAGED, false, true>(a, c, B, s) : launch_t<D, PAGED, false, false>(a, c, B, s);
+  if (mask)
+    return softcap ? launch_t<D, DV, PAGED, true, true>(a, c, B, s) : launch_t<D, DV, PAGED, true, false>(a, c, B, s);
+  return softcap ? launch_t<D, DV, PAGED, false, true>(a, c, B, s) : launch_t<D, DV, PAGED, false, false>(a, c, B, s);
+}
+
+template <int D>
+hipError_t launch_dv(const DecodeArgs& a, const CombineArgs& c, int dv, bool paged, int B, bool mask, bool softcap,
+                     hipStream_t s) {
+  if (paged) {  // one stride set for both pools: dv == d only
+    if (dv != D) return hipErrorInvalidValue;
+    return launch_p<D, D, true>(a, c, B, mask, softcap, s);
+  }
+  if (dv == 64) return launch_p<D, 64, false>(a, c, B, mask, softcap, s);
+  return launch_p<D, 128, false>(a, c, B, mask, softcap, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, bool paged, int B, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, int dv, bool paged, int B, hipStream_t s) {
   const bool mask = a.wl >= 0 || a.wr >= 0;
   const bool softcap = a.softcap_pre != 0.0f;
   if (B <= 0 || a.hkv <= 0 || c.sq <= 0) return hipSuccess;
-  if (d == 128) return paged ? launch_p<128, true>(a, c, B, mask, softcap, s) : launch_p<128, false>(a, c, B, mask, softcap, s);
-  return paged ? launch_p<64, true>(a, c, B, mask, softcap, s) : launch_p<64, false>(a, c, B, mask, softcap, s);
+  if (d == 128) return launch_dv<128>(a, c, dv, paged, B, mask, softcap, s);
+  return launch_dv<64>(a, c, dv, paged, B, mask, softcap, s);
 }
 
 }  // namespace attn

@@ -80,7 +80,7 @@ struct DecodeArgs {
   const float* alibi;         // nullable: ALiBi slope of (b, q-head) at alibi[b*alibi_sb + hq]
   int64_t alibi_sb;
   float bias_mul;             // natural-log logit units -> the kernel's logit units
-  float* part_o;              // [B][hkv][n_splits][m_rows][d] fp32
+  float* part_o;              // [B][hkv][n_splits][m_rows][dv] fp32
   float* part_lse;            // [B][hkv][n_splits][m_rows]
   int fp8;                    // Q/K/V stored as E4M3FN (descales folded into c_exp2 and the combine)
   const int32_t* cache_idx;   // contiguous K/V only, nullable: K/V batch entry of each request
@@ -125,7 +125,8 @@ int prefill_rows_per_tile(int in_type);  // packed query rows per prefill workgr
 // d: head dim of Q and K; dv: head dim of V and O ({64, 128} each; paged mode: dv == d)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int batch_or_seqs,
                           hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, bool paged, int B,
+// d: head dim of Q and K; dv: head dim of V and O (contiguous K/V only; paged: dv == d)
+hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, int dv, bool paged, int B,
                          hipStream_t stream);
 hipError_t launch_f32(const F32Args& a, int d, hipStream_t stream);
 

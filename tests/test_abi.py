@@ -250,11 +250,15 @@ def test_head_dim_v_validation():
     assert _fwd(p, d=128) == 2 and "head_dim_v" in _err()
     p = _params(head_dim_v=64)                               # decode shape (sq=1, ratio 4)
     assert _paged(p) == 2 and "paged" in _err()
+    # contiguous decode shapes take head_dim_v: the split-KV partials are sized by it
+    ws64 = lib().attn_workspace_bytes(ctypes.byref(p), 4, 32, 8, 1, 128, 4096)
+    ws128 = lib().attn_workspace_bytes(ctypes.byref(_params()), 4, 32, 8, 1, 128, 4096)
+    assert 0 < ws64 < ws128
     st = [32 * 128, 128, 128]
     kst = [8 * 4096 * 128, 4096 * 128, 128]
     r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
-                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
-    assert r == 2 and "decode path" in _err()
+                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, ws64 - 1, NULL)
+    assert r == 3 and "workspace" in _err()
 
 
 def test_v_layout_validation():

@@ -1,5 +1,6 @@
 """GPU parity of hdim_q != hdim_v (V and O with their own head dim, 64 or
-128) on batch-mode prefill and varlen, bf16 and fp8, against the fp64 oracle."""
+128) on batch-mode prefill, varlen and the split-KV decode path (contiguous
+K/V), bf16 and fp8, against the fp64 oracle."""
 
 import numpy as np
 import pytest
@@ -55,3 +56,29 @@ def test_varlen_head_dim_v(d, dv):
     assert out.shape[-1] == dv
     O, LSE = C.oracle_varlen(c)
     C.assert_parity(out, lse.T, O, LSE.T, "bf16", f"varlen head_dim_v d={d} dv={dv}")
+
+
+@pytest.mark.parametrize("d,dv,dtype,B,Hq,Hkv,sq,sk,split,kw", [
+    (128, 64, "bf16", 3, 32, 8, 1, 3000, 0, dict()),                             # default split plan
+    (64, 128, "bf16", 2, 16, 4, 2, 1500, 256, dict(causal=True, softcap=30.0)),  # 2 queries, cap
+    (128, 64, "fp8", 2, 32, 8, 1, 2100, 512, dict(window=(700, 0))),             # fp8 QK, window
+    (64, 128, "fp8", 1, 8, 1, 2, 999, 64, dict(causal=True)),                    # ratio 8, 16 rows
+])
+def test_decode_head_dim_v(d, dv, dtype, B, Hq, Hkv, sq, sk, split, kw):
+    case = _dense(B, Hq, Hkv, sq, sk, d, dv, dtype, seed=sk + dv, **kw)
+    out, lse = C.run_dense(case, kv_split_tokens=split)
+    assert out.shape == (B, Hq, sq, dv)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, dtype, f"decode head_dim_v d={d} dv={dv} {dtype}")
+
+
+def test_decode_head_dim_v_sinks_alibi():
+    case = _dense(2, 32, 8, 1, 2500, 128, 64, "bf16", 43, window=(400, 0))
+    rng = np.random.default_rng(5)
+    sinks = rng.uniform(-2, 2, size=32)
+    slopes = rng.uniform(0.0, 0.05, size=(2, 32))
+    out, lse = C.run_dense(case, kv_split_tokens=256, sink_size=8,
+                           sink_logits=torch.tensor(sinks, dtype=torch.float32, device=DEV),
+                           alibi_slopes=torch.tensor(slopes, dtype=torch.float32, device=DEV))
+    O, LSE = C.oracle_dense(case, sink_size=8, sink_logits=sinks, alibi_slopes=slopes)
+    C.assert_parity(out, lse, O, LSE, "bf16", "decode head_dim_v with sinks and ALiBi")
