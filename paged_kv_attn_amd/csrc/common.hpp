@@ -47,6 +47,17 @@ __device__ __forceinline__ f32x16 mfma32_bf16(const bf16x8& a, const bf16x8& b, 
 __device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 A and B and unit scales (E8M0 127):
+// the full-rate fp8 product. Lane i + 32 h supplies 32 bytes, k = 32 h .. 32 h + 31,
+// of A's row i and of B's column i (checked on the hardware with an in-bounds
+// probe: A and B pair byte for byte); C as for the other 32x32 shapes.
+__device__ __forceinline__ f32x16 mfma32x64_fp8(const U128& a0, const U128& a1, const U128& b0, const U128& b1,
+                                               const f32x16& c) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const v8i b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 __device__ __forceinline__ f32x16 mfma32_fp8(const U64& a, const U64& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
                                                     c, 0, 0, 0);

@@ -97,15 +97,11 @@ __host__ __device__ inline int group_units(int n_qtiles) {
   return n_qtiles >= kGroupTiles ? 1 : kGroupTiles / n_qtiles;
 }
 
-template <bool FP8> struct QFrag;
-template <> struct QFrag<false> { using T = U128; };
-template <> struct QFrag<true> { using T = U64; };
 
 template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   static_assert(!VT || (!FP8 && D == DV), "column-major V: bf16 with equal head dims");
   using Tr = Traits<D, DV, FP8>;
-  using QT = typename QFrag<FP8>::T;
   // Separate LDS objects per slot: the compiler can then prove that reads of
   // one slot do not alias the HBM->LDS loads in flight into the other, and
   // does not wait for those loads before reading.
@@ -235,14 +231,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int bias_lane = BIAS == kBiasElem ? (int)((int64_t)hq * a.bias_sh + (int64_t)pos * a.bias_sr) * 4 : 0;
 
   // ---- Q fragment, resident in registers for the whole key loop ----
-  // B operand of S^T = K Q^T: lane (row lane%32, half h) holds Q[row][16s + 8h .. +7].
-  QT qf[Tr::kQkSteps];
+  // B operand of S^T = K Q^T. bf16: lane (row lane%32, half h) holds Q[row][16s + 8h .. +7] for step s of
+  // 32x32x16 products. fp8: it holds Q[row][64s + 32h .. +31] (chunks 2s, 2s + 1 of
+  // qf) for step s of 32x32x64 products.
+  U128 qf[FP8 ? D / 32 : Tr::kQkSteps];
   {
     const char* qp = (const char*)a.q + (q_off + (int64_t)hq * a.q_sh + (int64_t)pos * a.q_sr) * Tr::kElem;
 #pragma unroll
-    for (int s = 0; s < Tr::kQkSteps; ++s) {
-      if (row_ok) qf[s] = *(const QT*)(qp + (16 * s + 8 * h) * Tr::kElem);
-      else qf[s] = QT{};
+    for (int s = 0; s < (FP8 ? D / 32 : Tr::kQkSteps); ++s) {
+      const int byte = FP8 ? 64 * (s >> 1) + 32 * h + 16 * (s & 1) : (16 * s + 8 * h) * 2;
+      qf[s] = row_ok ? *(const U128*)(qp + byte) : U128{0, 0, 0, 0};
     }
   }
 
@@ -269,6 +267,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   lds_char* const vl1 = (lds_char*)v_lds1;
   auto kslot = [&](int slot) -> lds_char* { return slot ? kl1 : kl0; };
   auto vslot = [&](int slot) -> lds_char* { return slot ? vl1 : vl0; };
+  // K row swizzle. bf16 rows (256 B) use swz; fp8 rows (128 or 64 B) rotate
+  // their chunks by the row's index among the rows sharing a 256-byte bank
+  // window, so the 16 rows of a 16-byte operand read hit 16 different banks.
+  auto kswz = [](int R) -> int {
+    return FP8 ? (R / (256 / Tr::kKRow)) & (Tr::kKCh - 1) : swz(R, Tr::kKCh);
+  };
   // Wave w fills LDS blocks w, w+4, ... (1 KiB each) of a tile; lane l of block q
   // covers LDS bytes 1024 q + 16 l = (row R, slot s), fetching global chunk s ^ swz(R).
   int koff[Tr::kKInstr], voff[Tr::kVInstr];
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   for (int i = 0; i < Tr::kKInstr; ++i) {
     const int B = 1024 * (wave + 4 * i) + 16 * lane;
     const int R = B / Tr::kKRow, sl = (B % Tr::kKRow) / 16;
-    koff[i] = (int)((VT ? k_row_perm(R) : R) * krow) + 16 * (sl ^ swz(R, Tr::kKCh));
+    koff[i] = (int)((VT ? k_row_perm(R) : R) * krow) + 16 * (sl ^ kswz(R));
   }
 #pragma unroll
   for (int i = 0; i < Tr::kVInstr; ++i) {
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // lane-constant LDS read offsets. K operand: row lane%32 (+32 for the second
   // block, same swizzle), chunk (16 kk + 8 h) * elem / 16.
   const int kR = lane & 31;
-  const int k_swz = swz(kR, Tr::kKCh);
+  const int k_swz = kswz(kR);
   auto k_addr = [&](int kk) -> int {
     const int byte = (16 * kk + 8 * h) * Tr::kElem;
     return kR * Tr::kKRow + 16 * ((byte >> 4) ^ k_swz) + (byte & 15);
@@ -373,11 +377,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     s0 = f32x16{};
     s1 = f32x16{};
     if (FP8) {
+      // 32x32x64 products: lane (key lane%32, half h) reads K[key][64 kk + 32 h .. +31],
+      // chunks 4 kk + 2 h and 4 kk + 2 h + 1 of its LDS row
 #pragma unroll
-      for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
-        const lds_char* p = kt + k_addr(kk);
-        s0 = mfma32_fp8(lds_load8(p), *(const U64*)&qf[kk], s0);
-        s1 = mfma32_fp8(lds_load8(p + 32 * Tr::kKRow), *(const U64*)&qf[kk], s1);
+      for (int kk = 0; kk < D / 64; ++kk) {
+        const lds_char* r = kt + kR * Tr::kKRow;
+        const int c0 = 16 * ((4 * kk + 2 * h) ^ k_swz), c1 = 16 * ((4 * kk + 2 * h + 1) ^ k_swz);
+        s0 = mfma32x64_fp8(lds_load16(r + c0), lds_load16(r + c1), qf[2 * kk], qf[2 * kk + 1], s0);
+        s1 = mfma32x64_fp8(lds_load16(r + 32 * Tr::kKRow + c0), lds_load16(r + 32 * Tr::kKRow + c1),
+                           qf[2 * kk], qf[2 * kk + 1], s1);
       }
     } else {
       // operands of step kk+1 are read while step kk's products run
