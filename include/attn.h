@@ -165,7 +165,9 @@ void attn_params_init(attn_params_t* p, float scale);
  * each addressed as base + b*stride[0] + head*stride[1] + row*stride[2] + c.
  * lse (nullable) is a dense fp32 [B, Hq, sq] array.
  * seqused_q / seqused_k (nullable, int32 [B] on the device) give per-batch used
- * lengths Lq <= sq, Lk <= sk; NULL means Lq = sq, Lk = sk.
+ * lengths Lq <= sq, Lk <= sk; NULL means Lq = sq, Lk = sk. Both the prefill and
+ * the split-KV decode paths honour them (the mask diagonal sits on the used
+ * rows; rows at or past Lq are not written).
  * Short query blocks (sq * Hq / Hkv <= 16) run the split-KV decode path, which
  * needs `workspace` of attn_workspace_bytes() bytes (else workspace may be NULL).
  * (Batch-mode arguments of the Composable Kernel page's MakeKargs; the

@@ -279,7 +279,6 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   if (takes_decode_path(p->in_dtype, sq, ratio)) {
     if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
       return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
-    if (seqused_q) return fail(ATTN_ENOTSUP, "seqused_q is not supported on the decode path (sq*Hq/Hkv <= 16)");
     const int dv = dim_v(p, d);
     const int split = plan_split_tokens(p, B, Hkv, sk);
     const int nsp = n_splits_for(split, sk);
@@ -293,7 +292,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
     a.k_sb = k_stride[0]; a.k_sh = k_stride[1]; a.k_sr = k_stride[2];
     a.v_sb = v_stride[0]; a.v_sh = v_stride[1]; a.v_sr = v_stride[2];
-    a.seqlens_k = seqused_k; a.block_table = nullptr; a.bt_stride = 0; a.page_size = 0;
+    a.seqlens_k = seqused_k; a.seqused_q = seqused_q; a.block_table = nullptr; a.bt_stride = 0; a.page_size = 0;
     a.sk = sk; a.sq = sq; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio; a.m_rows = m_rows;
     a.split_tokens = split; a.n_splits = nsp;
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
@@ -308,7 +307,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     attn::CombineArgs c{};
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
-    c.seqlens_k = seqused_k; c.sk = sk;
+    c.seqlens_k = seqused_k; c.seqused_q = seqused_q; c.sk = sk;
     c.cache_idx = p->cache_batch_idx; c.cache_count = p->cache_batch_count;
     c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
     c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);

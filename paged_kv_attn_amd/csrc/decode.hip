@@ -115,17 +115,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int qc = lane & 15;
   const int j4 = lane >> 4;
   const int ratio = a.ratio;
-  const bool row_ok = qc < a.m_rows;
+  const int Lq = a.seqused_q ? a.seqused_q[b] : a.sq;  // used query rows of this request
+  if (Lq <= 0) return;  // no row of this request is written (the combine skips them too)
   const int pos = qc / ratio;
+  const bool row_ok = qc < a.m_rows && pos < Lq;
   const int hq = g * ratio + qc % ratio;
-  const int off = Lk - a.sq;
+  const int off = Lk - Lq;                             // bottom-right alignment on the used rows
   int lim_lo = 0, lim_hi = Lk - 1;
   // keys any row of the unit can see (bottom-right aligned window)
   int t_lo = t0, t_hi = t1;
   if (MASK) {
     if (a.wr >= 0) {
       lim_hi = min(Lk - 1, pos + off + a.wr);
-      t_hi = min(t1, (a.sq - 1) + off + a.wr + 1);
+      t_hi = min(t1, (Lq - 1) + off + a.wr + 1);
     }
     if (a.wl >= 0) {
       lim_lo = pos + off - a.wl;
@@ -370,6 +372,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int b = (int)(row / ((int64_t)a.sq * a.hq));
   const int g = hq / a.ratio;
   const int r = pos * a.ratio + hq % a.ratio;  // packed row
+  if (a.seqused_q && pos >= a.seqused_q[b]) return;  // row past the used query length: not written
   const int Lk = kv_entry(a.cache_idx, a.cache_count, b) < 0 ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
   const int n = Lk > 0 ? (Lk + a.split_tokens - 1) / a.split_tokens : 0;
   const int64_t unit0 = ((int64_t)b * a.hkv + g) * a.n_splits;

@@ -67,6 +67,7 @@ struct DecodeArgs {
   int64_t k_sb, k_sh, k_sr;   // contiguous: batch, head, row. paged: page, head, slot
   int64_t v_sb, v_sh, v_sr;
   const int32_t* seqlens_k;   // per-request Lk (paged: required; contiguous: nullable)
+  const int32_t* seqused_q;   // contiguous only, nullable: per-request used query rows Lq <= sq
   const int32_t* block_table; // paged only
   int64_t bt_stride;
   int page_size;
@@ -94,6 +95,7 @@ struct CombineArgs {
   float* lse;                 // nullable, [B, hq, sq]
   int64_t o_sb, o_sh, o_sr;
   const int32_t* seqlens_k;   // nullable (then sk)
+  const int32_t* seqused_q;   // nullable (then sq): rows at or past it are not written
   int sk;
   int B, sq, hq, hkv, ratio, m_rows, split_tokens, n_splits;
   float o_mul;                // applied to the normalised O (fp8-output scale)

@@ -121,3 +121,20 @@ def test_workspace_too_small_is_rejected():
                                                                                       kp.stride(1)]),
                               i64_array(t["q"].stride()), ctypes.c_void_p(small.data_ptr()), 16, ctypes.c_void_p(0))
     assert st == 3 and "workspace" in pk.attn_last_error()
+
+
+@pytest.mark.parametrize("dtype,window", [("bf16", (-1, 0)), ("bf16", (200, 0)), ("fp8", (-1, 0))])
+def test_contiguous_decode_seqused_q(dtype, window):
+    """Multi-token decode with per-request used query rows: the mask diagonal
+    sits on the used rows (bottom-right), rows at or past seqused_q are never
+    written, seqused_k tails (NaN-poisoned by the generator) are never read."""
+    su_q, su_k = [4, 1, 0, 3], [1500, 700, 300, 2]
+    case = synth.dense_case(4, 16, 4, 4, 1500, 128, dtype, seed=61 + len(dtype), window=window,
+                            seqused_q=su_q, seqused_k=su_k, device=DEV)
+    sentinel = torch.full((4, 16, 4, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    lse_s = torch.full((4, 16, 4), 7.0, dtype=torch.float32, device=DEV)
+    out, lse = C.run_dense(case, out=sentinel, lse=lse_s, kv_split_tokens=256)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, dtype, f"decode seqused_q {dtype} window={window}")
+    for b, lq in enumerate(su_q):
+        assert (out[b, :, lq:] == 7.0).all() and (lse[b, :, lq:] == 7.0).all(), "rows >= Lq were written"
