@@ -285,7 +285,7 @@ def main():
             "launch_us": round(dec_ms * 1e3, 2), "min_us": round(t_dec[0] * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
-                         "kernel": "decode_kernel<128, paged> + combine_kernel", "algorithmic_bytes": dbytes},
+                         "kernel": "decode_kernel<128, 128, paged> + combine_kernel", "algorithmic_bytes": dbytes},
             "splits": pk.attn_num_splits(p_dec, 64, 32, 8, 1, W * 128),
         },
     }
