@@ -240,10 +240,10 @@ attn_status_t attn_fwd_paged(const attn_params_t* p,
  * s (kv_start NULL: 0), i.e. slot (kv_start[s] + j) % page_size of page
  * block_table[s*block_table_stride + (kv_start[s] + j) / page_size];
  * kv_start[s] + Lk <= block_table_stride * page_size. Bottom-right aligned mask
- * per sequence. page_size must be a multiple of 64 and every kv_start[s] a
- * multiple of 64 (each 64-key tile then lies in one page); a sequence whose
- * kv_start is negative or not a multiple of 64 is not computed: its O and LSE
- * rows are set to NaN and no key of it is read. BF16 or FP8_E4M3 inputs, the
+ * per sequence. page_size must be a multiple of 64; kv_start[s] may be any
+ * non-negative position (a 64-key tile then spans at most two pages). A
+ * sequence whose kv_start is negative is not computed: its O and LSE rows are
+ * set to NaN and no key of it is read. BF16 or FP8_E4M3 inputs, the
  * prefill kernel for every query length; no workspace. Not supported with
  * cache_batch_idx, column-major V or head_dim_v != d.
  */

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   int Lq, Lk;
   int64_t q_off, k_off, v_off, o_off, lse_off;
   int kv0 = 0;       // logical position of key 0 in the sequence's page list
-  bool bad = false;  // varlen-paged: a start that is not tile-aligned -> NaN rows, nothing read
+  bool bad = false;  // varlen-paged: a negative key start -> NaN rows, nothing read
   if (VARLEN) {
     const int q0 = a.cu_q[z], k0 = a.cu_k[z];
     Lq = a.cu_q[z + 1] - q0;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     Lk = a.seqused_k[z];
     if (Lq <= a.min_seqlen_q) return;  // skipped sequence: its rows stay untouched
     kv0 = a.kv_start ? a.kv_start[z] : 0;
-    if (kv0 < 0 || (kv0 & (kBlockN - 1))) {
+    if (kv0 < 0) {
       bad = true;
       kv0 = 0;
       Lk = 0;
@@ -248,8 +248,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const char* kh = (const char*)a.k + (k_off + (int64_t)g * a.k_sh) * Tr::kElem;
   const char* vh = (const char*)a.v + (v_off + (int64_t)g * a.v_sh) * Tr::kElem;
   // start of the 64 rows of tile j0 / 64: contiguous, or (paged) the tile's page
-  // (page_size is a multiple of 64, so a tile never straddles two pages) plus the
-  // in-page offset, as in the page-block navigator of the Composable Kernel page
+  // plus the in-page offset, as in the page-block navigator of the Composable
+  // Kernel page (page_size is a multiple of 64, so with a key start that is a
+  // multiple of 64 a tile lies in one page; other tiles are split below)
   auto tile_rows = [&](const char* head_base, int64_t page_stride, int64_t row_bytes, int j0) -> const char* {
     if (PAGED) {
       const int jl = kv0 + j0;  // logical token position in the page list
@@ -259,6 +260,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     return head_base + j0 * row_bytes;
   };
   const int64_t krow = a.k_sr * Tr::kElem, vrow = a.v_sr * Tr::kElem;  // global bytes per key row
+  // Varlen over a paged pool with a key start that is not a multiple of 64: a
+  // 64-key tile can straddle two pages. Rows 0 .. na-1 of tile j0 lie at the end
+  // of one page, rows na .. at the start of the next; such a tile is loaded in
+  // two lane-masked parts, each through its own page's buffer range.
+  auto rows_in_first_page = [&](int j0) -> int {
+    return VPAGED ? a.page_size - (kv0 + j0) % a.page_size : kBlockN;
+  };
+  auto page_base = [&](const char* head_base, int64_t page_stride, int jl) -> const char* {
+    const int page = a.block_table[(int64_t)z * a.bt_stride + jl / a.page_size];
+    return head_base + (int64_t)page * page_stride * Tr::kElem;
+  };
   // LDS addresses stay in the LDS address space (a generic pointer converted
   // back would cost a null check per use)
   lds_char* const kl0 = (lds_char*)k_lds0;
@@ -299,8 +311,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
   auto load_k = [&](int t, int slot) {
     const int j0 = t * kBlockN;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(kh, a.k_sb, krow, j0), (uint32_t)(min(kBlockN, Lk - j0) * krow));
+    const int rows = min(kBlockN, Lk - j0);
     lds_char* base = kslot(slot);
+    const int na = rows_in_first_page(j0);
+    if (VPAGED && na < rows) {
+      const int jl = kv0 + j0;
+      const __amdgpu_buffer_rsrc_t ra =
+          make_rsrc(page_base(kh, a.k_sb, jl) + (int64_t)(jl % a.page_size) * krow, (uint32_t)(na * krow));
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(page_base(kh, a.k_sb, jl + na), (uint32_t)((rows - na) * krow));
+#pragma unroll
+      for (int i = 0; i < Tr::kKInstr; ++i) {
+        const int R = (1024 * (wave + 4 * i) + 16 * lane) / Tr::kKRow;   // tile row of this lane's chunk
+        if (R < na) buf_load16_lds(ra, base + 1024 * (wave + 4 * i), koff[i]);
+        else buf_load16_lds(rb, base + 1024 * (wave + 4 * i), koff[i] - na * (int)krow);
+      }
+      return;
+    }
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(kh, a.k_sb, krow, j0), (uint32_t)(rows * krow));
 #pragma unroll
     for (int i = 0; i < Tr::kKInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), koff[i]);
   };
@@ -319,7 +346,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         buf_load16_lds(r, base + 1024 * (wave + 4 * i), j0 + 8 * vt_kc[i] < Lk ? voff[i] : 0x7FFFFFF0);
       return;
     }
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(vh, a.v_sb, vrow, j0), (uint32_t)(min(kBlockN, Lk - j0) * vrow));
+    const int rows = min(kBlockN, Lk - j0);
+    const int na = rows_in_first_page(j0);
+    if (VPAGED && na < rows) {
+      const int jl = kv0 + j0;
+      const __amdgpu_buffer_rsrc_t ra =
+          make_rsrc(page_base(vh, a.v_sb, jl) + (int64_t)(jl % a.page_size) * vrow, (uint32_t)(na * vrow));
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(page_base(vh, a.v_sb, jl + na), (uint32_t)((rows - na) * vrow));
+      if (FP8) {
+#pragma unroll
+        for (int i = 0; i < Tr::kV8Loads; ++i) {
+          const int R = v8row + i * (kThreads / Tr::kV8Ch);
+          const int off = (int)(R * vrow) + 16 * v8ch;
+          v8[i] = R < na ? buf_load16(ra, off) : buf_load16(rb, off - na * (int)vrow);
+        }
+      } else {
+        lds_char* base = vslot(slot);
+#pragma unroll
+        for (int i = 0; i < Tr::kVInstr; ++i) {
+          const int R = (1024 * (wave + 4 * i) + 16 * lane) / Tr::kVRow;
+          if (R < na) buf_load16_lds(ra, base + 1024 * (wave + 4 * i), voff[i]);
+          else buf_load16_lds(rb, base + 1024 * (wave + 4 * i), voff[i] - na * (int)vrow);
+        }
+      }
+      return;
+    }
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_rows(vh, a.v_sb, vrow, j0), (uint32_t)(rows * vrow));
     if (FP8) {
 #pragma unroll
       for (int i = 0; i < Tr::kV8Loads; ++i)

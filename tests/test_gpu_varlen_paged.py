@@ -1,8 +1,9 @@
 """GPU parity of group mode over a paged KV cache (attn_fwd_varlen_paged):
 varlen queries, keys through the block table from a per-sequence logical
 start (gappy group mode), against the fp64 oracle; bit-exact against
-attn_fwd_varlen on the same keys gathered contiguously; starts that are not
-multiples of 64 give NaN rows and read nothing."""
+attn_fwd_varlen on the same keys gathered contiguously. Starts that are not
+multiples of 64 make 64-key tiles straddle two pages (loaded in two parts);
+a negative start gives NaN rows and reads nothing."""
 
 import numpy as np
 import pytest
@@ -53,13 +54,14 @@ def test_varlen_paged_parity(page, Hq, Hkv, d, causal):
     C.assert_parity(out, lse.T, O, LSE.T, "bf16", f"varlen paged page={page} d={d}")
 
 
-def test_varlen_paged_bitexact_vs_contiguous_varlen():
-    case = synth.varlen_paged_case([400, 129, 64], [700, 300, 64], [128, 0, 256], 8, 2, 128, page_size=64, seed=3,
+@pytest.mark.parametrize("starts,page", [([128, 0, 256], 64), ([5, 100, 63], 64), ([127, 1, 200], 128)])
+def test_varlen_paged_bitexact_vs_contiguous_varlen(starts, page):
+    case = synth.varlen_paged_case([400, 129, 64], [700, 300, 64], starts, 8, 2, 128, page_size=page, seed=3,
                                    device=DEV)
     t = case.t
     o_p, l_p = _run(case)
     # the same keys gathered into a packed [Tk, Hkv, d] layout
-    P, table = 64, t["block_table"].cpu()
+    P, table = page, t["block_table"].cpu()
     ks, vs = [], []
     for s, (L, st) in enumerate(zip(case.meta["lens_k"], case.meta["starts"])):
         tok = torch.arange(st, st + L)
@@ -73,17 +75,32 @@ def test_varlen_paged_bitexact_vs_contiguous_varlen():
     assert torch.equal(C.bits(o_p), C.bits(o_c)) and torch.equal(C.bits(l_p), C.bits(l_c))
 
 
-def test_varlen_paged_misaligned_start_gives_nan_rows():
+@pytest.mark.parametrize("page,d,dtype,causal", [(64, 128, "bf16", True), (128, 64, "bf16", False),
+                                                  (192, 128, "fp8", True)])
+def test_varlen_paged_unaligned_starts(page, d, dtype, causal):
+    """Key starts anywhere in a page: tiles straddle page boundaries at every offset."""
+    lens_q, lens_k = [100, 60, 50, 1, 300, 77], [200, 100, 90, 500, 300, 64]
+    starts = [0, 32, 7, 63, 129, page - 1]
+    case = synth.varlen_paged_case(lens_q, lens_k, starts, 8, 2, d, page_size=page, dtype=dtype, seed=page + d,
+                                   causal=causal, device=DEV)
+    out, lse = _run(case)
+    O, LSE = _oracle(case)
+    C.assert_parity(out, lse.T, O, LSE.T, dtype, f"varlen paged unaligned starts page={page} d={d} {dtype}")
+
+
+def test_varlen_paged_negative_start_gives_nan_rows():
     case = synth.varlen_paged_case([100, 60, 50], [200, 100, 90], [0, 32, 64], 4, 2, 128, page_size=64, seed=7,
                                    device=DEV)
+    case.t["kv_start"][1] = -32                 # sequence 1: not computed
     out, lse = _run(case)
-    rows = slice(100, 160)                     # sequence 1 (start 32)
+    rows = slice(100, 160)
     assert torch.isnan(out[rows].float()).all() and torch.isnan(lse[:, rows]).all()
     keep = torch.ones(out.shape[0], dtype=torch.bool, device=DEV)
     keep[rows] = False
+    case.t["kv_start"][1] = 32
     O, LSE = _oracle(case)
     o_ok, l_ok = out[keep], lse[:, keep]
-    C.assert_parity(o_ok, l_ok.T, O[keep.cpu().numpy()], LSE[:, keep.cpu().numpy()].T, "bf16", "aligned sequences")
+    C.assert_parity(o_ok, l_ok.T, O[keep.cpu().numpy()], LSE[:, keep.cpu().numpy()].T, "bf16", "other sequences")
 
 
 def test_varlen_paged_fp8_window_softcap_and_skip():
