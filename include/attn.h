@@ -147,12 +147,16 @@ typedef struct {
                           64 or 128. A value different from d is supported by attn_fwd (prefill
                           and split-KV decode shapes alike) and by attn_fwd_varlen, BF16 / FP8
                           only; V's rows then have head_dim_v elements and O's rows too. The
-                          paged entry points take one stride set for both pools: head_dim_v = d. */
+                          paged entry points need v_pool_stride for it (the pools' rows differ). */
   int v_layout;        /* attn_v_layout_t. ATTN_V_COL_MAJOR (keys contiguous, v_stride[2] the
                           stride between head-dim rows) is supported by attn_fwd on prefill
                           shapes with BF16 inputs and head_dim_v = d; sk must be a multiple of 8
                           and (head_dim_v - 1) * v_stride[2] * 2 + 128 < 2^31. Keys past
                           seqused_k may hold any bits: they are never used. */
+  int64_t v_pool_stride[3]; /* attn_fwd_paged / attn_fwd_varlen_paged: the V pool's {page, head,
+                          slot} element strides when they differ from the K pool's (required with
+                          head_dim_v != d); all zero = kv_stride for both pools. Same rules as
+                          kv_stride (multiples of 16 bytes, d contiguous). */
 } attn_params_t;
 
 /* Fill *p with defaults: BF16 in/out, the given scale, no soft-cap, no mask,
@@ -245,7 +249,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p,
  * sequence whose kv_start is negative is not computed: its O and LSE rows are
  * set to NaN and no key of it is read. BF16 or FP8_E4M3 inputs, the
  * prefill kernel for every query length; no workspace. Not supported with
- * cache_batch_idx, column-major V or head_dim_v != d.
+ * cache_batch_idx or column-major V. head_dim_v != d needs v_pool_stride.
  */
 attn_status_t attn_fwd_varlen_paged(const attn_params_t* p,
                                     const void* q, const void* k_pool, const void* v_pool,

@@ -40,6 +40,7 @@ class AttnParams(ctypes.Structure):
         ("min_seqlen_q", ctypes.c_int),
         ("head_dim_v", ctypes.c_int),
         ("v_layout", ctypes.c_int),
+        ("v_pool_stride", ctypes.c_int64 * 3),
     ]
 
 

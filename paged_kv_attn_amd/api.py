@@ -170,27 +170,35 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     return out, lse
 
 
+def _set_v_pool(p, d, k_pool, v_pool):
+    """The V pool's head dim and {page, head, slot} strides (when they differ
+    from the K pool's) into the call's attn_params_t."""
+    if v_pool.shape[3] != d:
+        p.head_dim_v = v_pool.shape[3]
+    if v_pool.stride() != k_pool.stride() or v_pool.shape[3] != d:
+        for i, s in enumerate((v_pool.stride(0), v_pool.stride(2), v_pool.stride(1))):
+            p.v_pool_stride[i] = s
+
+
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
                    softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
                    workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None, o_scale=1.0):
-    """Paged KV cache. q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d]
-    (any strides, d contiguous; K and V pools with equal strides);
+    """Paged KV cache. q [B, Hq, sq, d]; k_pool [num_pages, page_size, Hkv, d],
+    v_pool [num_pages, page_size, Hkv, dv] (any strides, last dim contiguous);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
     (sq * Hq / Hkv <= 16, bf16 or fp8) run the split-KV decode kernel; longer ones
     (bf16 or fp8, page_size a multiple of 64) the prefill kernel. Returns (out, lse)."""
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
-    if k_pool.stride() != v_pool.stride():
-        raise ValueError("k_pool and v_pool must have the same strides")
+    dv = v_pool.shape[3]
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
     W = block_table.shape[1]
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
-    if v_pool.shape[3] != d:
-        p.head_dim_v = v_pool.shape[3]     # rejected by the library (equal dims only in paged mode)
+    _set_v_pool(p, d, k_pool, v_pool)
     if out is None:
-        out = torch.empty((B, Hq, sq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((B, Hq, sq, dv), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
     ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, W * page_size)
@@ -209,15 +217,13 @@ def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_tabl
                           lse=None, return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None,
                           out_dtype=None, o_scale=1.0, min_seqlen_q=0):
     """Varlen queries over a paged KV cache. q [Tq, Hq, d] with cu_seqlens_q
-    int32 [n+1]; pools [num_pages, page_size, Hkv, d] (equal strides);
+    int32 [n+1]; k_pool [num_pages, page_size, Hkv, d], v_pool [.., dv] (any strides);
     block_table int32 [n, W]; seqlens_k int32 [n]; kv_start (int32 [n] or
-    None): logical position of each sequence's first key in its page list, a
-    multiple of 64 (else that sequence's rows come back NaN). Returns
-    (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
+    None): logical position of each sequence's first key in its page list
+    (a negative start gives that sequence NaN rows). Returns
+    (out [Tq, Hq, dv], lse [Hq, Tq] or None)."""
     Tq, Hq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
-    if k_pool.stride() != v_pool.stride():
-        raise ValueError("k_pool and v_pool must have the same strides")
     for name, t in (("block_table", block_table), ("seqlens_k", seqlens_k), ("cu_seqlens_q", cu_seqlens_q),
                     ("kv_start", kv_start)):
         if t is not None and t.dtype != torch.int32:
@@ -226,8 +232,9 @@ def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_tabl
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     p.min_seqlen_q = int(min_seqlen_q)
+    _set_v_pool(p, d, k_pool, v_pool)
     if out is None:
-        out = torch.empty((Tq, Hq, d), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((Tq, Hq, v_pool.shape[3]), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     kv_stride = i64_array([k_pool.stride(0), k_pool.stride(2), k_pool.stride(1)])

@@ -74,6 +74,12 @@ void set_bias(const attn_params_t* p, float c_exp2, attn::DecodeArgs* a) {
   a->bias_mul = 1.4426950408889634f / c_exp2;
 }
 
+// the V pool's strides: its own when any is set, else the K pool's
+const int64_t* v_pool_strides(const attn_params_t* p, const int64_t* kv_stride) {
+  const bool own = p->v_pool_stride[0] || p->v_pool_stride[1] || p->v_pool_stride[2];
+  return own ? p->v_pool_stride : kv_stride;
+}
+
 size_t decode_ws_bytes(int B, int Hkv, int n_splits, int m_rows, int d) {
   const size_t units = (size_t)B * Hkv * n_splits * m_rows;
   return align256(units * d * sizeof(float)) + align256(units * sizeof(float));
@@ -212,6 +218,7 @@ void attn_params_init(attn_params_t* p, float scale) {
   p->min_seqlen_q = 0;
   p->head_dim_v = 0;
   p->v_layout = ATTN_V_ROW_MAJOR;
+  p->v_pool_stride[0] = p->v_pool_stride[1] = p->v_pool_stride[2] = 0;
 }
 
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d, int max_seqlen_k) {
@@ -404,7 +411,10 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
                              const int64_t o_stride[3], void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_params(p, d));
   TRY(check_mode_fields(p, false, false));
-  if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "head_dim_v != d is not supported in paged mode (one stride set for both pools)");
+  const int dv = dim_v(p, d);
+  const int64_t* v_st = v_pool_strides(p, kv_stride);
+  if (dv != d && v_st == kv_stride)
+    return fail(ATTN_EINVAL, "head_dim_v != d in paged mode needs v_pool_stride (the V pool's strides)");
   if (B < 0 || sq < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
     return fail(ATTN_EINVAL, "bad sizes B=%d sq=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", B, sq, Hq, Hkv,
                 block_table_stride, num_pages);
@@ -426,6 +436,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   const int eb = elem_bytes(p->in_dtype);
   TRY(check_strides("q", q_stride, 3, eb));
   TRY(check_strides("kv", kv_stride, 3, eb));
+  TRY(check_strides("v_pool_stride", v_st, 3, eb));
   TRY(check_strides("o", o_stride, 3, elem_bytes(p->out_dtype)));
   if (B == 0 || sq == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
@@ -441,7 +452,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.q = q; a.k = k_pool; a.v = v_pool; a.o = o; a.lse = lse;
     a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
     a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
-    a.v_sb = kv_stride[0]; a.v_sh = kv_stride[1]; a.v_sr = kv_stride[2];
+    a.v_sb = v_st[0]; a.v_sh = v_st[1]; a.v_sr = v_st[2];
     a.o_sb = o_stride[0]; a.o_sh = o_stride[1]; a.o_sr = o_stride[2];
     a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
     a.seqused_q = nullptr; a.seqused_k = seqlens_k;
@@ -455,13 +466,13 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
     set_bias(p, c_exp2, &a);
-    return launched(attn::launch_prefill(a, d, d, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
+    return launched(attn::launch_prefill(a, d, dv, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
   }
 
   const int split = plan_split_tokens(p, B, Hkv, max_len);
   const int nsp = n_splits_for(split, max_len);
   const int m_rows = sq * ratio;
-  const size_t need = decode_ws_bytes(B, Hkv, nsp, m_rows, d);
+  const size_t need = decode_ws_bytes(B, Hkv, nsp, m_rows, dv);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
   TRY(check_ptr("workspace", workspace));
@@ -469,7 +480,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   a.q = q; a.k = k_pool; a.v = v_pool;
   a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
   a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
-  a.v_sb = kv_stride[0]; a.v_sh = kv_stride[1]; a.v_sr = kv_stride[2];
+  a.v_sb = v_st[0]; a.v_sh = v_st[1]; a.v_sr = v_st[2];
   a.seqlens_k = seqlens_k; a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
   a.sk = max_len; a.sq = sq; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio; a.m_rows = m_rows;
   a.split_tokens = split; a.n_splits = nsp;
@@ -480,7 +491,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   set_bias(p, c_exp2, &a);
   const size_t units = (size_t)B * Hkv * nsp * m_rows;
   a.part_o = (float*)workspace;
-  a.part_lse = (float*)((char*)workspace + align256(units * d * sizeof(float)));
+  a.part_lse = (float*)((char*)workspace + align256(units * dv * sizeof(float)));
   attn::CombineArgs c{};
   c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
   c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
@@ -489,7 +500,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
   c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
   c.sink_logits = p->sink_logits;
-  return launched(attn::launch_decode(a, c, d, d, true, B, (hipStream_t)stream));
+  return launched(attn::launch_decode(a, c, d, dv, true, B, (hipStream_t)stream));
 }
 
 attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const void* k_pool, const void* v_pool,
@@ -500,7 +511,10 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
                                     const int64_t o_stride[2], void* stream) {
   TRY(check_params(p, d));
   TRY(check_mode_fields(p, false, true));
-  if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "head_dim_v != d is not supported in paged mode (one stride set for both pools)");
+  const int dv = dim_v(p, d);
+  const int64_t* v_st = v_pool_strides(p, kv_stride);
+  if (dv != d && v_st == kv_stride)
+    return fail(ATTN_EINVAL, "head_dim_v != d in paged mode needs v_pool_stride (the V pool's strides)");
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "paged KV supports bf16 and fp8 inputs");
   if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
     return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
@@ -521,6 +535,7 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   const int eb = elem_bytes(p->in_dtype);
   TRY(check_strides("q", q_stride, 2, eb));
   TRY(check_strides("kv", kv_stride, 3, eb));
+  TRY(check_strides("v_pool_stride", v_st, 3, eb));
   TRY(check_strides("o", o_stride, 2, elem_bytes(p->out_dtype)));
   if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
@@ -532,7 +547,7 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   a.q = q; a.k = k_pool; a.v = v_pool; a.o = o; a.lse = lse;
   a.q_sb = 0; a.q_sh = q_stride[1]; a.q_sr = q_stride[0];
   a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
-  a.v_sb = kv_stride[0]; a.v_sh = kv_stride[1]; a.v_sr = kv_stride[2];
+  a.v_sb = v_st[0]; a.v_sh = v_st[1]; a.v_sr = v_st[2];
   a.o_sb = 0; a.o_sh = o_stride[1]; a.o_sr = o_stride[0];
   a.lse_sb = 0; a.lse_sh = total_q;
   a.cu_q = cu_seqlens_q; a.cu_k = nullptr;
@@ -548,7 +563,7 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
-  return launched(attn::launch_prefill(a, d, d, p->in_dtype, attn::kPrefillVarlenPaged, n, (hipStream_t)stream));
+  return launched(attn::launch_prefill(a, d, dv, p->in_dtype, attn::kPrefillVarlenPaged, n, (hipStream_t)stream));
 }
 
 }  // extern "C"

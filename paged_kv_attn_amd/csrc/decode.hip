@@ -466,10 +466,7 @@ hipError_t launch_p(const DecodeArgs& a, const CombineArgs& c, int B, bool mask,
 template <int D>
 hipError_t launch_dv(const DecodeArgs& a, const CombineArgs& c, int dv, bool paged, int B, bool mask, bool softcap,
                      hipStream_t s) {
-  if (paged) {  // one stride set for both pools: dv == d only
-    if (dv != D) return hipErrorInvalidValue;
-    return launch_p<D, D, true>(a, c, B, mask, softcap, s);
-  }
+  if (paged) return dv == 64 ? launch_p<D, 64, true>(a, c, B, mask, softcap, s) : launch_p<D, 128, true>(a, c, B, mask, softcap, s);
   if (dv == 64) return launch_p<D, 64, false>(a, c, B, mask, softcap, s);
   return launch_p<D, 128, false>(a, c, B, mask, softcap, s);
 }

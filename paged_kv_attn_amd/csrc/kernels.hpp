@@ -127,7 +127,7 @@ int prefill_rows_per_tile(int in_type);  // packed query rows per prefill workgr
 // d: head dim of Q and K; dv: head dim of V and O ({64, 128} each; paged mode: dv == d)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int batch_or_seqs,
                           hipStream_t stream);
-// d: head dim of Q and K; dv: head dim of V and O (contiguous K/V only; paged: dv == d)
+// d: head dim of Q and K; dv: head dim of V and O
 hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, int dv, bool paged, int B,
                          hipStream_t stream);
 hipError_t launch_f32(const F32Args& a, int d, hipStream_t stream);

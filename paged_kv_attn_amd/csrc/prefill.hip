@@ -811,13 +811,8 @@ hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipSt
 template <int D, int DV, bool FP8>
 hipError_t launch_f(const PrefillArgs& a, int mode, int nz, bool mask, bool softcap, hipStream_t s) {
   if (mode == kPrefillVarlen) return launch_m<D, DV, FP8, kPrefillVarlen>(a, nz, mask, softcap, s);
-  if constexpr (D == DV) {
-    if (mode == kPrefillPaged) return launch_m<D, DV, FP8, kPrefillPaged>(a, nz, mask, softcap, s);
-    if (mode == kPrefillVarlenPaged) return launch_m<D, DV, FP8, kPrefillVarlenPaged>(a, nz, mask, softcap, s);
-  } else {
-    if (mode == kPrefillPaged || mode == kPrefillVarlenPaged)
-      return hipErrorInvalidValue;  // one stride set for both pools: equal dims only
-  }
+  if (mode == kPrefillPaged) return launch_m<D, DV, FP8, kPrefillPaged>(a, nz, mask, softcap, s);
+  if (mode == kPrefillVarlenPaged) return launch_m<D, DV, FP8, kPrefillVarlenPaged>(a, nz, mask, softcap, s);
   return launch_m<D, DV, FP8, kPrefillBatch>(a, nz, mask, softcap, s);
 }
 

@@ -248,8 +248,13 @@ def test_head_dim_v_validation():
     assert _fwd(p) == 2 and "head_dim_v" in _err()
     p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, head_dim_v=64)
     assert _fwd(p, d=128) == 2 and "head_dim_v" in _err()
-    p = _params(head_dim_v=64)                               # decode shape (sq=1, ratio 4)
-    assert _paged(p) == 2 and "paged" in _err()
+    p = _params(head_dim_v=64)                               # paged: the V pool's strides are required
+    assert _paged(p) == 1 and "v_pool_stride" in _err()
+    p.v_pool_stride[0], p.v_pool_stride[1], p.v_pool_stride[2] = 64 * 8 * 64, 64, 8 * 64
+    q = _params(head_dim_v=64)
+    q.v_pool_stride[0], q.v_pool_stride[1], q.v_pool_stride[2] = 64 * 8 * 64 + 4, 64, 8 * 64
+    assert _paged(q) == 1 and "v_pool_stride" in _err()      # not a multiple of 16 bytes
+    p = _params(head_dim_v=64)
     # contiguous decode shapes take head_dim_v: the split-KV partials are sized by it
     ws64 = lib().attn_workspace_bytes(ctypes.byref(p), 4, 32, 8, 1, 128, 4096)
     ws128 = lib().attn_workspace_bytes(ctypes.byref(_params()), 4, 32, 8, 1, 128, 4096)
@@ -293,6 +298,6 @@ def test_varlen_paged_rejects_bad_arguments():
     assert _vpaged(p, kv_start=ctypes.c_void_p(0x10002)) == 1 and "kv_start" in _err()
     assert _vpaged(p, table=NULL) == 1 and "block_table" in _err()
     assert _vpaged(_params(cache_batch_idx=0x10000, cache_batch_count=1)) == 1 and "batch mode" in _err()
-    assert _vpaged(_params(head_dim_v=64)) == 2 and "head_dim_v" in _err()
+    assert _vpaged(_params(head_dim_v=64)) == 1 and "v_pool_stride" in _err()
     assert _vpaged(_params(v_layout=_lib.ATTN_V_COL_MAJOR)) == 2 and "column-major" in _err()
     assert _vpaged(_params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)) == 2

@@ -1,11 +1,13 @@
 """GPU parity of hdim_q != hdim_v (V and O with their own head dim, 64 or
-128) on batch-mode prefill, varlen and the split-KV decode path (contiguous
-K/V), bf16 and fp8, against the fp64 oracle."""
+128) on batch-mode prefill, varlen, the split-KV decode path (contiguous and
+paged K/V), paged prefill and varlen over a paged pool (V pool strides of its
+own), bf16 and fp8, against the fp64 oracle."""
 
 import numpy as np
 import pytest
 import torch
 
+import paged_kv_attn_amd as pk
 import synth
 from tests import _cases as C
 
@@ -82,3 +84,47 @@ def test_decode_head_dim_v_sinks_alibi():
                            alibi_slopes=torch.tensor(slopes, dtype=torch.float32, device=DEV))
     O, LSE = C.oracle_dense(case, sink_size=8, sink_logits=sinks, alibi_slopes=slopes)
     C.assert_parity(out, lse, O, LSE, "bf16", "decode head_dim_v with sinks and ALiBi")
+
+
+def _paged(lens, sq, Hq, Hkv, d, dv, page, dtype, seed, **kw):
+    """K pool with head dim d, V pool with dv: two draws with one seed share the block table."""
+    c = synth.paged_case(lens, sq, Hq, Hkv, d, page, dtype, seed=seed, device=DEV, **kw)
+    cv = synth.paged_case(lens, sq, Hq, Hkv, dv, page, dtype, seed=seed, device=DEV, **kw)
+    assert torch.equal(c.t["block_table"], cv.t["block_table"])
+    c.t["v_pool"] = cv.t["v_pool"]
+    c.descale["v"] = cv.descale["v"]
+    return c
+
+
+@pytest.mark.parametrize("d,dv,dtype,sq,kw", [
+    (128, 64, "bf16", 1, dict()),                                   # split-KV decode
+    (64, 128, "fp8", 2, dict(causal=True, softcap=30.0)),           # decode, fp8, cap
+    (128, 64, "bf16", 150, dict(causal=True)),                      # paged prefill
+    (64, 128, "fp8", 130, dict(window=(70, 0))),                    # paged prefill, fp8, window
+])
+def test_paged_head_dim_v(d, dv, dtype, sq, kw):
+    case = _paged([900, 64, 1500], sq, 16, 4, d, dv, 128, dtype, seed=dv + sq, **kw)
+    out, lse = C.run_paged(case, kv_split_tokens=256)
+    assert out.shape[-1] == dv
+    O, LSE = C.oracle_paged(case)
+    C.assert_parity(out, lse, O, LSE, dtype, f"paged head_dim_v d={d} dv={dv} {dtype} sq={sq}")
+
+
+@pytest.mark.parametrize("d,dv", [(128, 64), (64, 128)])
+def test_varlen_paged_head_dim_v(d, dv):
+    import oracle
+    lens_q, lens_k, starts = [120, 1, 77], [300, 40, 200], [5, 0, 64]
+    c = synth.varlen_paged_case(lens_q, lens_k, starts, 8, 2, d, page_size=64, seed=d + 3, device=DEV)
+    cv = synth.varlen_paged_case(lens_q, lens_k, starts, 8, 2, dv, page_size=64, seed=d + 3, device=DEV)
+    t = c.t
+    out, lse = pk.attn_fwd_varlen_paged(t["q"], t["k_pool"], cv.t["v_pool"], t["cu_seqlens_q"], t["seqlens_k"],
+                                        t["block_table"], c.meta["max_q"], kv_start=t["kv_start"], scale=c.scale,
+                                        causal=True)
+    assert out.shape[-1] == dv
+    kb = t["k_pool"].cpu().view(torch.int16).numpy()
+    vb = cv.t["v_pool"].cpu().view(torch.int16).numpy()
+    O, LSE = oracle.attention_varlen_paged(C.decode(t["q"], "bf16"), kb, vb, t["cu_seqlens_q"].cpu().numpy(),
+                                           t["seqlens_k"].cpu().numpy(), t["block_table"].cpu().numpy(), c.scale,
+                                           0.0, -1, 0, kv_start=t["kv_start"].cpu().numpy(), workers=8,
+                                           decode=(oracle.bf16_bits_to_f64, oracle.bf16_bits_to_f64))
+    C.assert_parity(out, lse.T, O, LSE.T, "bf16", f"varlen paged head_dim_v d={d} dv={dv}")
