@@ -97,7 +97,6 @@ __host__ __device__ inline int group_units(int n_qtiles) {
   return n_qtiles >= kGroupTiles ? 1 : kGroupTiles / n_qtiles;
 }
 
-
 template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   static_assert(!VT || (!FP8 && D == DV), "column-major V: bf16 with equal head dims");
@@ -286,7 +285,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     return FP8 ? (R / (256 / Tr::kKRow)) & (Tr::kKCh - 1) : swz(R, Tr::kKCh);
   };
   // Wave w fills LDS blocks w, w+4, ... (1 KiB each) of a tile; lane l of block q
-  // covers LDS bytes 1024 q + 16 l = (row R, slot s), fetching global chunk s ^ swz(R).
+  // covers LDS bytes 1024 q + 16 l = (row R, slot s), fetching global chunk s ^ kswz(R) of
+  // a K row (s ^ swz(R) of a V row).
   int koff[Tr::kKInstr], voff[Tr::kVInstr];
 #pragma unroll
   for (int i = 0; i < Tr::kKInstr; ++i) {
