@@ -149,8 +149,8 @@ typedef struct {
                           only; V's rows then have head_dim_v elements and O's rows too. The
                           paged entry points need v_pool_stride for it (the pools' rows differ). */
   int v_layout;        /* attn_v_layout_t. ATTN_V_COL_MAJOR (keys contiguous, v_stride[2] the
-                          stride between head-dim rows) is supported by attn_fwd on prefill
-                          shapes with BF16 inputs and head_dim_v = d; sk must be a multiple of 8
+                          stride between head-dim rows) is supported by attn_fwd (prefill and
+                          split-KV decode shapes) with BF16 inputs and head_dim_v = d; sk must be a multiple of 8
                           and (head_dim_v - 1) * v_stride[2] * 2 + 128 < 2^31. Keys past
                           seqused_k may hold any bits: they are never used. */
   int64_t v_pool_stride[3]; /* attn_fwd_paged / attn_fwd_varlen_paged: the V pool's {page, head,

@@ -110,7 +110,7 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
     contiguous). With ``cache_batch_idx`` (int32 [B] on the device) k / v are
     [C, Hkv, sk, d] caches and batch entry b reads entry cache_batch_idx[b]
     (an index outside [0, C) reads no keys). With ``v_colmajor`` v is
-    [B, Hkv, dv, sk] with keys contiguous (bf16 prefill shapes, dv = d).
+    [B, Hkv, dv, sk] with keys contiguous (bf16, dv = d, sk a multiple of 8).
     Returns (out [B, Hq, sq, dv], lse [B, Hq, sq] or None)."""
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]

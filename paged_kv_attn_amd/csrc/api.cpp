@@ -257,8 +257,6 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   if (p->v_layout == ATTN_V_COL_MAJOR) {
     if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "column-major V needs bf16 inputs");
     if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "column-major V needs head_dim_v = d");
-    if (takes_decode_path(p->in_dtype, sq, Hq / Hkv))
-      return fail(ATTN_ENOTSUP, "column-major V is not supported on the decode path (sq*Hq/Hkv <= 16)");
     if (sk % 8) return fail(ATTN_EINVAL, "column-major V needs sk a multiple of 8 (got %d)", sk);
     if ((int64_t)(d - 1) * v_stride[2] * 2 + 128 >= ((int64_t)1 << 31))
       return fail(ATTN_EINVAL, "column-major V: head-dim row stride too large");
@@ -300,6 +298,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.k_sb = k_stride[0]; a.k_sh = k_stride[1]; a.k_sr = k_stride[2];
     a.v_sb = v_stride[0]; a.v_sh = v_stride[1]; a.v_sr = v_stride[2];
     a.seqlens_k = seqused_k; a.seqused_q = seqused_q; a.block_table = nullptr; a.bt_stride = 0; a.page_size = 0;
+    a.v_colmajor = p->v_layout == ATTN_V_COL_MAJOR;
     a.sk = sk; a.sq = sq; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio; a.m_rows = m_rows;
     a.split_tokens = split; a.n_splits = nsp;
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;

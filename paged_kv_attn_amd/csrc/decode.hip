@@ -86,8 +86,14 @@ __device__ __forceinline__ float xor_shfl(float x, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ mask) << 2), __builtin_bit_cast(int, x)));
 }
 
-template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP, bool FP8>
+// Column-major V (keys contiguous): the granule's V^T sits in LDS as DV rows of
+// 32 keys (64 B); 16-byte chunk c of row R lives in slot c ^ vt_sw(R), so the 8-byte
+// operand reads of 16 rows x 2 halves fall in 32 different bank pairs.
+__device__ __forceinline__ int vt_sw(int row) { return (row >> 2) & 3; }
+
+template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP, bool FP8, bool VT>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+  static_assert(!VT || (!PAGED && !FP8), "column-major V: contiguous bf16 V only");
   using Tr = DTr<D, DV, FP8>;
   // One LDS object per pipeline buffer, so the compiler can tell the
   // HBM->LDS copies into one buffer from the reads of the other.
@@ -179,12 +185,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     if (FP8) {
       const int ch = 64 * q + lane, R = ch / (DV / 16), c8 = ch % (DV / 16);
       voff[q] = (int)(R * vrow) + 16 * c8;
+    } else if (VT) {  // block q: V^T rows 16 q .. 16 q + 15, lane l: row 16 q + l / 4, slot l % 4
+      const int R = 16 * q + (lane >> 2), kc = (lane & 3) ^ vt_sw(R);
+      voff[q] = (int)(R * vrow) + 16 * kc;
     } else {
       const int B = 1024 * q + 16 * lane;
       const int R = B / Tr::kVRow, sl = (B % Tr::kVRow) / 16;
       voff[q] = (int)(R * vrow) + 16 * (sl ^ vswz<DV>(R));
     }
   }
+  // column-major V: keys of chunk (lane & 3) ^ vt_sw(row) of this lane's load rows
+  const int vt_kc = VT ? (lane & 3) ^ vt_sw(lane >> 2) : 0;   // vt_sw(16 q + l / 4) = vt_sw(l / 4)
+  const char* const vt_head = VT ? (const char*)a.v + ((int64_t)kb * a.v_sb + (int64_t)g * a.v_sh) * 2 : nullptr;
   // K A-operand reads: lane (key 16 kb + L, group j4) takes K[key][32 st + 8 j4 .. +7],
   // chunk 4 st + j4 of row 16 kb + L, whose swizzle kswz(16 kb + L) = kswz(L) = ksw:
   // slot (4 st + j4) ^ ksw = ((4 st) ^ (ksw & ~3)) + ((j4 ^ ksw) & 3).
@@ -224,8 +236,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int gp = rows > 0 ? gs : t0;  // any valid page for an empty range
     const __amdgpu_buffer_rsrc_t kr =
         make_rsrc(rows_base(gp, a.k, a.k_sb, a.k_sh, a.k_sr), (uint32_t)(rows * krow));
+    // column-major V: the granule's 32-key span of every head-dim row; chunks of keys
+    // at or past the range get an offset beyond it and arrive as zeros
     const __amdgpu_buffer_rsrc_t vr =
-        make_rsrc(rows_base(gp, a.v, a.v_sb, a.v_sh, a.v_sr), (uint32_t)(rows * vrow));
+        VT ? make_rsrc(vt_head + 2 * (int64_t)gp, (uint32_t)((DV - 1) * vrow + 2 * kGran))
+           : make_rsrc(rows_base(gp, a.v, a.v_sb, a.v_sh, a.v_sr), (uint32_t)(rows * vrow));
 #pragma unroll
     for (int q = 0; q < Tr::kBlocks; ++q) buf_load16_lds_stream(kr, kb + 1024 * q, koff[q]);
     if (FP8) {
@@ -233,7 +248,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       for (int q = 0; q < Tr::kV8; ++q) v8[q] = buf_load16(vr, voff[q]);
     } else {
 #pragma unroll
-      for (int q = 0; q < Tr::kVBlocks; ++q) buf_load16_lds_stream(vr, vb + 1024 * q, voff[q]);
+      for (int q = 0; q < Tr::kVBlocks; ++q)
+        buf_load16_lds_stream(vr, vb + 1024 * q, (!VT || 8 * vt_kc < rows) ? voff[q] : 0x7FFFFFF0);
     }
   };
   // fp8 V of one granule: widen (exactly) to bf16 into the LDS layout of bf16 V
@@ -313,6 +329,19 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     // P^T as the B operand: slot 4 kb + r <-> key 16 kb + 4 j4 + r
     const U128 pu{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     const bf16x8 pb = as_bf16x8(pu);
+    if (VT) {
+      // V^T row 16 dblk + L holds the keys; slot 4 kb + r of the operand is key
+      // 16 kb + 4 j4 + r: bytes 32 kb + 8 j4 of the row, i.e. half j4 & 1 of chunk
+      // 2 kb + j4 / 2 (swizzle vt_sw(16 dblk + L) = vt_sw(L))
+      const int sw = vt_sw(L);
+      const int c0 = 16 * ((j4 >> 1) ^ sw) + 8 * (j4 & 1), c1 = 16 * ((2 + (j4 >> 1)) ^ sw) + 8 * (j4 & 1);
+#pragma unroll
+      for (int dblk = 0; dblk < Tr::kDBlocks; ++dblk) {
+        const lds_char* row = vb + (16 * dblk + L) * (2 * kGran);
+        acc[dblk] = mfma16_bf16(as_bf16x8(lds_load8(row + c0), lds_load8(row + c1)), pb, acc[dblk]);
+      }
+      return;
+    }
     int v_base = v_base0, v_hi = v_swhi;
     asm volatile("" : "+v"(v_base), "+v"(v_hi));
 #pragma unroll
@@ -323,6 +352,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       acc[dblk] = mfma16_bf16(as_bf16x8(v0, v1), pb, acc[dblk]);
     }
   };
+  // column-major V: the chunk holding key Lk - 1 also brought keys Lk .. (past the
+  // used length, possibly not finite); zero them in LDS before the products read them
+  auto vt_zero_tail = [&](int gs, lds_char* vb) {
+    const int cs = Lk & ~7;
+    if (VT && (Lk & 7) && cs >= gs && cs < gs + kGran && cs < t_hi) {
+      const int kc = (cs - gs) >> 3;
+      for (int R = lane; R < DV; R += 64) {
+        lds_char* row = vb + R * (2 * kGran) + 16 * (kc ^ vt_sw(R));
+        for (int e = Lk & 7; e < 8; ++e) *(__attribute__((address_space(3))) uint16_t*)(row + 2 * e) = 0;
+      }
+    }
+  };
 
   int gs = t_lo;
   if (gs < t_hi) {
@@ -331,12 +372,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       issue(gs + kGran, k1, v1, v8b);
       wait_vmem_le<Tr::kOps>();
       if (FP8) store_v8(v0, v8a);
+      vt_zero_tail(gs, v0);
       compute(gs, k0, v0);
       gs += kGran;
       if (gs >= t_hi) break;
       issue(gs + kGran, k0, v0, v8a);
       wait_vmem_le<Tr::kOps>();
       if (FP8) store_v8(v1, v8b);
+      vt_zero_tail(gs, v1);
       compute(gs, k1, v1);
       gs += kGran;
       if (gs >= t_hi) break;
@@ -447,8 +490,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_t s) {
   dim3 grid(a.hkv, a.n_splits, B);
-  if (a.fp8) hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false>), grid, dim3(64), 0, s, a);
+  if constexpr (!PAGED && D == DV) {
+    if (a.v_colmajor) {  // bf16 only (the host checks)
+      hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false, true>), grid, dim3(64), 0, s, a);
+    } else if (a.fp8) {
+      hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true, false>), grid, dim3(64), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false, false>), grid, dim3(64), 0, s, a);
+    }
+  } else {
+    if (a.v_colmajor) return hipErrorInvalidValue;  // contiguous V with head_dim_v = d only
+    if (a.fp8) hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true, false>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false, false>), grid, dim3(64), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)B * c.hq * c.sq;

@@ -68,6 +68,7 @@ struct DecodeArgs {
   int64_t v_sb, v_sh, v_sr;
   const int32_t* seqlens_k;   // per-request Lk (paged: required; contiguous: nullable)
   const int32_t* seqused_q;   // contiguous only, nullable: per-request used query rows Lq <= sq
+  int v_colmajor;             // contiguous bf16 V with keys contiguous: v_sr = head-dim row stride
   const int32_t* block_table; // paged only
   int64_t bt_stride;
   int page_size;

@@ -276,12 +276,13 @@ def test_v_layout_validation():
     assert _fwd(p) == 2 and "bf16" in _err()
     p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, head_dim_v=64)
     assert _fwd(p) == 2 and "head_dim_v" in _err()
-    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)             # decode shape: the same checks apply
     st = [32 * 128, 128, 128]
     kst = [8 * 4096 * 128, 4096 * 128, 128]
+    vst = [8 * 4096 * 128, 4096 * 128, 1 << 30]              # head-dim row stride too large for 32-bit offsets
     r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
-                       i64_array(kst), i64_array(kst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
-    assert r == 2 and "decode path" in _err()
+                       i64_array(kst), i64_array(vst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
+    assert r == 1 and "row stride too large" in _err()
 
 
 def _vpaged(p, page=64, kv_start=NULL, table=FAKE, d=128):
