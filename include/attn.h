@@ -165,8 +165,10 @@ typedef struct {
 void attn_params_init(attn_params_t* p, float scale);
 
 /*
- * Batch mode. Q [B, Hq, sq, d], K and V [B, Hkv, sk, d], O [B, Hq, sq, d],
- * each addressed as base + b*stride[0] + head*stride[1] + row*stride[2] + c.
+ * Batch mode. Q [B, Hq, sq, d], K [B, Hkv, sk, d], V [B, Hkv, sk, dv] and
+ * O [B, Hq, sq, dv] (dv = head_dim_v, default d), each addressed as
+ * base + b*stride[0] + head*stride[1] + row*stride[2] + c (column-major V: see
+ * v_layout).
  * lse (nullable) is a dense fp32 [B, Hq, sq] array.
  * seqused_q / seqused_k (nullable, int32 [B] on the device) give per-batch used
  * lengths Lq <= sq, Lk <= sk; NULL means Lq = sq, Lk = sk. Both the prefill and
@@ -205,10 +207,10 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Paged-KV mode. Q [B, Hq, sq, d] and O [B, Hq, sq, d] strided as in attn_fwd;
+ * Paged-KV mode. Q [B, Hq, sq, d] and O [B, Hq, sq, dv] strided as in attn_fwd;
  * K and V live in page pools of num_pages pages of page_size tokens,
  * addressed as pool + page*kv_stride[0] + head*kv_stride[1] + slot*kv_stride[2] + c
- * (64-bit offsets). Token t of request b is slot t % page_size of page
+ * (64-bit offsets; the V pool with v_pool_stride instead when that is set). Token t of request b is slot t % page_size of page
  * block_table[b*block_table_stride + t / page_size] (the page-block navigator
  * of the Composable Kernel page: block_table_ptr, batch_stride_block_table,
  * page_block_size). seqlens_k (int32 [B], device) gives Lk per request;
