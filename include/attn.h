@@ -189,8 +189,8 @@ attn_status_t attn_fwd(const attn_params_t* p,
 
 /*
  * Varlen (group) mode. n sequences packed along the token axis:
- * Q [total_q, Hq, d], K and V [total_k, Hkv, d], O [total_q, Hq, d], addressed
- * as base + token*stride[0] + head*stride[1] + c. Sequence s owns query tokens
+ * Q [total_q, Hq, d], K [total_k, Hkv, d], V [total_k, Hkv, dv], O [total_q, Hq, dv]
+ * (dv = head_dim_v, default d), addressed as base + token*stride[0] + head*stride[1] + c. Sequence s owns query tokens
  * cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and key tokens likewise
  * (int32 [n+1] device arrays, the seqstart_q/k pointers of the Composable Kernel
  * page's group-mode MakeKargs). max_seqlen_q / max_seqlen_k bound every
