@@ -4,8 +4,9 @@ One step = the whole hot path over one batch of synthetic input:
   * batch-mode causal prefill, bf16, B=4, H=16, s=2048, d=128 (scale 1/sqrt(d),
     bf16 O, fp32 LSE) -> TFLOP/s, the headline value;
   * paged-KV decode, bf16, 64 requests with context lengths ~ U[1024, 32768],
-    128-token pages in a randomly permuted pool, Hq=32, Hkv=8, d=128 (split-KV
-    kernel + combine) -> HBM GB/s.
+    128-token pages in a randomly permuted pool (each page stored head-major:
+    a kv-head's 128 slots contiguous), Hq=32, Hkv=8, d=128 (split-KV kernel +
+    combine) -> HBM GB/s.
 Inputs are generated on the GPU and resident in HBM before timing. Each launch
 is bracketed by HIP events (device-scope release) on the stream the library
 enqueues on; values are
@@ -281,7 +282,8 @@ def main():
         "cpu_baseline": cpu,
         "paged_decode": {
             "value": round(gbs, 1), "unit": "GB/s",
-            "workload": "bf16 paged decode, 64 requests L~U[1024,32768], page 128, Hq=32 Hkv=8 d=128, sq=1",
+            "workload": "bf16 paged decode, 64 requests L~U[1024,32768], page 128 (head-major pages), Hq=32 Hkv=8 "
+                        "d=128, sq=1",
             "launch_us": round(dec_ms * 1e3, 2), "min_us": round(t_dec[0] * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),

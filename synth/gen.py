@@ -131,7 +131,7 @@ def varlen_case(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, causal=True, s
 
 def paged_case(lens_k, sq, Hq, Hkv, d, page_size=128, dtype="bf16", seed=0, causal=False,
                softcap=0.0, window=None, scale=None, device="cpu", table_width=None,
-               permute=True, rng=None) -> Case:
+               permute=True, rng=None, head_major=False) -> Case:
     """Paged KV: pools [N, page_size, Hkv, d]; block_table [B, W] int32;
     seqlens_k [B] int32; Q [B, Hq, sq, d].
 
@@ -139,7 +139,10 @@ def paged_case(lens_k, sq, Hq, Hkv, d, page_size=128, dtype="bf16", seed=0, caus
     sum(n_r) real pages plus one NaN-filled guard page (the last id). Real page
     ids are a seeded permutation (identity if ``permute`` is False) dealt out in
     request order; unused table entries point at the guard page; slots past L_r
-    in a request's last page are NaN.
+    in a request's last page are NaN. The pools are always viewed as
+    [N, page_size, Hkv, d]; with ``head_major`` their storage is
+    [N, Hkv, page_size, d] (each kv-head's slots of a page contiguous), the same
+    values drawn in the same order.
     """
     lens_k = [int(x) for x in lens_k]
     B = len(lens_k)
@@ -168,6 +171,9 @@ def paged_case(lens_k, sq, Hq, Hkv, d, page_size=128, dtype="bf16", seed=0, caus
                 last = int(table[r, n_pages[r] - 1])
                 kp[last, L % page_size:] = float("nan")
                 vp[last, L % page_size:] = float("nan")
+    if head_major:
+        kp = kp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        vp = vp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     t = {"q": q, "k_pool": kp, "v_pool": vp,
          "block_table": torch.from_numpy(table).to(device),
          "seqlens_k": torch.tensor(lens_k, dtype=torch.int32, device=device)}
@@ -274,7 +280,7 @@ def workload(n: int, device="cpu") -> Case:
         rng = np.random.Generator(np.random.PCG64(seed))
         lens = rng.integers(1024, 32768, size=64, endpoint=True)
         return paged_case(lens, 1, 32, 8, 128, 128, "bf16", seed, causal=False, device=device,
-                          table_width=256, rng=rng)
+                          table_width=256, rng=rng, head_major=True)
     if n == 5:
         return dense_case(2, 16, 16, 16384, 16384, 128, "fp8", seed, causal=True, softcap=30.0,
                           device=device)

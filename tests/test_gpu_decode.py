@@ -138,3 +138,19 @@ def test_contiguous_decode_seqused_q(dtype, window):
     C.assert_parity(out, lse, O, LSE, dtype, f"decode seqused_q {dtype} window={window}")
     for b, lq in enumerate(su_q):
         assert (out[b, :, lq:] == 7.0).all() and (lse[b, :, lq:] == 7.0).all(), "rows >= Lq were written"
+
+
+@pytest.mark.parametrize("sq,split", [(1, 0), (1, 64), (200, 0)])
+def test_head_major_pages_bitexact_vs_slot_major(sq, split):
+    """The same pool stored [page, slot, head, d] and [page, head, slot, d] (one
+    logical view, different strides) gives identical bits, decode and paged prefill."""
+    kw = dict(causal=sq > 1)
+    a = synth.paged_case([2000, 129, 700], sq, 16, 4, 128, 128, "bf16", seed=31 + sq, device=DEV, **kw)
+    b = synth.paged_case([2000, 129, 700], sq, 16, 4, 128, 128, "bf16", seed=31 + sq, device=DEV,
+                         head_major=True, **kw)
+    assert b.t["k_pool"].stride(1) == 128 and torch.equal(C.bits(a.t["k_pool"]), C.bits(b.t["k_pool"]))
+    oa, la = C.run_paged(a, kv_split_tokens=split)
+    ob, lb = C.run_paged(b, kv_split_tokens=split)
+    assert torch.equal(C.bits(oa), C.bits(ob)) and torch.equal(C.bits(la), C.bits(lb))
+    O, LSE = C.oracle_paged(b)
+    C.assert_parity(ob, lb, O, LSE, "bf16", f"head-major pages sq={sq}")
