@@ -19,7 +19,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "f32.hip"]
+# (source, object, extra defines): the prefill kernel's instantiations compile
+# in four parts, one per (input type, head dim), in parallel
+SOURCES = [("api.cpp", "api", []), ("decode.hip", "decode", []), ("f32.hip", "f32", [])] + \
+    [("prefill.hip", f"prefill_p{k}", [f"-DATTN_PREFILL_PART={k}"]) for k in range(4)]
 # Per-source code-generation options. The decode kernel keeps its MFMA
 # accumulators in ordinary VGPRs: its online-softmax rescale touches them
 # between matrix ops, and accumulation registers would cost a copy each way.
@@ -38,9 +41,10 @@ def _flags():
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, name, defines = job
+    obj = os.path.join(OBJ, name + ".o")
+    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln)

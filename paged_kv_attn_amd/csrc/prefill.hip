@@ -816,26 +816,59 @@ hipError_t launch_f(const PrefillArgs& a, int mode, int nz, bool mask, bool soft
   return launch_m<D, DV, FP8, kPrefillBatch>(a, nz, mask, softcap, s);
 }
 
-template <int D, int DV>
-hipError_t launch_d(const PrefillArgs& a, int in_type, int mode, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (in_type == kInFP8) return launch_f<D, DV, true>(a, mode, nz, mask, softcap, s);
-  return launch_f<D, DV, false>(a, mode, nz, mask, softcap, s);
+
+// One (input type, d) combination per part, both head_dim_v values each. The
+// build compiles this file once per part (ATTN_PREFILL_PART = 0..3) so the
+// instantiations compile in parallel; without the macro one object holds all.
+template <int D, bool FP8>
+hipError_t launch_part(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
+  const bool mask = a.wl >= 0 || a.wr >= 0;
+  const bool softcap = a.softcap_pre != 0.0f;
+  if (dv == 64) return launch_f<D, 64, FP8>(a, mode, nz, mask, softcap, s);
+  return launch_f<D, 128, FP8>(a, mode, nz, mask, softcap, s);
 }
 
 }  // namespace
 
+#if !defined(ATTN_PREFILL_PART)
+#define ATTN_PREFILL_ALL 1
+#define ATTN_PREFILL_PART -1
+#endif
+
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 0
+hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
+  return launch_part<128, false>(a, dv, mode, nz, s);
+}
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 1
+hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
+  return launch_part<64, false>(a, dv, mode, nz, s);
+}
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 2
+hipError_t launch_prefill_fp8_d128(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
+  return launch_part<128, true>(a, dv, mode, nz, s);
+}
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 3
+hipError_t launch_prefill_fp8_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
+  return launch_part<64, true>(a, dv, mode, nz, s);
+}
+#endif
+
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 0
+hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_fp8_d128(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_fp8_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
+
 int prefill_rows_per_tile(int) { return kBlockM; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int nz, hipStream_t stream) {
-  const bool mask = a.wl >= 0 || a.wr >= 0;
-  const bool softcap = a.softcap_pre != 0.0f;
   if (a.n_qtiles <= 0 || nz <= 0 || a.hkv <= 0) return hipSuccess;
-  if (d == 128) {
-    if (dv == 64) return launch_d<128, 64>(a, in_type, mode, nz, mask, softcap, stream);
-    return launch_d<128, 128>(a, in_type, mode, nz, mask, softcap, stream);
-  }
-  if (dv == 128) return launch_d<64, 128>(a, in_type, mode, nz, mask, softcap, stream);
-  return launch_d<64, 64>(a, in_type, mode, nz, mask, softcap, stream);
+  if (in_type == kInFP8)
+    return d == 128 ? launch_prefill_fp8_d128(a, dv, mode, nz, stream) : launch_prefill_fp8_d64(a, dv, mode, nz, stream);
+  return d == 128 ? launch_prefill_bf16_d128(a, dv, mode, nz, stream) : launch_prefill_bf16_d64(a, dv, mode, nz, stream);
 }
+#endif
 
 }  // namespace attn
