@@ -176,6 +176,54 @@ def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
                       f"value = those heads' algorithmic (causal) flops / time"}
 
 
+def time_workload(n: int, steps: int, warmup: int) -> None:
+    """Time one of the other prefill workloads alone (for its kernel-trace
+    summary): 3 = varlen GQA causal (8 sequences of 256..8192, Hq=32, Hkv=8),
+    5 = fp8 causal with soft-cap 30 (B=2, H=16, s=16384). Algorithmic flops =
+    4 d per visible (query, key) pair per q-head."""
+    import torch
+    import paged_kv_attn_amd as pk
+    import synth
+    case = synth.workload(n, "cuda")
+    t, m = case.t, case.meta
+    if n == 3:
+        lens = (t["cu_seqlens_q"][1:] - t["cu_seqlens_q"][:-1]).tolist()
+        flops = sum(4.0 * m["d"] * L * (L + 1) / 2 * m["Hq"] for L in lens)
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((m["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
+
+        def run():
+            pk.attn_fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens_q"], t["cu_seqlens_k"], m["max_q"], m["max_k"],
+                               scale=case.scale, causal=True, out=o, lse=lse)
+        name = "bf16 varlen GQA causal prefill, 8 sequences L~U[256,8192], Hq=32 Hkv=8 d=128"
+    else:
+        S = m["sq"]
+        flops = 4.0 * m["d"] * S * (S + 1) / 2 * m["B"] * m["Hq"]
+        o = torch.empty(t["q"].shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda")
+        ds = case.descale
+
+        def run():
+            pk.attn_fwd(t["q"], t["k"], t["v"], scale=case.scale, causal=True, softcap=case.softcap,
+                        descale=(ds["q"], ds["k"], ds["v"]), out=o, lse=lse)
+        name = "fp8 (E4M3FN) causal prefill, soft-cap 30, B=2 H=16 sq=sk=16384 d=128, bf16 O"
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = HipEvents(2 * steps, torch.cuda.current_stream().cuda_stream)
+    for i in range(steps):
+        ev.record(2 * i)
+        run()
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    ts = sorted(ev.ms(2 * i, 2 * i + 1) for i in range(steps))
+    ev.close()
+    mean = sum(ts) / len(ts)
+    print(json.dumps({"workload": name, "metric": "TFLOP/s", "value": round(flops / (mean * 1e-3) / 1e12, 2),
+                      "launch_us": round(mean * 1e3, 2), "min_us": round(ts[0] * 1e3, 2), "steps": steps,
+                      "algorithmic_flops": flops}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +232,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--decode-split", type=int, default=0, help="keys per split-KV unit (0 = library default)")
+    ap.add_argument("--workload", type=int, default=0, choices=[0, 3, 5],
+                    help="only time workload 3 (varlen GQA prefill) or 5 (fp8 soft-cap prefill) and print its line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -194,6 +244,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload:
+        time_workload(args.workload, args.steps, args.warmup)
         return
 
     import torch
