@@ -4,7 +4,8 @@ Each case draws one combination: the mode (batch, varlen, paged, varlen over a
 paged pool), bf16 or fp8 inputs, d and head_dim_v from {64, 128}, the GQA ratio,
 ragged lengths on either side of the decode/prefill dispatch boundary, the
 mask (none, causal, two-sided window), the logit soft-cap, attention sinks
-(streaming sink keys and per-head sink logits) and ALiBi slopes. The per-option
+(streaming sink keys and per-head sink logits), ALiBi slopes, head-major page
+storage and column-major V. The per-option
 tests pin each option alone; these catch interactions between them."""
 
 import numpy as np
@@ -33,6 +34,8 @@ def _draw(seed):
     o["sink_size"] = int(r.choice([0, 0, 4, 33]))
     o["sinks"] = r.uniform(-3, 3, size=o["hkv"] * o["ratio"]) if r.random() < 0.4 else None
     o["alibi"] = r.uniform(0.0, 0.08, size=o["hkv"] * o["ratio"]) if r.random() < 0.3 else None
+    o["head_major"] = bool(r.random() < 0.5)      # paged: pool pages stored [Hkv, P, d]
+    o["colmajor"] = bool(r.random() < 0.3)        # batch, bf16, dv == d: V stored [B, Hkv, d, sk]
     o["rng"] = r
     return o
 
@@ -62,16 +65,26 @@ def test_random_option_mix(seed):
     sq_max = max(1, 16 // o["ratio"]) if o["decode"] else int(r.integers(17, 260))
     gpu, ref = _extras(o)
     what = f"seed {seed}: {o['mode']} {dtype} d={d} dv={dv} Hq={hq} Hkv={hkv} sq<={sq_max} " \
+           f"head_major={o['head_major']} colmajor={o['colmajor']} " \
            f"causal={o['causal']} window={o['window']} cap={o['softcap']} sinks={o['sink_size']}," \
            f"{o['sinks'] is not None} alibi={o['alibi'] is not None}"
     if o["mode"] == "batch":
         B = int(r.integers(1, 4))
         sk = int(r.integers(1, 700))
+        colmajor = o["colmajor"] and dtype == "bf16" and dv == d
+        if colmajor:
+            sk = 8 * max(1, sk // 8)
         c = synth.dense_case(B, hq, hkv, sq_max, sk, d, dtype, seed=seed, device=DEV, **_mask(o))
         if dv != d:
             cv = synth.dense_case(B, hq, hkv, sq_max, sk, dv, dtype, seed=seed + 1, device=DEV, **_mask(o))
             c.t["v"], c.descale["v"] = cv.t["v"], cv.descale["v"]
-        out, lse = C.run_dense(c, **gpu)
+        if colmajor:
+            t = c.t
+            out, lse = pk.attn_fwd(t["q"], t["k"], t["v"].transpose(2, 3).contiguous(), scale=c.scale,
+                                   window=(c.window_left, c.window_right), softcap=c.softcap, v_colmajor=True,
+                                   **gpu)
+        else:
+            out, lse = C.run_dense(c, **gpu)
         O, LSE = C.oracle_dense(c, **ref)
         C.assert_parity(out, lse, O, LSE, dtype, what)
     elif o["mode"] == "varlen":
@@ -91,9 +104,12 @@ def test_random_option_mix(seed):
         B = int(r.integers(1, 4))
         lens = [int(x) for x in r.integers(0, 900, size=B)]
         page = int(r.choice([32, 64, 128])) if o["decode"] else int(r.choice([64, 128]))
-        c = synth.paged_case(lens, sq_max, hq, hkv, d, page, dtype, seed=seed, device=DEV, **_mask(o))
+        hm = o["head_major"]
+        c = synth.paged_case(lens, sq_max, hq, hkv, d, page, dtype, seed=seed, device=DEV, head_major=hm,
+                             **_mask(o))
         if dv != d:
-            cv = synth.paged_case(lens, sq_max, hq, hkv, dv, page, dtype, seed=seed, device=DEV, **_mask(o))
+            cv = synth.paged_case(lens, sq_max, hq, hkv, dv, page, dtype, seed=seed, device=DEV, head_major=hm,
+                                  **_mask(o))
             c.t["v_pool"], c.descale["v"] = cv.t["v_pool"], cv.descale["v"]
         out, lse = C.run_paged(c, kv_split_tokens=int(r.choice([0, 64, 256])), **gpu)
         O, LSE = C.oracle_paged(c, **ref)
