@@ -185,13 +185,14 @@ def paged_case(lens_k, sq, Hq, Hkv, d, page_size=128, dtype="bf16", seed=0, caus
 
 
 def varlen_paged_case(lens_q, lens_k, starts, Hq, Hkv, d, page_size=64, dtype="bf16", seed=0, causal=True,
-                      softcap=0.0, window=None, scale=None, device="cpu") -> Case:
+                      softcap=0.0, window=None, scale=None, device="cpu", head_major=False) -> Case:
     """Group mode over a paged pool: Q [Tq, Hq, d] packed by cu_seqlens_q;
     sequence s reads lens_k[s] keys starting at logical token starts[s] of its
     block-table row (kv_start). Request s owns ceil((starts[s] + lens_k[s]) / P)
     pages dealt from a seeded permutation; every slot outside
     [starts[s], starts[s] + lens_k[s]) and a guard page (the last id, filling
-    unused table entries) are NaN (bf16 only)."""
+    unused table entries) are NaN (bf16 only). With ``head_major`` the pools'
+    storage is [N, Hkv, P, d] (same values, as in paged_case)."""
     lens_q = [int(x) for x in lens_q]
     lens_k = [int(x) for x in lens_k]
     starts = [int(x) for x in starts]
@@ -226,6 +227,9 @@ def varlen_paged_case(lens_q, lens_k, starts, Hq, Hkv, d, page_size=64, dtype="b
                     if b_ > a_:
                         kp[page, a_:b_] = float("nan")
                         vp[page, a_:b_] = float("nan")
+    if head_major:
+        kp = kp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        vp = vp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     t = {"q": q, "k_pool": kp, "v_pool": vp,
          "block_table": torch.from_numpy(table).to(device),
          "seqlens_k": torch.tensor(lens_k, dtype=torch.int32, device=device),

@@ -19,7 +19,7 @@ from tests import _cases as C
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 128
+N_CASES = 512
 
 
 def _draw(seed):
@@ -120,13 +120,14 @@ def test_random_option_mix(seed):
         lk = [int(x) for x in r.integers(0, 500, size=n)]
         starts = [int(x) for x in r.integers(0, 200, size=n)]
         page = int(r.choice([64, 128]))
+        hm = o["head_major"]
         c = synth.varlen_paged_case(lq, lk, starts, hq, hkv, d, page_size=page, dtype=dtype, seed=seed, device=DEV,
-                                    **_mask(o))
+                                    head_major=hm, **_mask(o))
         vp = c.t["v_pool"]
         dsv = c.descale["v"]
         if dv != d:
             cv = synth.varlen_paged_case(lq, lk, starts, hq, hkv, dv, page_size=page, dtype=dtype, seed=seed,
-                                         device=DEV, **_mask(o))
+                                         device=DEV, head_major=hm, **_mask(o))
             vp, dsv = cv.t["v_pool"], cv.descale["v"]
         t, ds = c.t, c.descale
         out, lse = pk.attn_fwd_varlen_paged(t["q"], t["k_pool"], vp, t["cu_seqlens_q"], t["seqlens_k"],
