@@ -51,6 +51,18 @@
  *   - Device-resident metadata (seqused, cu_seqlens, seqlens_k, block tables)
  *     is a precondition: monotone, in range, page ids < num_pages. Violating it
  *     is undefined behaviour (it is not checked on the device).
+ *     With the environment variable ATTN_VALIDATE set (to anything but "" or
+ *     "0", read on every call) each call first waits for its stream, copies
+ *     that metadata to the host and checks it:
+ *       seqused_q/k within [0, sq] / [0, sk] (cache_batch_idx may hold any
+ *       index, see attn_params_t);
+ *       cu_seqlens starting >= 0 and non-decreasing, every length within
+ *       max_seqlen_q / max_seqlen_k, cu_seqlens_q[n] <= total_q;
+ *       seqlens_k, and kv_start + seqlens_k, within block_table_stride *
+ *       page_size;
+ *       every block-table entry that a used key falls in within [0, num_pages).
+ *     A violation returns ATTN_EINVAL with no launch. The check synchronises,
+ *     so it is a debugging aid, not for graph capture.
  *   - Results are deterministic: the same call gives the same bits. Calls that
  *     differ only in addressing (paged vs contiguous KV with the same logical
  *     contents and the same split size; varlen vs padded batch with seqused)

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "kernels.hpp"
@@ -188,6 +189,71 @@ attn_status_t launched(hipError_t e) {
     if (st_ != ATTN_OK) return st_;  \
   } while (0)
 
+// ---- optional host-side check of device-resident metadata (ATTN_VALIDATE) ----
+// Read per call, so a process can switch it on and off. It synchronises the
+// stream, so it is a debugging aid, not for graph capture or serving loops.
+bool validate_on() {
+  const char* e = getenv("ATTN_VALIDATE");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+// Waits for the stream (whose earlier work may still write the array), then
+// copies count int32 from dev (device or host memory) into out.
+attn_status_t fetch_i32(const char* name, const int32_t* dev, size_t count, hipStream_t s, std::vector<int32_t>& out) {
+  out.assign(count, 0);
+  if (count == 0) return ATTN_OK;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(out.data(), dev, count * sizeof(int32_t), hipMemcpyDefault);
+  if (e != hipSuccess) return fail(ATTN_EINVAL, "ATTN_VALIDATE: cannot read %s: %s", name, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+// per-entry values 0 <= x <= hi (an absent array: nothing to check); the values are returned in h
+attn_status_t validate_range(const char* name, const int32_t* dev, int count, int hi, hipStream_t s,
+                             std::vector<int32_t>& h) {
+  if (!dev) return ATTN_OK;
+  TRY(fetch_i32(name, dev, (size_t)count, s, h));
+  for (int i = 0; i < count; ++i)
+    if (h[i] < 0 || h[i] > hi) return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s[%d] = %d is outside [0, %d]", name, i, h[i], hi);
+  return ATTN_OK;
+}
+
+// cu[0] >= 0, non-decreasing, every length <= max_len, cu[n] <= total (total < 0: unbounded)
+attn_status_t validate_cu(const char* name, const int32_t* dev, int n, int max_len, int64_t total, hipStream_t s) {
+  std::vector<int32_t> h;
+  TRY(fetch_i32(name, dev, (size_t)n + 1, s, h));
+  if (h[0] < 0) return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s[0] = %d is negative", name, h[0]);
+  for (int i = 0; i < n; ++i) {
+    const int64_t l = (int64_t)h[i + 1] - h[i];
+    if (l < 0) return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s decreases at entry %d (%d -> %d)", name, i, h[i], h[i + 1]);
+    if (l > max_len)
+      return fail(ATTN_EINVAL, "ATTN_VALIDATE: sequence %d of %s has length %lld > its maximum %d", i, name, (long long)l,
+                  max_len);
+  }
+  if (total >= 0 && h[n] > total)
+    return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s[%d] = %d exceeds %lld", name, n, h[n], (long long)total);
+  return ATTN_OK;
+}
+
+// page ids of the tokens [first[r], first[r] + count[r]) of each table row r
+// lie in [0, num_pages); a row with count 0, or first < 0 (not computed), uses no entry
+attn_status_t validate_pages(const int32_t* table_dev, int rows, int stride, int page_size, int num_pages,
+                             const std::vector<int32_t>& first, const std::vector<int32_t>& count, hipStream_t s) {
+  std::vector<int32_t> t;
+  TRY(fetch_i32("block_table", table_dev, (size_t)rows * stride, s, t));
+  for (int r = 0; r < rows; ++r) {
+    if (count[r] <= 0 || first[r] < 0) continue;
+    const int64_t end = (int64_t)first[r] + count[r];
+    for (int64_t i = first[r] / page_size; i < (end + page_size - 1) / page_size; ++i) {
+      const int32_t id = t[(size_t)r * stride + i];
+      if (id < 0 || id >= num_pages)
+        return fail(ATTN_EINVAL, "ATTN_VALIDATE: block_table[%d][%lld] = %d is not a page id in [0, %d)", r,
+                    (long long)i, id, num_pages);
+    }
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,6 +330,11 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   if (B == 0 || sq == 0) return ATTN_OK;
   const int ratio = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
+  if (validate_on()) {
+    std::vector<int32_t> h;
+    TRY(validate_range("seqused_q", seqused_q, B, sq, s, h));
+    TRY(validate_range("seqused_k", seqused_k, B, sk, s, h));
+  }
   float c_exp2, pre, post;
   logit_consts(p, &c_exp2, &pre, &post);
 
@@ -379,6 +450,10 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   TRY(check_strides("v", v_stride, 2, eb));
   TRY(check_strides("o", o_stride, 2, ob));
   if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
+  if (validate_on()) {
+    TRY(validate_cu("cu_seqlens_q", cu_seqlens_q, n, max_seqlen_q, total_q, (hipStream_t)stream));
+    TRY(validate_cu("cu_seqlens_k", cu_seqlens_k, n, max_seqlen_k, -1, (hipStream_t)stream));
+  }
   float c_exp2, pre, post;
   logit_consts(p, &c_exp2, &pre, &post);
   const int ratio = Hq / Hkv;
@@ -441,6 +516,12 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
   const int max_len = (int)max_len64;
+  if (validate_on()) {
+    std::vector<int32_t> lk;
+    TRY(validate_range("seqlens_k", seqlens_k, B, max_len, (hipStream_t)stream, lk));
+    TRY(validate_pages(block_table, B, block_table_stride, page_size, num_pages, std::vector<int32_t>(B, 0), lk,
+                       (hipStream_t)stream));
+  }
   float c_exp2, pre, post;
   logit_consts(p, &c_exp2, &pre, &post);
 
@@ -539,6 +620,22 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
+  if (validate_on()) {
+    hipStream_t vs = (hipStream_t)stream;
+    std::vector<int32_t> lk, st;
+    TRY(validate_cu("cu_seqlens_q", cu_seqlens_q, n, max_seqlen_q, total_q, vs));
+    TRY(validate_range("seqlens_k", seqlens_k, n, (int)max_len64, vs, lk));
+    if (kv_start) {
+      TRY(fetch_i32("kv_start", kv_start, (size_t)n, vs, st));
+    } else {
+      st.assign(n, 0);
+    }
+    for (int i = 0; i < n; ++i)
+      if (st[i] >= 0 && (int64_t)st[i] + lk[i] > max_len64)
+        return fail(ATTN_EINVAL, "ATTN_VALIDATE: kv_start[%d] + seqlens_k[%d] = %lld exceeds the table row (%lld tokens)",
+                    i, i, (long long)st[i] + lk[i], (long long)max_len64);
+    TRY(validate_pages(block_table, n, block_table_stride, page_size, num_pages, st, lk, vs));
+  }
   float c_exp2, pre, post;
   logit_consts(p, &c_exp2, &pre, &post);
   const int ratio = Hq / Hkv;
