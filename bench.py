@@ -170,7 +170,14 @@ def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
                 break
     dt /= reps
     flops = prefill_flops(case) * n / (m["B"] * m["Hq"])
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model,
             "sample": f"fp64 oracle on {n} of {m['B'] * m['Hq']} (batch, head) pairs of the prefill workload, "
                       f"{dt:.3f} s per pass (mean of {reps} passes) on {cores} threads, one BLAS thread each; "
                       f"value = those heads' algorithmic (causal) flops / time"}
@@ -227,7 +234,7 @@ def time_workload(n: int, steps: int, warmup: int) -> None:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
@@ -298,6 +305,7 @@ def main():
     t_dec = sorted(ev.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps))
     ev.close()
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    median = lambda xs: 0.5 * (xs[(len(xs) - 1) // 2] + xs[len(xs) // 2])  # noqa: E731  (xs sorted)
     pre_ms, dec_ms = mean(t_pre), mean(t_dec)
     flops = prefill_flops(pre)
     dbytes = decode_bytes(dec)
@@ -331,13 +339,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "prefill_kernel<128, bf16, batch, causal>", "launch_us": round(pre_ms * 1e3, 2),
+                     "median_us": round(median(t_pre) * 1e3, 2), "min_us": round(t_pre[0] * 1e3, 2),
                      "algorithmic_flops": flops},
         "cpu_baseline": cpu,
         "paged_decode": {
             "value": round(gbs, 1), "unit": "GB/s",
             "workload": "bf16 paged decode, 64 requests L~U[1024,32768], page 128 (head-major pages), Hq=32 Hkv=8 "
                         "d=128, sq=1",
-            "launch_us": round(dec_ms * 1e3, 2), "min_us": round(t_dec[0] * 1e3, 2),
+            "launch_us": round(dec_ms * 1e3, 2), "median_us": round(median(t_dec) * 1e3, 2),
+            "min_us": round(t_dec[0] * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
                          "kernel": "decode_kernel<128, 128, paged> + combine_kernel", "algorithmic_bytes": dbytes},
