@@ -184,16 +184,25 @@ def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
 
 
 def time_workload(n: int, steps: int, warmup: int) -> None:
-    """Time one of the other prefill workloads alone (for its kernel-trace
-    summary): 3 = varlen GQA causal (8 sequences of 256..8192, Hq=32, Hkv=8),
-    5 = fp8 causal with soft-cap 30 (B=2, H=16, s=16384). Algorithmic flops =
-    4 d per visible (query, key) pair per q-head."""
+    """Time one of the other workloads alone (for its kernel-trace summary):
+    1 = tiny fp32 attention (B=1, H=2, s=128, d=64; launch latency, too small
+    for a roofline), 3 = varlen GQA causal (8 sequences of 256..8192, Hq=32,
+    Hkv=8), 5 = fp8 causal with soft-cap 30 (B=2, H=16, s=16384). Algorithmic
+    flops = 4 d per visible (query, key) pair per q-head."""
     import torch
     import paged_kv_attn_amd as pk
     import synth
     case = synth.workload(n, "cuda")
     t, m = case.t, case.meta
-    if n == 3:
+    if n == 1:
+        flops = 4.0 * m["d"] * m["sq"] * m["sk"] * m["B"] * m["Hq"]
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda")
+
+        def run():
+            pk.attn_fwd(t["q"], t["k"], t["v"], scale=case.scale, out=o, lse=lse)
+        name = "fp32 attention, B=1 H=2 sq=sk=128 d=64, no mask (launch latency)"
+    elif n == 3:
         lens = (t["cu_seqlens_q"][1:] - t["cu_seqlens_q"][:-1]).tolist()
         flops = sum(4.0 * m["d"] * L * (L + 1) / 2 * m["Hq"] for L in lens)
         o = torch.empty_like(t["q"])
@@ -226,9 +235,10 @@ def time_workload(n: int, steps: int, warmup: int) -> None:
     ts = sorted(ev.ms(2 * i, 2 * i + 1) for i in range(steps))
     ev.close()
     mean = sum(ts) / len(ts)
+    median = 0.5 * (ts[(len(ts) - 1) // 2] + ts[len(ts) // 2])
     print(json.dumps({"workload": name, "metric": "TFLOP/s", "value": round(flops / (mean * 1e-3) / 1e12, 2),
-                      "launch_us": round(mean * 1e3, 2), "min_us": round(ts[0] * 1e3, 2), "steps": steps,
-                      "algorithmic_flops": flops}), flush=True)
+                      "launch_us": round(mean * 1e3, 2), "median_us": round(median * 1e3, 2),
+                      "min_us": round(ts[0] * 1e3, 2), "steps": steps, "algorithmic_flops": flops}), flush=True)
 
 
 def main():
@@ -239,8 +249,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--decode-split", type=int, default=0, help="keys per split-KV unit (0 = library default)")
-    ap.add_argument("--workload", type=int, default=0, choices=[0, 3, 5],
-                    help="only time workload 3 (varlen GQA prefill) or 5 (fp8 soft-cap prefill) and print its line")
+    ap.add_argument("--workload", type=int, default=0, choices=[0, 1, 3, 5],
+                    help="only time workload 1 (tiny fp32, latency), 3 (varlen GQA prefill) or 5 (fp8 soft-cap "
+                         "prefill) and print its line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()

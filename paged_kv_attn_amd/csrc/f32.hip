@@ -2,12 +2,15 @@
 // and an fp32 result are wanted (the FP32 data type of the Composable Kernel
 // page "fmha_fwd_pagedkv_kernel.hpp Source File").
 //
-// Vector-ALU kernel: each query row is owned by D/64 lanes (64 d-values each),
-// holding its q slice and O accumulator in registers. K/V tiles of 32 keys are
-// staged in LDS with 128-bit loads and read back as broadcasts (every lane of
-// a row group reads the same key row). Per tile: the 32 logits, soft-cap and
-// mask, tile max, one rescale of O and l by alpha = exp(m_old - m_new), then
-// O += p_j V_j (the FlashAttention-2 loop of the CUDA-Learn-Notes page
+// Vector-ALU kernel: each query row is owned by the 16 lanes of one DPP row,
+// each holding D/16 d-values of q and of the O accumulator in registers, so a
+// small problem still spreads over many workgroups and short per-lane loops.
+// K/V tiles of 32 keys are staged in LDS with 128-bit loads; the four query
+// rows of a wave read the same key row (broadcast). Per key, the lanes' partial
+// dot products are summed across the 16 lanes by four DPP adds (every lane
+// ends with the same bits). Per tile: the 32 logits, soft-cap and mask, tile
+// max, one rescale of O and l by alpha = exp(m_old - m_new), then O += p_j V_j
+// (the FlashAttention-2 loop of the CUDA-Learn-Notes page
 // "flash_attn_mma_share_kv_F32F16F16F32.cu", without matrix cores).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -15,18 +18,35 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;
 constexpr int kTileN = 32;
+constexpr int kLPR = 16;                  // lanes per query row: one DPP row
+constexpr int kRows = kThreads / kLPR;    // query rows per workgroup
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; each step adds a symmetric partner, so
+// every lane of the row holds the same bits afterwards.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane i ^ 1
+  x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane i ^ 2
+  x += dpp_mov<0x141>(x);  // row_half_mirror: lane 7 - i within 8
+  x += dpp_mov<0x140>(x);  // row_mirror: lane 15 - i within 16
+  return x;
+}
 
 template <int D, bool MASK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
-  constexpr int LPR = D / 64;              // lanes per query row
-  constexpr int ROWS = kThreads / LPR;     // query rows per workgroup
+  constexpr int DPL = D / kLPR;           // d-values per lane
+  constexpr int ROWS = kRows;
   __shared__ __attribute__((aligned(16))) float ks[kTileN * D];
   __shared__ __attribute__((aligned(16))) float vs[kTileN * D];
 
   const int tid = threadIdx.x;
-  const int part = tid % LPR;
+  const int part = tid % kLPR;
   const int bh = blockIdx.y;
   const int b = bh / a.hq, hq = bh % a.hq;
   const int g = hq / a.ratio;
@@ -34,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
   const int Lk = a.seqused_k ? a.seqused_k[b] : a.sk;
   const int r0 = blockIdx.x * ROWS;
   if (r0 >= Lq) return;
-  const int row = r0 + tid / LPR;
+  const int row = r0 + tid / kLPR;
   const bool row_ok = row < Lq;
   const int off = Lk - Lq;
   const int rmax = min(r0 + ROWS, Lq) - 1;
@@ -45,13 +65,15 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
     if (a.wr >= 0) { j_hi = min(Lk, rmax + off + a.wr + 1); lim_hi = min(Lk - 1, row + off + a.wr); }
   }
 
-  float q[64], o[64];
-  const float* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_sr + part * 64;
+  float q[DPL], o[DPL];
+  const float* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (int64_t)row * a.q_sr + part * DPL;
 #pragma unroll
-  for (int c = 0; c < 64; ++c) {
-    q[c] = row_ok ? qp[c] : 0.0f;
-    o[c] = 0.0f;
+  for (int c = 0; c < DPL; c += 4) {
+    const f32x4 v = row_ok ? *(const f32x4*)(qp + c) : f32x4{};
+    q[c] = v[0]; q[c + 1] = v[1]; q[c + 2] = v[2]; q[c + 3] = v[3];
   }
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) o[c] = 0.0f;
   const float* kg = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
   const float* vg = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
   const float c2 = a.c_exp2;
@@ -77,8 +99,8 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
     for (int j = 0; j < kTileN; ++j) {
       float dot = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 64; ++c) dot = __builtin_fmaf(q[c], ks[j * D + part * 64 + c], dot);
-      if (LPR == 2) dot += __shfl_xor(dot, 1);
+      for (int c = 0; c < DPL; ++c) dot = __builtin_fmaf(q[c], ks[j * D + part * DPL + c], dot);
+      dot = row16_sum(dot);
       float x = SOFTCAP ? a.softcap_post * tanh_fast(dot * a.softcap_pre) : dot;
       const int key = j0 + j;
       x = (key >= lim_lo && key <= lim_hi) ? x : kNegInf;
@@ -90,30 +112,30 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
     const float alpha = fast_exp2((m_run - m_use) * c2);
     l_run *= alpha;
 #pragma unroll
-    for (int c = 0; c < 64; ++c) o[c] *= alpha;
+    for (int c = 0; c < DPL; ++c) o[c] *= alpha;
     m_run = m_new;
 #pragma unroll
     for (int j = 0; j < kTileN; ++j) {
       const float p = fast_exp2(__builtin_fmaf(s[j], c2, -m_use * c2));
       l_run += p;
 #pragma unroll
-      for (int c = 0; c < 64; ++c) o[c] = __builtin_fmaf(p, vs[j * D + part * 64 + c], o[c]);
+      for (int c = 0; c < DPL; ++c) o[c] = __builtin_fmaf(p, vs[j * D + part * DPL + c], o[c]);
     }
   }
 
   if (!row_ok) return;
   const bool empty = !(l_run > 0.0f);
   const float inv = empty ? 0.0f : 1.0f / l_run;
-  float* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)row * a.o_sr + part * 64;
+  float* op = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + (int64_t)row * a.o_sr + part * DPL;
 #pragma unroll
-  for (int c = 0; c < 64; c += 4) *(f32x4*)(op + c) = f32x4{o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
+  for (int c = 0; c < DPL; c += 4) *(f32x4*)(op + c) = f32x4{o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
   if (a.lse && part == 0)
     a.lse[((int64_t)b * a.hq + hq) * a.sq + row] = empty ? kNegInf : (m_run * c2 + __builtin_log2f(l_run)) * kLn2;
 }
 
 template <int D, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const F32Args& a, hipStream_t s) {
-  constexpr int ROWS = kThreads / (D / 64);
+  constexpr int ROWS = kRows;
   dim3 grid((a.sq + ROWS - 1) / ROWS, a.B * a.hq);
   hipLaunchKernelGGL((f32_kernel<D, MASK, SOFTCAP>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
