@@ -45,12 +45,15 @@ def prefill_flops(case) -> float:
     return 4.0 * d * pairs * B * Hq
 
 
-def decode_bytes(case) -> float:
+def decode_bytes(case, eb: int = 2) -> float:
+    """Algorithmic bytes of a paged decode: K and V of every valid token and
+    kv-head, Q and LSE once, O (bf16) once, the used block-table entries and
+    seqlens; eb = bytes per stored Q/K/V element."""
     m = case.meta
     lens = m["lens_k"]
-    kv = 2 * sum(lens) * m["Hkv"] * m["d"] * 2
-    q = m["B"] * m["Hq"] * m["sq"] * m["d"] * 2
-    o = q
+    kv = 2 * sum(lens) * m["Hkv"] * m["d"] * eb
+    q = m["B"] * m["Hq"] * m["sq"] * m["d"] * eb
+    o = m["B"] * m["Hq"] * m["sq"] * m["d"] * 2
     lse = m["B"] * m["Hq"] * m["sq"] * 4
     table = sum(-(-L // m["page_size"]) for L in lens) * 4
     return float(kv + q + o + lse + table + m["B"] * 4)
@@ -183,18 +186,44 @@ def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
                       f"value = those heads' algorithmic (causal) flops / time"}
 
 
-def time_workload(n: int, steps: int, warmup: int) -> None:
+def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16") -> None:
     """Time one of the other workloads alone (for its kernel-trace summary):
     1 = tiny fp32 attention (B=1, H=2, s=128, d=64; launch latency, too small
     for a roofline), 3 = varlen GQA causal (8 sequences of 256..8192, Hq=32,
-    Hkv=8), 5 = fp8 causal with soft-cap 30 (B=2, H=16, s=16384). Algorithmic
-    flops = 4 d per visible (query, key) pair per q-head."""
+    Hkv=8), 4 = the paged decode (64 requests, head-major pages) with bf16 or
+    E4M3 (kv_dtype) Q/K/V, in GB/s, 5 = fp8 causal with soft-cap 30 (B=2,
+    H=16, s=16384). Algorithmic flops = 4 d per visible (query, key) pair per
+    q-head."""
     import torch
     import paged_kv_attn_amd as pk
     import synth
-    case = synth.workload(n, "cuda")
+    if n == 4 and kv_dtype == "fp8":
+        import numpy as np
+        rng = np.random.Generator(np.random.PCG64(1004))   # the lengths and table of workload 4
+        lens = rng.integers(1024, 32768, size=64, endpoint=True)
+        case = synth.paged_case(lens, 1, 32, 8, 128, 128, "fp8", 1004, device="cuda", table_width=256, rng=rng,
+                                head_major=True)
+    else:
+        case = synth.workload(n, "cuda")
     t, m = case.t, case.meta
-    if n == 1:
+    unit = "TFLOP/s"
+    if n == 4:
+        flops = decode_bytes(case, 1 if kv_dtype == "fp8" else 2)   # bytes, reported as GB/s below
+        unit = "GB/s"
+        o = torch.empty(t["q"].shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda")
+        ds = case.descale
+        W = t["block_table"].shape[1]
+        p = pk.attn_params(t["q"].dtype, 128)
+        ws = torch.empty(max(1, pk.attn_workspace_bytes(p, 64, 32, 8, 1, 128, W * 128)), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            pk.attn_fwd_paged(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"], scale=case.scale,
+                              descale=(ds["q"], ds["k"], ds["v"]), out=o, lse=lse, workspace=ws)
+        name = (f"{kv_dtype} paged decode, 64 requests L~U[1024,32768], page 128 (head-major pages), Hq=32 Hkv=8 "
+                "d=128, sq=1, bf16 O")
+    elif n == 1:
         flops = 4.0 * m["d"] * m["sq"] * m["sk"] * m["B"] * m["Hq"]
         o = torch.empty_like(t["q"])
         lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda")
@@ -236,9 +265,11 @@ def time_workload(n: int, steps: int, warmup: int) -> None:
     ev.close()
     mean = sum(ts) / len(ts)
     median = 0.5 * (ts[(len(ts) - 1) // 2] + ts[len(ts) // 2])
-    print(json.dumps({"workload": name, "metric": "TFLOP/s", "value": round(flops / (mean * 1e-3) / 1e12, 2),
+    scale = 1e9 if unit == "GB/s" else 1e12
+    print(json.dumps({"workload": name, "metric": unit, "value": round(flops / (mean * 1e-3) / scale, 2),
                       "launch_us": round(mean * 1e3, 2), "median_us": round(median * 1e3, 2),
-                      "min_us": round(ts[0] * 1e3, 2), "steps": steps, "algorithmic_flops": flops}), flush=True)
+                      "min_us": round(ts[0] * 1e3, 2), "steps": steps,
+                      ("algorithmic_bytes" if unit == "GB/s" else "algorithmic_flops"): flops}), flush=True)
 
 
 def main():
@@ -249,9 +280,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--decode-split", type=int, default=0, help="keys per split-KV unit (0 = library default)")
-    ap.add_argument("--workload", type=int, default=0, choices=[0, 1, 3, 5],
-                    help="only time workload 1 (tiny fp32, latency), 3 (varlen GQA prefill) or 5 (fp8 soft-cap "
-                         "prefill) and print its line")
+    ap.add_argument("--workload", type=int, default=0, choices=[0, 1, 3, 4, 5],
+                    help="only time workload 1 (tiny fp32, latency), 3 (varlen GQA prefill), 4 (paged decode, "
+                         "see --kv-dtype) or 5 (fp8 soft-cap prefill) and print its line")
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="with --workload 4: bf16 or E4M3 Q/K/V pools (same lengths and table)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -264,7 +297,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.workload:
-        time_workload(args.workload, args.steps, args.warmup)
+        time_workload(args.workload, args.steps, args.warmup, args.kv_dtype)
         return
 
     import torch
