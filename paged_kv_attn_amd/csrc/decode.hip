@@ -104,7 +104,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   lds_char* const k0 = (lds_char*)kbuf0;
   lds_char* const v0 = (lds_char*)vbuf0;
   lds_char* const k1 = (lds_char*)kbuf1;
-  lds_char* const v1 = (lds_char*)vbuf1;
+  // fp8 V is in flight in registers and widened into LDS just before its
+  // granule's products, so one bf16 V buffer serves both stages: this wave's
+  // LDS accesses stay in program order, and the widening of granule g+1 comes
+  // after the reads of granule g. 16 KB instead of 24 KB per wave lets 10
+  // waves share a CU instead of 6, which keeps as many bytes in flight per CU
+  // as the bf16 variant.
+  lds_char* const v1 = FP8 ? (lds_char*)vbuf0 : (lds_char*)vbuf1;
 
   const int lane = threadIdx.x;
   const int g = blockIdx.x;      // kv-heads fastest: the units running together read the
