@@ -186,7 +186,7 @@ def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
                       f"value = those heads' algorithmic (causal) flops / time"}
 
 
-def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16") -> None:
+def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16", decode_split: int = 0) -> None:
     """Time one of the other workloads alone (for its kernel-trace summary):
     1 = tiny fp32 attention (B=1, H=2, s=128, d=64; launch latency, too small
     for a roofline), 3 = varlen GQA causal (8 sequences of 256..8192, Hq=32,
@@ -214,13 +214,14 @@ def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16") -> No
         lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda")
         ds = case.descale
         W = t["block_table"].shape[1]
-        p = pk.attn_params(t["q"].dtype, 128)
+        p = pk.attn_params(t["q"].dtype, 128, kv_split_tokens=decode_split)
         ws = torch.empty(max(1, pk.attn_workspace_bytes(p, 64, 32, 8, 1, 128, W * 128)), dtype=torch.uint8,
                          device="cuda")
 
         def run():
             pk.attn_fwd_paged(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"], scale=case.scale,
-                              descale=(ds["q"], ds["k"], ds["v"]), out=o, lse=lse, workspace=ws)
+                              descale=(ds["q"], ds["k"], ds["v"]), out=o, lse=lse, workspace=ws,
+                              kv_split_tokens=decode_split)
         name = (f"{kv_dtype} paged decode, 64 requests L~U[1024,32768], page 128 (head-major pages), Hq=32 Hkv=8 "
                 "d=128, sq=1, bf16 O")
     elif n == 1:
@@ -297,7 +298,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.workload:
-        time_workload(args.workload, args.steps, args.warmup, args.kv_dtype)
+        time_workload(args.workload, args.steps, args.warmup, args.kv_dtype, args.decode_split)
         return
 
     import torch

@@ -126,6 +126,10 @@ def test_workspace_and_split_queries():
     assert lib().attn_num_splits(ctypes.byref(p), 64, 32, 8, 1, 32768) == 16     # 2048-key splits
     assert lib().attn_num_splits(ctypes.byref(p), 1, 32, 8, 1, 32768) == 128     # 256-key floor
     assert lib().attn_num_splits(ctypes.byref(p), 8, 32, 8, 1, 32768) == 64      # 512: 64 units x 64 = 4096
+    # fp8 K/V start from 1024-key splits
+    p8 = _params(in_dtype=2, out_dtype=1)
+    assert lib().attn_num_splits(ctypes.byref(p8), 64, 32, 8, 1, 32768) == 32    # 1024-key splits
+    assert lib().attn_num_splits(ctypes.byref(p8), 8, 32, 8, 1, 32768) == 64     # 512 as for bf16
     p.kv_split_tokens = 256
     assert lib().attn_num_splits(ctypes.byref(p), 64, 32, 8, 1, 32768) == 128
     ws = lib().attn_workspace_bytes(ctypes.byref(p), 64, 32, 8, 1, 128, 32768)
