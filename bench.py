@@ -186,14 +186,17 @@ def cpu_baseline(case, n_heads: int, min_seconds: float = 10.0):
                       f"value = those heads' algorithmic (causal) flops / time"}
 
 
-def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16", decode_split: int = 0) -> None:
+def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16", decode_split: int = 0,
+                  slot_major: bool = False) -> None:
     """Time one of the other workloads alone (for its kernel-trace summary):
     1 = tiny fp32 attention (B=1, H=2, s=128, d=64; launch latency, too small
     for a roofline), 3 = varlen GQA causal (8 sequences of 256..8192, Hq=32,
     Hkv=8), 4 = the paged decode (64 requests, head-major pages) with bf16 or
     E4M3 (kv_dtype) Q/K/V, in GB/s, 5 = fp8 causal with soft-cap 30 (B=2,
-    H=16, s=16384). Algorithmic flops = 4 d per visible (query, key) pair per
-    q-head."""
+    H=16, s=16384), 6 = chunked prefill into a paged cache (B=4, 512 new
+    queries on 8192-key contexts, Hq=32, Hkv=8, causal; head-major pages, or
+    slot-major with slot_major). Algorithmic flops = 4 d per visible (query,
+    key) pair per q-head."""
     import torch
     import paged_kv_attn_amd as pk
     import synth
@@ -203,11 +206,25 @@ def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16", decod
         lens = rng.integers(1024, 32768, size=64, endpoint=True)
         case = synth.paged_case(lens, 1, 32, 8, 128, 128, "fp8", 1004, device="cuda", table_width=256, rng=rng,
                                 head_major=True)
+    elif n == 6:
+        case = synth.paged_case([8192] * 4, 512, 32, 8, 128, 128, "bf16", seed=1006, causal=True, device="cuda",
+                                head_major=not slot_major)
     else:
         case = synth.workload(n, "cuda")
     t, m = case.t, case.meta
     unit = "TFLOP/s"
-    if n == 4:
+    if n == 6:
+        # query i of 512 sees 8192 - 512 + i + 1 keys
+        flops = 4.0 * 128 * 32 * 4 * sum(8192 - 512 + i + 1 for i in range(512))
+        o = torch.empty(t["q"].shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device="cuda")
+
+        def run():
+            pk.attn_fwd_paged(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"], scale=case.scale,
+                              causal=True, out=o, lse=lse)
+        name = (f"bf16 chunked prefill into a paged cache, B=4, 512 new queries on 8192-key contexts, page 128 "
+                f"({'slot' if slot_major else 'head'}-major pages), Hq=32 Hkv=8 d=128, causal")
+    elif n == 4:
         flops = decode_bytes(case, 1 if kv_dtype == "fp8" else 2)   # bytes, reported as GB/s below
         unit = "GB/s"
         o = torch.empty(t["q"].shape, dtype=torch.bfloat16, device="cuda")
@@ -281,9 +298,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--decode-split", type=int, default=0, help="keys per split-KV unit (0 = library default)")
-    ap.add_argument("--workload", type=int, default=0, choices=[0, 1, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=0, choices=[0, 1, 3, 4, 5, 6],
                     help="only time workload 1 (tiny fp32, latency), 3 (varlen GQA prefill), 4 (paged decode, "
-                         "see --kv-dtype) or 5 (fp8 soft-cap prefill) and print its line")
+                         "see --kv-dtype), 5 (fp8 soft-cap prefill) or 6 (chunked prefill into a paged cache, "
+                         "see --slot-major) and print its line")
+    ap.add_argument("--slot-major", action="store_true",
+                    help="with --workload 6: pages stored [page, slot, head, d] instead of head-major")
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="with --workload 4: bf16 or E4M3 Q/K/V pools (same lengths and table)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -298,7 +318,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.workload:
-        time_workload(args.workload, args.steps, args.warmup, args.kv_dtype, args.decode_split)
+        time_workload(args.workload, args.steps, args.warmup, args.kv_dtype, args.decode_split, args.slot_major)
         return
 
     import torch
