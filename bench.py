@@ -200,12 +200,12 @@ def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16", decod
     import torch
     import paged_kv_attn_amd as pk
     import synth
-    if n == 4 and kv_dtype == "fp8":
+    if n == 4 and (kv_dtype == "fp8" or slot_major):
         import numpy as np
         rng = np.random.Generator(np.random.PCG64(1004))   # the lengths and table of workload 4
         lens = rng.integers(1024, 32768, size=64, endpoint=True)
-        case = synth.paged_case(lens, 1, 32, 8, 128, 128, "fp8", 1004, device="cuda", table_width=256, rng=rng,
-                                head_major=True)
+        case = synth.paged_case(lens, 1, 32, 8, 128, 128, kv_dtype, 1004, device="cuda", table_width=256, rng=rng,
+                                head_major=not slot_major)
     elif n == 6:
         case = synth.paged_case([8192] * 4, 512, 32, 8, 128, 128, "bf16", seed=1006, causal=True, device="cuda",
                                 head_major=not slot_major)
@@ -239,8 +239,8 @@ def time_workload(n: int, steps: int, warmup: int, kv_dtype: str = "bf16", decod
             pk.attn_fwd_paged(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"], scale=case.scale,
                               descale=(ds["q"], ds["k"], ds["v"]), out=o, lse=lse, workspace=ws,
                               kv_split_tokens=decode_split)
-        name = (f"{kv_dtype} paged decode, 64 requests L~U[1024,32768], page 128 (head-major pages), Hq=32 Hkv=8 "
-                "d=128, sq=1, bf16 O")
+        name = (f"{kv_dtype} paged decode, 64 requests L~U[1024,32768], page 128 "
+                f"({'slot' if slot_major else 'head'}-major pages), Hq=32 Hkv=8 d=128, sq=1, bf16 O")
     elif n == 1:
         flops = 4.0 * m["d"] * m["sq"] * m["sk"] * m["B"] * m["Hq"]
         o = torch.empty_like(t["q"])
@@ -303,7 +303,7 @@ def main():
                          "see --kv-dtype), 5 (fp8 soft-cap prefill) or 6 (chunked prefill into a paged cache, "
                          "see --slot-major) and print its line")
     ap.add_argument("--slot-major", action="store_true",
-                    help="with --workload 6: pages stored [page, slot, head, d] instead of head-major")
+                    help="with --workload 4 or 6: pages stored [page, slot, head, d] instead of head-major")
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="with --workload 4: bf16 or E4M3 Q/K/V pools (same lengths and table)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
