@@ -119,8 +119,10 @@ typedef struct {
   float k_descale;
   float v_descale;
   int kv_split_tokens; /* decode path: keys per split-KV work unit, a multiple of 64
-                          in [64, 2048]; 0 = choose from the shape. Calls that must agree bit for bit
-                          pass the same value (or the same shape with 0). */
+                          in [64, 2048]; 0 = choose from the shape and input type (the largest
+                          power of two up to 2048, 1024 for FP8, that still gives >= 4096 units).
+                          Calls that must agree bit for bit pass the same value (or the same shape
+                          and type with 0). */
   int sink_size;       /* streaming sink keys (sink_size of the Composable Kernel page's
                           mask): keys j < sink_size are visible to every row whose right
                           bound reaches them, whatever window_left says; 0 = none */
