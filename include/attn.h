@@ -32,7 +32,10 @@
  *     (a hipStream_t; NULL = the legacy default stream) and returns.
  *   - Strides are in ELEMENTS of the stored type; the head dimension d is
  *     contiguous (unit stride). Every tensor base pointer must be 16-byte
- *     aligned and every stride a multiple of 16 bytes.
+ *     aligned and every stride a multiple of 16 bytes. K and V may be NULL
+ *     when there are no keys (attn_fwd with sk = 0, attn_fwd_varlen with
+ *     max_seqlen_k = 0): every row then gets O = 0 and LSE = -inf (or the sink
+ *     logit).
  *   - Supported: d (the head dim of Q and K) in {64, 128}, head_dim_v (of V
  *     and O; attn_params_t) in {64, 128}; (in_dtype, out_dtype) in {(F32, F32),
  *     (BF16, BF16), (BF16, FP8_E4M3), (FP8_E4M3, BF16), (FP8_E4M3, FP8_E4M3)}.

@@ -316,8 +316,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
   const int eb = elem_bytes(p->in_dtype), ob = elem_bytes(p->out_dtype);
   TRY(check_ptr("q", q));
-  TRY(check_ptr("k", k));
-  TRY(check_ptr("v", v));
+  if (sk > 0 || k) TRY(check_ptr("k", k));   // no keys: K and V may be NULL (nothing is read)
+  if (sk > 0 || v) TRY(check_ptr("v", v));
   TRY(check_ptr("o", o));
   if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
   TRY(check_strides("q", q_stride, 3, eb));
@@ -445,8 +445,8 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_EINVAL, "cu_seqlens_q / cu_seqlens_k is NULL");
   const int eb = elem_bytes(p->in_dtype), ob = elem_bytes(p->out_dtype);
   TRY(check_ptr("q", q));
-  TRY(check_ptr("k", k));
-  TRY(check_ptr("v", v));
+  if (max_seqlen_k > 0 || k) TRY(check_ptr("k", k));   // no keys anywhere: K and V may be NULL
+  if (max_seqlen_k > 0 || v) TRY(check_ptr("v", v));
   TRY(check_ptr("o", o));
   if (lse && ((uintptr_t)lse & 3u)) return fail(ATTN_EINVAL, "lse is not 4-byte aligned");
   TRY(check_strides("q", q_stride, 2, eb));

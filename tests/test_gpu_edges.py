@@ -52,3 +52,23 @@ def test_many_tiny_decode_requests():
     out, lse = C.run_paged(case)
     O, LSE = C.oracle_paged(case)
     C.assert_parity(out, lse, O, LSE, "bf16", "300 tiny requests")
+
+
+@pytest.mark.parametrize("mode,sq,dtype", [("batch", 1, "bf16"), ("batch", 200, "bf16"), ("batch", 64, "f32"),
+                                           ("batch", 1, "fp8"), ("varlen", 40, "bf16")])
+def test_no_keys_with_empty_kv_tensors(mode, sq, dtype):
+    """No keys at all: K and V are empty tensors (NULL data pointers); every row
+    gets O = 0 and LSE = -inf, as the oracle's empty-row rule says."""
+    if mode == "batch":
+        d = 64 if dtype == "f32" else 128
+        c = synth.dense_case(2, 8, 2, sq, 0, d, dtype, seed=400 + sq, device=DEV)
+        assert c.t["k"].numel() == 0
+        out, lse = C.run_dense(c)
+        O, LSE = C.oracle_dense(c)
+        C.assert_parity(out, lse, O, LSE, dtype, f"batch sk=0 sq={sq} {dtype}")
+    else:
+        c = synth.varlen_case([5, sq, 0], [0, 0, 0], 8, 2, 128, dtype, seed=401, device=DEV)
+        assert c.t["k"].numel() == 0 and c.meta["max_k"] == 0
+        out, lse = C.run_varlen(c)
+        O, LSE = C.oracle_varlen(c)
+        C.assert_parity(out, lse.T, O, LSE.T, dtype, "varlen, no keys")
