@@ -9,7 +9,9 @@ the HIP path consume the exact bytes produced here.
 
 from .gen import (  # noqa: F401
     Case,
+    FP8_NAN_BYTE,
     dense_case,
+    poison_,
     paged_case,
     varlen_case,
     varlen_paged_case,

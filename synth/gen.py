@@ -17,7 +17,9 @@ Stored formats:
 
 Poisoning: key/value rows that the method must never read (rows at or beyond a
 sequence's used length, tail slots of a request's last page, a guard page that
-unused block-table entries point at) are filled with NaN, so any leak shows up.
+unused block-table entries point at) are filled with NaN, so any leak shows up:
+the float NaN for f32 / bf16 tensors, the E4M3FN NaN byte 0x7F (S.1111.111)
+for fp8 tensors.
 """
 
 from __future__ import annotations
@@ -29,6 +31,17 @@ import numpy as np
 import torch
 
 FP8_MAX = 448.0
+
+
+FP8_NAN_BYTE = 0x7F
+
+
+def poison_(t: torch.Tensor, index) -> None:
+    """Fill t[index] with NaN in t's stored format (E4M3FN: the byte 0x7F)."""
+    if t.dtype == torch.float8_e4m3fn:
+        t.view(torch.uint8)[index] = FP8_NAN_BYTE
+    else:
+        t[index] = float("nan")
 
 
 def _torch_gen(seed: int, device) -> torch.Generator:
@@ -93,13 +106,13 @@ def dense_case(B, Hq, Hkv, sq, sk, d, dtype="bf16", seed=0, causal=False, softca
         t["seqused_q"] = torch.tensor(list(seqused_q), dtype=torch.int32, device=device)
     if seqused_k is not None:
         t["seqused_k"] = torch.tensor(list(seqused_k), dtype=torch.int32, device=device)
-    if poison and dtype != "fp8":
+    if poison:
         for b in range(B):
             if seqused_k is not None:
-                k[b, :, int(seqused_k[b]):] = float("nan")
-                v[b, :, int(seqused_k[b]):] = float("nan")
+                poison_(k, (b, slice(None), slice(int(seqused_k[b]), None)))
+                poison_(v, (b, slice(None), slice(int(seqused_k[b]), None)))
             if seqused_q is not None:
-                q[b, :, int(seqused_q[b]):] = float("nan")
+                poison_(q, (b, slice(None), slice(int(seqused_q[b]), None)))
     wl, wr = _mask_args(causal, window)
     return Case("dense", dtype, t, {"q": dq, "k": dk, "v": dv},
                 scale if scale is not None else 1.0 / math.sqrt(d), softcap, wl, wr,
@@ -163,14 +176,13 @@ def paged_case(lens_k, sq, Hq, Hkv, d, page_size=128, dtype="bf16", seed=0, caus
     q, dq = to_stored(normal((B, Hq, sq, d), g, device), dtype)
     kp, dk = _pool(N, page_size, Hkv, d, g, device, dtype)
     vp, dv = _pool(N, page_size, Hkv, d, g, device, dtype)
-    if dtype != "fp8":
-        kp[guard] = float("nan")
-        vp[guard] = float("nan")
-        for r, L in enumerate(lens_k):
-            if L % page_size:
-                last = int(table[r, n_pages[r] - 1])
-                kp[last, L % page_size:] = float("nan")
-                vp[last, L % page_size:] = float("nan")
+    poison_(kp, guard)
+    poison_(vp, guard)
+    for r, L in enumerate(lens_k):
+        if L % page_size:
+            last = int(table[r, n_pages[r] - 1])
+            poison_(kp, (last, slice(L % page_size, None)))
+            poison_(vp, (last, slice(L % page_size, None)))
     if head_major:
         kp = kp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         vp = vp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
@@ -191,7 +203,7 @@ def varlen_paged_case(lens_q, lens_k, starts, Hq, Hkv, d, page_size=64, dtype="b
     block-table row (kv_start). Request s owns ceil((starts[s] + lens_k[s]) / P)
     pages dealt from a seeded permutation; every slot outside
     [starts[s], starts[s] + lens_k[s]) and a guard page (the last id, filling
-    unused table entries) are NaN (bf16 only). With ``head_major`` the pools'
+    unused table entries) are NaN (the E4M3FN NaN byte for fp8). With ``head_major`` the pools'
     storage is [N, Hkv, P, d] (same values, as in paged_case)."""
     lens_q = [int(x) for x in lens_q]
     lens_k = [int(x) for x in lens_k]
@@ -215,18 +227,17 @@ def varlen_paged_case(lens_q, lens_k, starts, Hq, Hkv, d, page_size=64, dtype="b
     q, dq = to_stored(normal((int(cu_q[-1]), Hq, d), g, device), dtype)
     kp, dk = _pool(N, P, Hkv, d, g, device, dtype)
     vp, dv = _pool(N, P, Hkv, d, g, device, dtype)
-    if dtype != "fp8":
-        kp[guard] = float("nan")
-        vp[guard] = float("nan")
-        for r in range(n):
-            for t0 in range(0, n_pages[r] * P, P):   # page by page, slots outside the used range
-                page = int(table[r, t0 // P])
-                lo = min(P, max(0, starts[r] - t0))
-                hi = min(P, max(0, starts[r] + lens_k[r] - t0))
-                for a_, b_ in ((0, lo), (max(lo, hi), P)):
-                    if b_ > a_:
-                        kp[page, a_:b_] = float("nan")
-                        vp[page, a_:b_] = float("nan")
+    poison_(kp, guard)
+    poison_(vp, guard)
+    for r in range(n):
+        for t0 in range(0, n_pages[r] * P, P):   # page by page, slots outside the used range
+            page = int(table[r, t0 // P])
+            lo = min(P, max(0, starts[r] - t0))
+            hi = min(P, max(0, starts[r] + lens_k[r] - t0))
+            for a_, b_ in ((0, lo), (max(lo, hi), P)):
+                if b_ > a_:
+                    poison_(kp, (page, slice(a_, b_)))
+                    poison_(vp, (page, slice(a_, b_)))
     if head_major:
         kp = kp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         vp = vp.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)

@@ -57,8 +57,10 @@ def test_fp8_decode_bitexact_paged_vs_contiguous():
     t = case.t
     W = case.meta["table_width"]
     table = t["block_table"].cpu()
-    k = torch.zeros((len(lens), Hkv, W * P, 128), dtype=t["k_pool"].dtype, device=DEV)
-    v = torch.zeros_like(k)
+    # keys past each request's length hold the E4M3FN NaN byte: never read
+    k = torch.full((len(lens), Hkv, W * P, 128), synth.FP8_NAN_BYTE, dtype=torch.uint8,
+                   device=DEV).view(torch.float8_e4m3fn)
+    v = k.clone()
     for b, L in enumerate(lens):
         for i in range(-(-L // P)):
             n = min(P, L - i * P)

@@ -1,7 +1,9 @@
 """The five measured workloads at their full sizes, launched exactly as bench.py
-launches them, checked against the oracle on sampled outputs the oracle can
-compute one by one (whole heads, whole requests, or blocks of query rows; a
-causal block of rows [a, b) is reproduced exactly by the keys [0, b))."""
+launches them, checked against the oracle. Workloads 1, 2 and 4 are compared
+in full (every head, every request); workloads 3 and 5, whose full oracle takes
+minutes, on sampled outputs the oracle can compute one by one (whole heads or
+blocks of query rows; a causal block of rows [a, b) is reproduced exactly by
+the keys [0, b)), every other output checked for finite values."""
 
 import numpy as np
 import pytest
@@ -29,17 +31,12 @@ def test_workload1_tiny_fp32_full():
     C.assert_parity(out, lse, O, LSE, "f32", "workload 1")
 
 
-def test_workload2_causal_prefill_sampled_heads():
+def test_workload2_causal_prefill_all_heads():
     case = synth.workload(2, DEV)
     out, lse = C.run_dense(case)
     torch.cuda.synchronize()
-    for b, h in [(0, 0), (1, 7), (3, 15)]:
-        q = C.decode(case.t["q"][b, h], "bf16")
-        k = C.decode(case.t["k"][b, h], "bf16")
-        v = C.decode(case.t["v"][b, h], "bf16")
-        O, LSE = oracle.head_attention(q, k, v, case.scale, 0.0, -1, 0)
-        C.assert_parity(out[b, h], lse[b, h], O, LSE, "bf16", f"workload 2 (b={b}, h={h})")
-    assert torch.isfinite(out.float()).all()
+    O, LSE = C.oracle_dense(case, workers=16)
+    C.assert_parity(out, lse, O, LSE, "bf16", "workload 2 (all 64 heads)")
 
 
 def test_workload3_varlen_gqa_sampled():
@@ -64,15 +61,12 @@ def test_workload3_varlen_gqa_sampled():
     assert torch.isfinite(out.float()).all()
 
 
-def test_workload4_paged_decode_sampled_requests():
+def test_workload4_paged_decode_all_requests():
     case = synth.workload(4, DEV)
     out, lse = C.run_paged(case)
     torch.cuda.synchronize()
-    lens = np.array(case.meta["lens_k"])
-    reqs = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 63]
-    O, LSE = C.oracle_paged(case, requests=reqs)
-    C.assert_parity(out[reqs], lse[reqs], O, LSE, "bf16", f"workload 4 (requests {reqs})")
-    assert torch.isfinite(out.float()).all()
+    O, LSE = C.oracle_paged(case, workers=8)
+    C.assert_parity(out, lse, O, LSE, "bf16", "workload 4 (all 64 requests)")
 
 
 def test_workload5_fp8_softcap_sampled_blocks():

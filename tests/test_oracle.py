@@ -581,3 +581,65 @@ def test_varlen_paged_equals_varlen_on_the_keys_it_addresses():
                                 -1, 0)
             np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
             np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# fp8 page pools whose K and V carry different per-tensor descales: each pool
+# is decoded with its own scale (checked against torch's E4M3FN cast and the
+# brute force, not against the oracle's own decoder).
+# ---------------------------------------------------------------------------
+
+def _fp8_pool_bytes(rng, shape):
+    """Random E4M3FN bytes with the two NaN codes (0x7F, 0xFF) replaced."""
+    b = rng.integers(0, 256, size=shape).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x3C
+    return b
+
+
+def _torch_e4m3(b, descale):
+    return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).to(torch.float64).numpy() * descale
+
+
+def test_paged_fp8_pools_decoded_with_their_own_descales():
+    rng = np.random.default_rng(71)
+    P, Hq, Hkv, d, sq, lens = 4, 4, 2, 5, 2, [7, 3]
+    n = sum(-(-L // P) for L in lens)
+    kb, vb = _fp8_pool_bytes(rng, (n, P, Hkv, d)), _fp8_pool_bytes(rng, (n, P, Hkv, d))
+    dk, dv = 0.011, 0.37          # deliberately different per-tensor descales
+    table = np.zeros((2, 2), dtype=np.int32)
+    perm = rng.permutation(n)
+    table[0, :2], table[1, :1] = perm[:2], perm[2:3]
+    q = rng.standard_normal((2, Hq, sq, d))
+    dec = (lambda a: oracle.e4m3fn_bits_to_f64(a, dk), lambda a: oracle.e4m3fn_bits_to_f64(a, dv))
+    o, lse = oracle.attention_paged(q, kb, vb, table, lens, 0.9, 0.0, -1, -1, decode=dec)
+    kf, vf = _torch_e4m3(kb, dk), _torch_e4m3(vb, dv)
+    for b, L in enumerate(lens):
+        keys = np.stack([kf[table[b, t // P], t % P] for t in range(L)])
+        vals = np.stack([vf[table[b, t // P], t % P] for t in range(L)])
+        for h in range(Hq):
+            bo, bl = brute_head(q[b, h].tolist(), keys[:, h // 2].tolist(), vals[:, h // 2].tolist(), 0.9, 0.0, -1, -1)
+            np.testing.assert_allclose(o[b, h], np.array(bo).reshape(sq, d), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[b, h], np.array(bl), atol=1e-12, rtol=0)
+
+
+def test_varlen_paged_fp8_pools_decoded_with_their_own_descales():
+    rng = np.random.default_rng(72)
+    P, n_pages, Hq, Hkv, d = 4, 12, 2, 1, 6
+    kb, vb = _fp8_pool_bytes(rng, (n_pages, P, Hkv, d)), _fp8_pool_bytes(rng, (n_pages, P, Hkv, d))
+    dk, dv = 0.02, 0.5
+    lens_q, lens_k, starts = [2, 3], [5, 6], [3, 1]
+    table = np.stack([rng.permutation(n_pages)[:4] for _ in range(2)])
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    q = rng.standard_normal((cq[-1], Hq, d))
+    dec = (lambda a: oracle.e4m3fn_bits_to_f64(a, dk), lambda a: oracle.e4m3fn_bits_to_f64(a, dv))
+    o, lse = oracle.attention_varlen_paged(q, kb, vb, cq, lens_k, table, 0.6, 0.0, -1, 0, kv_start=starts,
+                                           decode=dec)
+    kf, vf = _torch_e4m3(kb, dk), _torch_e4m3(vb, dv)
+    for s in range(2):
+        keys = np.stack([kf[table[s, (starts[s] + j) // P], (starts[s] + j) % P] for j in range(lens_k[s])])
+        vals = np.stack([vf[table[s, (starts[s] + j) // P], (starts[s] + j) % P] for j in range(lens_k[s])])
+        rows = slice(cq[s], cq[s + 1])
+        for h in range(Hq):
+            bo, bl = brute_head(q[rows, h].tolist(), keys[:, 0].tolist(), vals[:, 0].tolist(), 0.6, 0.0, -1, 0)
+            np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)

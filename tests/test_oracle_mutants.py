@@ -61,6 +61,13 @@ MUTANTS = {
                                 "return sign * (man / 8.0) * 2.0 ** (0 - 7)"),
     "e4m3 NaN for every top exponent": ("if exp == 0xF and man == 0x7:", "if exp == 0xF:"),
     "bf16 shifted by 15": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "paged V pool decoded with the K decoder": (
+        "vs = dec_v(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]",
+        "vs = dec_k(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]"),
+    "varlen-paged V pool decoded with the K decoder": ("kk, vv = dec_k(kk), dec_v(vv)", "kk, vv = dec_k(kk), dec_k(vv)"),
+    "paged K pool decoded with the V decoder": (
+        "ks = dec_k(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]",
+        "ks = dec_v(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]"),
 }
 
 
