@@ -73,6 +73,15 @@
  *   - Return value: ATTN_OK, or an error status with no kernel launched (except
  *     ATTN_ELAUNCH, reported when the runtime rejects a launch). attn_last_error()
  *     then describes it.
+ *   - In-tile byte offsets are 32-bit: 64 rows of K or V (the prefill tile), or
+ *     32 rows (a split-KV granule), must span less than 2 GiB, i.e.
+ *     64 * row stride * element size < 2^31 (32 * ... on the decode path);
+ *     a larger row stride is ATTN_EINVAL.
+ *   - With the environment variable ATTN_LOG set (to anything but "" or "0",
+ *     read on every call) each accepted call writes one line to stderr: the
+ *     entry point, the path taken (prefill, split-KV decode, f32), the types,
+ *     shape and mask, the launch grid and the split plan (the analogue of the
+ *     Composable Kernel page's GetName / PrintParameters of a kernel instance).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -286,15 +295,27 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p,
  * the shape takes the prefill path). max_seqlen_k is sk for attn_fwd and
  * block_table_stride * page_size for attn_fwd_paged. Returns 0 for invalid
  * shapes as well; the entry point then reports the error.
+ * The workspace holds the split-KV partials: an fp32 O of [B, Hkv, n_splits,
+ * sq * Hq / Hkv, dv] and an fp32 LSE of [B, Hkv, n_splits, sq * Hq / Hkv], the
+ * num_splits axis that the O and LSE tensors of the flash-attention epilogue
+ * page "hopper/epilogue_fwd.hpp" carry (CollectiveEpilogueFwd: its shapes and
+ * strides have a split dimension indexed by split_idx), reduced here by the
+ * library's own combine kernel. Owned by the caller; contents are scratch.
  */
 size_t attn_workspace_bytes(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int d,
                             int max_seqlen_k);
 
 /* Number of split-KV work units per (request, kv-head) the decode path uses for
- * this shape (1 if it takes the prefill path). */
+ * this shape (1 if it takes the prefill path): the extent of the num_splits
+ * axis of the partial O / LSE described above (CollectiveEpilogueFwd of the
+ * flash-attention epilogue page). */
 int attn_num_splits(const attn_params_t* p, int B, int Hq, int Hkv, int sq, int max_seqlen_k);
 
-/* Text describing the last non-OK status returned on the calling thread. */
+/* Text describing the last non-OK status returned on the calling thread. The
+ * FlashAttention-2 mma page's entry point refuses unsupported input (head dim,
+ * dtype) by throwing with a message; a C ABI cannot throw, so each entry point
+ * returns a status and leaves the message here (thread-local, overwritten by
+ * the next failing call on the same thread). */
 const char* attn_last_error(void);
 
 /* Library version string. */

@@ -73,7 +73,77 @@ def _ptr(t):
 
 
 def _stream(t):
+    """torch's current stream on t's device; t must be a GPU tensor (the
+    library only ever receives device pointers)."""
+    _need(t.is_cuda, f"tensors must be on a GPU (got {t.device})")
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+# ---- argument checks --------------------------------------------------------
+# The C ABI sees only pointers, element strides and sizes: it scales strides by
+# the element size of in_dtype / out_dtype and cannot tell a host pointer from a
+# device one. These checks run before any call, so a tensor of the wrong type,
+# shape or device never reaches a kernel.
+
+def _need(cond, msg, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_like(name, t, q):
+    """t shares q's dtype and device, and its last dim is contiguous."""
+    _need(t.dtype == q.dtype, f"{name} has dtype {t.dtype}, expected {q.dtype} (the dtype of q)", TypeError)
+    _need(t.device == q.device, f"{name} is on {t.device}, expected {q.device} (the device of q)")
+    _need(t.dim() == 0 or t.shape[-1] <= 1 or t.stride(-1) == 1, f"{name} must have unit stride in its last dim")
+
+
+def _check_index(name, t, q, n_min):
+    """int32 metadata: contiguous, on q's device, at least n_min entries."""
+    if t is None:
+        return
+    _need(t.dtype == torch.int32, f"{name} must be int32 (got {t.dtype})", TypeError)
+    _need(t.device == q.device, f"{name} is on {t.device}, expected {q.device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.numel() >= n_min, f"{name} has {t.numel()} entries, at least {n_min} needed")
+
+
+def _check_f32(name, t, q):
+    if t is None:
+        return
+    _need(t.dtype == torch.float32, f"{name} must be float32 (got {t.dtype})", TypeError)
+    _need(t.device == q.device, f"{name} is on {t.device}, expected {q.device}")
+
+
+def _resolve_out_dtype(q, out, out_dtype):
+    """O's dtype: out_dtype if given, else the dtype of a caller's out, else the default."""
+    if out_dtype is None and out is not None:
+        out_dtype = out.dtype
+    return out_dtype_for(q.dtype, out_dtype)
+
+
+def _check_out(out, shape, dtype, q):
+    if out is None:
+        return
+    _need(out.dtype == dtype, f"out has dtype {out.dtype}, expected {dtype}", TypeError)
+    _need(tuple(out.shape) == tuple(shape), f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    _need(out.device == q.device, f"out is on {out.device}, expected {q.device}")
+    _need(out.stride(-1) == 1 or shape[-1] <= 1, "out must have unit stride in its last dim")
+
+
+def _check_lse(lse, shape, q):
+    """lse is written as a dense fp32 array of this shape."""
+    if lse is None:
+        return
+    _need(lse.dtype == torch.float32, f"lse must be float32 (got {lse.dtype})", TypeError)
+    _need(tuple(lse.shape) == tuple(shape), f"lse has shape {tuple(lse.shape)}, expected {tuple(shape)}")
+    _need(lse.is_contiguous(), "lse must be contiguous")
+    _need(lse.device == q.device, f"lse is on {lse.device}, expected {q.device}")
+
+
+def _check_params_tensors(q, sink_logits, bias, alibi_slopes):
+    _check_f32("sink_logits", sink_logits, q)
+    _check_f32("bias", bias, q)
+    _check_f32("alibi_slopes", alibi_slopes, q)
 
 
 def attn_params(dtype, d, scale=None, causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0),
@@ -98,6 +168,8 @@ def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None
     if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        _need(workspace.device == device, f"workspace is on {workspace.device}, expected {device}")
+        _need(workspace.is_contiguous(), "workspace must be contiguous")
         return workspace
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
@@ -115,6 +187,22 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
     dv = v.shape[2] if v_colmajor else v.shape[3]
+    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
+    _need(k.dim() == 4 and v.dim() == 4, "k and v must be 4-d")
+    _check_like("k", k, q)
+    if not v_colmajor:
+        _check_like("v", v, q)
+    else:
+        _need(v.dtype == q.dtype and v.device == q.device, "v must share q's dtype and device", TypeError)
+    _need(k.shape[3] == d, f"k has head dim {k.shape[3]}, q has {d}")
+    _need((v.shape[3] if v_colmajor else v.shape[2]) == sk and v.shape[1] == Hkv, "v's shape does not match k's")
+    _need(cache_batch_idx is not None or (k.shape[0] == B and v.shape[0] == B), "k / v batch size differs from q's")
+    _check_index("seqused_q", seqused_q, q, B)
+    _check_index("seqused_k", seqused_k, q, B)
+    _check_params_tensors(q, sink_logits, bias, alibi_slopes)
+    out_dtype = _resolve_out_dtype(q, out, out_dtype)
+    _check_out(out, (B, Hq, sq, dv), out_dtype, q)
+    _check_lse(lse, (B, Hq, sq), q)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 bias, alibi_slopes, out_dtype, o_scale)
     if dv != d:
@@ -126,10 +214,11 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
     if cache_batch_idx is not None:
         if cache_batch_idx.dtype != torch.int32 or cache_batch_idx.numel() < B or not cache_batch_idx.is_contiguous():
             raise TypeError("cache_batch_idx must be a contiguous int32 tensor with B entries")
+        _check_index("cache_batch_idx", cache_batch_idx, q, B)
         p.cache_batch_idx = cache_batch_idx.data_ptr()
         p.cache_batch_count = k.shape[0]
     if out is None:
-        out = torch.empty((B, Hq, sq, dv), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((B, Hq, sq, dv), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
     ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, sk)
@@ -152,14 +241,26 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
+    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
+    _need(k.dim() == 3 and v.dim() == 3, "k and v must be 3-d [tokens, heads, dim]")
+    _check_like("k", k, q)
+    _check_like("v", v, q)
+    _need(k.shape[2] == d and v.shape[:2] == k.shape[:2], "k / v shapes do not match q")
+    _need(n >= 0, "cu_seqlens_q needs at least one entry")
+    _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
+    _check_index("cu_seqlens_k", cu_seqlens_k, q, n + 1)
+    _check_params_tensors(q, sink_logits, None, alibi_slopes)
+    dv = v.shape[2]
+    out_dtype = _resolve_out_dtype(q, out, out_dtype)
+    _check_out(out, (Tq, Hq, dv), out_dtype, q)
+    _check_lse(lse, (Hq, Tq), q)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     p.min_seqlen_q = int(min_seqlen_q)
-    dv = v.shape[2]
     if dv != d:
         p.head_dim_v = dv
     if out is None:
-        out = torch.empty((Tq, Hq, dv), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((Tq, Hq, dv), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     st = lambda t: i64_array(t.stride()[:2])  # noqa: E731
@@ -168,6 +269,23 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                 int(max_seqlen_k), Hq, Hkv, d, st(q), st(k), st(v), st(out),
                                 ctypes.c_void_p(0), 0, _stream(q)))
     return out, lse
+
+
+def _check_pools(q, d, k_pool, v_pool):
+    _need(k_pool.dim() == 4 and v_pool.dim() == 4, "pools must be 4-d [num_pages, page_size, Hkv, dim]")
+    _check_like("k_pool", k_pool, q)
+    _check_like("v_pool", v_pool, q)
+    _need(k_pool.shape[3] == d, f"k_pool has head dim {k_pool.shape[3]}, q has {d}")
+    _need(v_pool.shape[:3] == k_pool.shape[:3], "v_pool's [num_pages, page_size, Hkv] differ from k_pool's")
+
+
+def _check_table(block_table, q, rows):
+    _need(block_table.dtype == torch.int32, "block_table must be int32", TypeError)
+    _need(block_table.dim() == 2, "block_table must be 2-d [rows, pages]")
+    _need(block_table.device == q.device, f"block_table is on {block_table.device}, expected {q.device}")
+    _need(block_table.shape[0] >= rows, f"block_table has {block_table.shape[0]} rows, {rows} needed")
+    _need(block_table.stride(1) == 1 or block_table.shape[1] <= 1, "block_table rows must be contiguous")
+    _need(block_table.stride(0) >= block_table.shape[1], "block_table rows must not overlap")
 
 
 def _set_v_pool(p, d, k_pool, v_pool):
@@ -193,12 +311,22 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     dv = v_pool.shape[3]
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
-    W = block_table.shape[1]
+    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
+    _check_pools(q, d, k_pool, v_pool)
+    _check_table(block_table, q, B)
+    _check_index("seqlens_k", seqlens_k, q, B)
+    _check_params_tensors(q, sink_logits, None, alibi_slopes)
+    out_dtype = _resolve_out_dtype(q, out, out_dtype)
+    _check_out(out, (B, Hq, sq, dv), out_dtype, q)
+    _check_lse(lse, (B, Hq, sq), q)
+    # the library reads row b of the table at b * stride(0) and bounds every
+    # request by stride(0) * page_size keys (its split plan too)
+    W = block_table.stride(0)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     _set_v_pool(p, d, k_pool, v_pool)
     if out is None:
-        out = torch.empty((B, Hq, sq, dv), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((B, Hq, sq, dv), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
     ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, W * page_size)
@@ -229,12 +357,23 @@ def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_tabl
         if t is not None and t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")
     n = cu_seqlens_q.numel() - 1
+    _need(n >= 0, "cu_seqlens_q needs at least one entry")
+    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
+    _check_pools(q, d, k_pool, v_pool)
+    _check_table(block_table, q, n)
+    _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
+    _check_index("seqlens_k", seqlens_k, q, n)
+    _check_index("kv_start", kv_start, q, n)
+    _check_params_tensors(q, sink_logits, None, alibi_slopes)
+    out_dtype = _resolve_out_dtype(q, out, out_dtype)
+    _check_out(out, (Tq, Hq, v_pool.shape[3]), out_dtype, q)
+    _check_lse(lse, (Hq, Tq), q)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
                 alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     p.min_seqlen_q = int(min_seqlen_q)
     _set_v_pool(p, d, k_pool, v_pool)
     if out is None:
-        out = torch.empty((Tq, Hq, v_pool.shape[3]), dtype=out_dtype_for(q.dtype, out_dtype), device=q.device)
+        out = torch.empty((Tq, Hq, v_pool.shape[3]), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     kv_stride = i64_array([k_pool.stride(0), k_pool.stride(2), k_pool.stride(1)])

@@ -182,6 +182,56 @@ void logit_consts(const attn_params_t* p, float* c_exp2, float* pre, float* post
   }
 }
 
+// In-tile byte offsets are 32-bit in the kernels (buffer-load offsets and
+// ranges): the rows of one tile (64 keys in the prefill kernel, a 32-key
+// granule in the split-KV kernel) must span less than 2 GiB.
+attn_status_t check_row_span(const char* name, int64_t row_stride, int eb, int rows) {
+  if ((int64_t)rows * row_stride * eb >= ((int64_t)1 << 31))
+    return fail(ATTN_EINVAL, "%s row stride %lld (x %d rows of a tile) spans 2 GiB or more; 32-bit in-tile offsets",
+                name, (long long)row_stride, rows);
+  return ATTN_OK;
+}
+constexpr int kPrefillTileRows = 64;
+constexpr int kDecodeGranRows = 32;
+
+// ---- ATTN_LOG: one stderr line per accepted call (entry point, path, types,
+// shape, mask, launch grid, split plan), read per call like ATTN_VALIDATE ----
+bool log_on() {
+  const char* e = getenv("ATTN_LOG");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+const char* dtype_name(int t) { return t == ATTN_F32 ? "f32" : (t == ATTN_BF16 ? "bf16" : "fp8_e4m3"); }
+
+void log_call(const char* entry, const char* path, const attn_params_t* p, int d, int dv, int nz, int Hq, int Hkv,
+              int sq, int sk, const char* launch) {
+  if (!log_on()) return;
+  fprintf(stderr,
+          "attn: %s path=%s in=%s out=%s d=%d dv=%d batch=%d Hq=%d Hkv=%d sq=%d sk=%d window=(%d,%d) softcap=%g "
+          "bias=%d sink_size=%d sink_logits=%d v_layout=%d %s\n",
+          entry, path, dtype_name(p->in_dtype), dtype_name(p->out_dtype), d, dv, nz, Hq, Hkv, sq, sk, p->window_left,
+          p->window_right, (double)p->softcap, p->bias_type, p->sink_size, p->sink_logits ? 1 : 0, p->v_layout,
+          launch);
+}
+
+void log_prefill(const char* entry, const attn_params_t* p, const attn::PrefillArgs& a, int d, int dv, int nz,
+                 int sq, int sk) {
+  if (!log_on()) return;
+  char g[160];
+  snprintf(g, sizeof(g), "grid=%lld workgroups x 256 threads (%d query tiles of %d packed rows per unit)",
+           (long long)attn::prefill_workgroups(a, nz), a.n_qtiles, attn::prefill_rows_per_tile(p->in_dtype));
+  log_call(entry, "prefill", p, d, dv, nz, a.hq, a.hkv, sq, sk, g);
+}
+
+void log_decode(const char* entry, const attn_params_t* p, const attn::DecodeArgs& a, int d, int dv, int B,
+                int sk) {
+  if (!log_on()) return;
+  char g[200];
+  snprintf(g, sizeof(g), "grid=(%d,%d,%d) x 64 threads, splits=%d of %d keys; combine grid=%lld x 256 threads",
+           a.hkv, a.n_splits, B, a.n_splits, a.split_tokens, (long long)(((int64_t)B * a.hq * a.sq + 3) / 4));
+  log_call(entry, "split-kv decode", p, d, dv, B, a.hq, a.hkv, a.sq, sk, g);
+}
+
 attn_status_t launched(hipError_t e) {
   if (e != hipSuccess) return fail(ATTN_ELAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
@@ -353,12 +403,19 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.B = B; a.sq = sq; a.sk = sk; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
     a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;
     a.wl = p->window_left; a.wr = p->window_right;
+    if (log_on()) {
+      char g[96];
+      snprintf(g, sizeof(g), "grid=%lld workgroups x 256 threads", (long long)B * Hq * ((sq + 15) / 16));
+      log_call("attn_fwd", "f32", p, d, d, B, Hq, Hkv, sq, sk, g);
+    }
     return launched(attn::launch_f32(a, d, s));
   }
 
   if (takes_decode_path(p->in_dtype, sq, ratio)) {
     if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
       return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
+    TRY(check_row_span("k", k_stride[2], eb, kDecodeGranRows));
+    if (p->v_layout == ATTN_V_ROW_MAJOR) TRY(check_row_span("v", v_stride[2], eb, kDecodeGranRows));
     const int dv = dim_v(p, d);
     const int split = plan_split_tokens(p, B, Hkv, sk);
     const int nsp = n_splits_for(split, sk);
@@ -389,14 +446,18 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.o_sb = o_stride[0]; c.o_sh = o_stride[1]; c.o_sr = o_stride[2];
     c.seqlens_k = seqused_k; c.seqused_q = seqused_q; c.sk = sk;
+    c.no_keys = !k || !v;
     c.cache_idx = p->cache_batch_idx; c.cache_count = p->cache_batch_count;
     c.B = B; c.sq = sq; c.hq = Hq; c.hkv = Hkv; c.ratio = ratio; c.m_rows = m_rows;
     c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
   c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
     c.sink_logits = p->sink_logits;
+    log_decode("attn_fwd", p, a, d, dv, B, sk);
     return launched(attn::launch_decode(a, c, d, dv, false, B, s));
   }
 
+  TRY(check_row_span("k", k_stride[2], eb, kPrefillTileRows));
+  if (p->v_layout == ATTN_V_ROW_MAJOR) TRY(check_row_span("v", v_stride[2], eb, kPrefillTileRows));
   attn::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_sr = q_stride[2];
@@ -422,6 +483,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     if (ext >= ((int64_t)1 << 31)) return fail(ATTN_EINVAL, "elementwise bias spans more than 2 GiB per batch entry");
     a.bias_bytes = (uint32_t)ext;
   }
+  log_prefill("attn_fwd", p, a, d, dim_v(p, d), B, sq, sk);
   return launched(attn::launch_prefill(a, d, dim_v(p, d), p->in_dtype, attn::kPrefillBatch, B, s));
 }
 
@@ -453,6 +515,8 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   TRY(check_strides("k", k_stride, 2, eb));
   TRY(check_strides("v", v_stride, 2, eb));
   TRY(check_strides("o", o_stride, 2, ob));
+  TRY(check_row_span("k", k_stride[0], eb, kPrefillTileRows));
+  TRY(check_row_span("v", v_stride[0], eb, kPrefillTileRows));
   if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
   if (validate_on()) {
     TRY(validate_cu("cu_seqlens_q", cu_seqlens_q, n, max_seqlen_q, total_q, (hipStream_t)stream));
@@ -479,6 +543,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
+  log_prefill("attn_fwd_varlen", p, a, d, dim_v(p, d), n, max_seqlen_q, max_seqlen_k);
   return launched(attn::launch_prefill(a, d, dim_v(p, d), p->in_dtype, attn::kPrefillVarlen, n, (hipStream_t)stream));
 }
 
@@ -516,6 +581,8 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   TRY(check_strides("kv", kv_stride, 3, eb));
   TRY(check_strides("v_pool_stride", v_st, 3, eb));
   TRY(check_strides("o", o_stride, 3, elem_bytes(p->out_dtype)));
+  TRY(check_row_span("k_pool", kv_stride[2], eb, decode_shape ? kDecodeGranRows : kPrefillTileRows));
+  TRY(check_row_span("v_pool", v_st[2], eb, decode_shape ? kDecodeGranRows : kPrefillTileRows));
   if (B == 0 || sq == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
@@ -550,6 +617,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.wl = p->window_left; a.wr = p->window_right;
     a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
     set_bias(p, c_exp2, &a);
+    log_prefill("attn_fwd_paged", p, a, d, dv, B, sq, max_len);
     return launched(attn::launch_prefill(a, d, dv, p->in_dtype, attn::kPrefillPaged, B, (hipStream_t)stream));
   }
 
@@ -584,6 +652,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   c.split_tokens = split; c.n_splits = nsp; c.o_mul = out_mul(p);
   c.out_fp8 = p->out_dtype == ATTN_FP8_E4M3;
   c.sink_logits = p->sink_logits;
+  log_decode("attn_fwd_paged", p, a, d, dv, B, max_len);
   return launched(attn::launch_decode(a, c, d, dv, true, B, (hipStream_t)stream));
 }
 
@@ -621,6 +690,8 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   TRY(check_strides("kv", kv_stride, 3, eb));
   TRY(check_strides("v_pool_stride", v_st, 3, eb));
   TRY(check_strides("o", o_stride, 2, elem_bytes(p->out_dtype)));
+  TRY(check_row_span("k_pool", kv_stride[2], eb, kPrefillTileRows));
+  TRY(check_row_span("v_pool", v_st[2], eb, kPrefillTileRows));
   if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
@@ -663,6 +734,7 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
+  log_prefill("attn_fwd_varlen_paged", p, a, d, dv, n, max_seqlen_q, (int)max_len64);
   return launched(attn::launch_prefill(a, d, dv, p->in_dtype, attn::kPrefillVarlenPaged, n, (hipStream_t)stream));
 }
 

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   // K/V batch entry of contiguous K/V (cache batch index; out of range: no keys)
   const int kb = PAGED ? b : kv_entry(a.cache_idx, a.cache_count, b);
-  const int Lk = kb < 0 ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
+  // an out-of-range cache entry, or NULL K or V, has no keys
+  const int Lk = (kb < 0 || !a.k || !a.v) ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
   const int t0 = split * a.split_tokens;
   if (t0 >= Lk) return;  // empty split: the combine reads only ceil(Lk / split_tokens) partials
   const int t1 = min(Lk, t0 + a.split_tokens);
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int g = hq / a.ratio;
   const int r = pos * a.ratio + hq % a.ratio;  // packed row
   if (a.seqused_q && pos >= a.seqused_q[b]) return;  // row past the used query length: not written
-  const int Lk = kv_entry(a.cache_idx, a.cache_count, b) < 0 ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
+  const int Lk = (a.no_keys || kv_entry(a.cache_idx, a.cache_count, b) < 0) ? 0 : (a.seqlens_k ? a.seqlens_k[b] : a.sk);
   const int n = Lk > 0 ? (Lk + a.split_tokens - 1) / a.split_tokens : 0;
   const int64_t unit0 = ((int64_t)b * a.hkv + g) * a.n_splits;
   const float* lse_p = a.part_lse + unit0 * a.m_rows + r;   // split s at lse_p[s * m_rows]

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(F32Args a) {
   const int b = bh / a.hq, hq = bh % a.hq;
   const int g = hq / a.ratio;
   const int Lq = a.seqused_q ? a.seqused_q[b] : a.sq;
-  const int Lk = a.seqused_k ? a.seqused_k[b] : a.sk;
+  // NULL K or V: no keys, whatever seqused_k says (nothing is dereferenced)
+  const int Lk = (!a.k || !a.v) ? 0 : (a.seqused_k ? a.seqused_k[b] : a.sk);
   const int r0 = blockIdx.x * ROWS;
   if (r0 >= Lq) return;
   const int row = r0 + tid / kLPR;

@@ -104,6 +104,7 @@ struct CombineArgs {
   const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
   const int32_t* cache_idx;   // as DecodeArgs (an out-of-range entry has no keys)
   int cache_count;
+  int no_keys;                // K or V is NULL: every row has no keys
 };
 
 // fp32 path (batch mode).
@@ -125,6 +126,7 @@ struct F32Args {
 };
 
 int prefill_rows_per_tile(int in_type);  // packed query rows per prefill workgroup
+int64_t prefill_workgroups(const PrefillArgs& a, int nz);  // workgroups of launch_prefill(a, .., nz, ..)
 // d: head dim of Q and K; dv: head dim of V and O ({64, 128} each; paged mode: dv == d)
 hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int batch_or_seqs,
                           hipStream_t stream);

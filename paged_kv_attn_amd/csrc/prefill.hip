@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     o_off = (int64_t)z * a.o_sb;
     lse_off = (int64_t)z * a.lse_sb;
   }
+  if (!a.k || !a.v) Lk = 0;  // NULL K or V: no keys, whatever the length arrays say
   const int ratio = a.ratio;
   const int rows_total = Lq * ratio;
   const int r0 = qt * kBlockM;
@@ -770,14 +771,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   if (row_ok && a.lse && h == 0) a.lse[lse_off + (int64_t)hq * a.lse_sh + pos] = lse2 * kLn2;
 }
 
+// workgroups of a launch: every XCD's list padded to whole dispatch groups
+int64_t grid_size(const PrefillArgs& a, int nz) {
+  const int64_t n_units = (int64_t)a.hkv * nz;
+  const int64_t units_x = (n_units + kXcds - 1) / kXcds;   // units per XCD
+  const int64_t G = group_units(a.n_qtiles);
+  return kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
+}
+
 template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
-  const int64_t n_units = (int64_t)a.hkv * nz;
-  const int64_t units_x = (n_units + kXcds - 1) / kXcds;   // units per XCD
-  const int64_t G = group_units(a.n_qtiles);
-  const int64_t grid = kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
+  const int64_t grid = grid_size(a, nz);
   hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MASK, SOFTCAP, BIAS, VT>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, b);
   return hipGetLastError();
@@ -862,6 +868,10 @@ hipError_t launch_prefill_fp8_d128(const PrefillArgs& a, int dv, int mode, int n
 hipError_t launch_prefill_fp8_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
 
 int prefill_rows_per_tile(int) { return kBlockM; }
+
+int64_t prefill_workgroups(const PrefillArgs& a, int nz) {
+  return (a.n_qtiles <= 0 || nz <= 0 || a.hkv <= 0) ? 0 : grid_size(a, nz);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int nz, hipStream_t stream) {
   if (a.n_qtiles <= 0 || nz <= 0 || a.hkv <= 0) return hipSuccess;

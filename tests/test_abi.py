@@ -306,3 +306,80 @@ def test_varlen_paged_rejects_bad_arguments():
     assert _vpaged(_params(head_dim_v=64)) == 1 and "v_pool_stride" in _err()
     assert _vpaged(_params(v_layout=_lib.ATTN_V_COL_MAJOR)) == 2 and "column-major" in _err()
     assert _vpaged(_params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)) == 2
+
+
+# ---------------------------------------------------------------------------
+# 32-bit in-tile offsets: a K/V row stride whose tile span reaches 2 GiB is
+# refused (64 rows on the prefill path, 32 rows on the split-KV path).
+# ---------------------------------------------------------------------------
+
+def test_row_stride_spanning_2gib_is_refused():
+    p = _params()
+    big = (1 << 31) // (64 * 2)                     # 64 rows x 2 bytes = 2 GiB exactly
+    st = [2 * 64 * 128, 64 * 128, 128]
+    kst = [2 * 64 * big, 64 * big, big]
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 1, 2, 2, 64, 64, 128, i64_array(st),
+                       i64_array(kst), i64_array(st), i64_array(st), NULL, NULL, NULL, 0, NULL)
+    assert r == 1 and "k row stride" in _err() and "2 GiB" in _err()
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 1, 2, 2, 64, 64, 128, i64_array(st),
+                       i64_array(st), i64_array(kst), i64_array(st), NULL, NULL, NULL, 0, NULL)
+    assert r == 1 and "v row stride" in _err()
+    # decode shapes: 32 rows per granule, so twice the stride is the limit there
+    dst = [2 * 128, 128, 128]
+    half = [2 * 64 * big, 64 * big, big]             # 32 rows x big x 2 B = 1 GiB: accepted up to the workspace
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 1, 2, 2, 1, 64, 128, i64_array(dst),
+                       i64_array(half), i64_array(half), i64_array(dst), NULL, NULL, NULL, 0, NULL)
+    assert r == 3, _err()
+    dbl = [2 * 64 * 2 * big, 64 * 2 * big, 2 * big]
+    r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 1, 2, 2, 1, 64, 128, i64_array(dst),
+                       i64_array(dbl), i64_array(dbl), i64_array(dst), NULL, NULL, NULL, 0, NULL)
+    assert r == 1 and "k row stride" in _err()
+
+
+def test_row_stride_span_refused_on_varlen_and_paged():
+    p = _params()
+    big = (1 << 31) // (64 * 2)
+    st = [2 * 128, 128]
+    r = lib().attn_fwd_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 2, 10, 5, 5, 2, 2, 128,
+                              i64_array(st), i64_array([big, 128]), i64_array(st), i64_array(st), NULL, 0, NULL)
+    assert r == 1 and "k row stride" in _err()
+    qst = [8 * 64 * 128, 64 * 128, 128]
+    kv = [64 * 2 * big, 128, big]
+    r = lib().attn_fwd_paged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 16, FAKE, 2, 64, 8, 2, 128,
+                             64, 10, i64_array(qst), i64_array(kv), i64_array(qst), NULL, 0, NULL)
+    assert r == 1 and "k_pool row stride" in _err()
+    r = lib().attn_fwd_varlen_paged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, NULL, FAKE, 16, 2, 10,
+                                    5, 8, 2, 128, 64, 10, i64_array([8 * 128, 128]), i64_array(kv),
+                                    i64_array([8 * 128, 128]), NULL)
+    assert r == 1 and "k_pool row stride" in _err()
+
+
+def test_attn_log_prints_one_line_per_accepted_call():
+    """ATTN_LOG: one stderr line naming the entry point, path, grid and split
+    plan for a call that passed validation (here the launch itself then fails:
+    there is no GPU in this process)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, sys; sys.path.insert(0, %r)\n"
+        "from paged_kv_attn_amd._lib import AttnParams, i64_array, lib\n"
+        "p = AttnParams(); lib().attn_params_init(ctypes.byref(p), 0.125)\n"
+        "F, N = ctypes.c_void_p(0x10000), ctypes.c_void_p(0)\n"
+        "st = [2 * 64 * 128, 64 * 128, 128]\n"
+        "lib().attn_fwd(ctypes.byref(p), F, F, F, F, N, 1, 2, 2, 64, 64, 128, i64_array(st), i64_array(st),"
+        " i64_array(st), i64_array(st), N, N, N, 0, N)\n"
+        "lib().attn_fwd(ctypes.byref(p), F, F, F, F, N, 1, 2, 2, 0, 64, 128, i64_array(st), i64_array(st),"
+        " i64_array(st), i64_array(st), N, N, N, 0, N)\n"   # empty: no line
+        "ws = lib().attn_workspace_bytes(ctypes.byref(p), 4, 32, 8, 1, 128, 4096)\n"
+        "kst = [8 * 4096 * 128, 4096 * 128, 128]\n"
+        "lib().attn_fwd(ctypes.byref(p), F, F, F, F, N, 4, 32, 8, 1, 4096, 128, i64_array([32 * 128, 128, 128]),"
+        " i64_array(kst), i64_array(kst), i64_array([32 * 128, 128, 128]), N, N, F, ws, N)\n" % ROOT)
+    env = dict(os.environ, ATTN_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("attn: ")]
+    assert len(lines) == 2, r.stderr
+    assert "attn_fwd path=prefill" in lines[0] and "grid=" in lines[0] and "Hq=2" in lines[0]
+    assert "path=split-kv decode" in lines[1] and "splits=" in lines[1] and "combine grid=" in lines[1]
+    env["ATTN_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert not [ln for ln in r.stderr.splitlines() if ln.startswith("attn: ")]

@@ -1,9 +1,11 @@
 """More GPU edge cases against the fp64 oracle: varlen with different query
 and key lengths (bottom-right causal alignment per sequence), head dim 64 on
 the varlen and paged-prefill paths, decode query blocks longer than the keys,
-single-key and exactly-one-tile problems, and a large batch of tiny requests."""
+single-key and exactly-one-tile problems, a large batch of tiny requests, and
+NULL K/V with stale key lengths."""
 
 import pytest
+import torch
 
 import synth
 from tests import _cases as C
@@ -72,3 +74,51 @@ def test_no_keys_with_empty_kv_tensors(mode, sq, dtype):
         out, lse = C.run_varlen(c)
         O, LSE = C.oracle_varlen(c)
         C.assert_parity(out, lse.T, O, LSE.T, dtype, "varlen, no keys")
+
+
+@pytest.mark.parametrize("mode,dtype", [("batch_prefill", "bf16"), ("batch_decode", "bf16"), ("batch_prefill", "f32"),
+                                        ("varlen", "bf16")])
+def test_null_kv_reads_no_keys_whatever_the_lengths_say(mode, dtype):
+    """K and V NULL (allowed when the call has no keys: sk = 0, or
+    max_seqlen_k = 0) while the device length arrays still list keys (a stale
+    seqused_k or cu_seqlens_k): the kernels read no key, every row gets O = 0
+    and LSE = -inf."""
+    import ctypes
+    from paged_kv_attn_amd._lib import AttnParams, i64_array, lib, check
+    Hq, Hkv, d = 8, 2, (64 if dtype == "f32" else 128)
+    sq = 1 if mode == "batch_decode" else 70
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    p = AttnParams()
+    lib().attn_params_init(ctypes.byref(p), 0.1)
+    p.in_dtype = p.out_dtype = 0 if dtype == "f32" else 1
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    N = ctypes.c_void_p(0)
+    if mode.startswith("batch"):
+        B = 2
+        q = torch.randn(B, Hq, sq, d, device=DEV).to(tdt)
+        out = torch.full((B, Hq, sq, d), 5.0, dtype=tdt, device=DEV)
+        lse = torch.full((B, Hq, sq), 5.0, device=DEV)
+        stale = torch.tensor([300, 7], dtype=torch.int32, device=DEV)   # more keys than sk = 0
+        ws_b = lib().attn_workspace_bytes(ctypes.byref(p), B, Hq, Hkv, sq, d, 0)
+        ws = torch.empty(max(ws_b, 256), dtype=torch.uint8, device=DEV)
+        st = i64_array(q.stride())
+        zst = i64_array([Hkv * d, d, d])
+        check(lib().attn_fwd(ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), N, N, ctypes.c_void_p(out.data_ptr()),
+                             ctypes.c_void_p(lse.data_ptr()), B, Hq, Hkv, sq, 0, d, st, zst, zst,
+                             i64_array(out.stride()), N, ctypes.c_void_p(stale.data_ptr()),
+                             ctypes.c_void_p(ws.data_ptr()), ws_b, stream))
+    else:
+        q = torch.randn(sq, Hq, d, device=DEV).to(tdt)
+        out = torch.full((sq, Hq, d), 5.0, dtype=tdt, device=DEV)
+        lse = torch.full((Hq, sq), 5.0, device=DEV)
+        cu_q = torch.tensor([0, 30, sq], dtype=torch.int32, device=DEV)
+        cu_k = torch.tensor([0, 500, 900], dtype=torch.int32, device=DEV)   # stale: lists keys
+        st = i64_array(q.stride()[:2])
+        zst = i64_array([Hkv * d, d])
+        check(lib().attn_fwd_varlen(ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), N, N,
+                                    ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                                    ctypes.c_void_p(cu_q.data_ptr()), ctypes.c_void_p(cu_k.data_ptr()), 2, sq, 40, 0,
+                                    Hq, Hkv, d, st, zst, zst, i64_array(out.stride()[:2]), N, 0, stream))
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all(), "a row with no keys must get O = 0"
+    assert torch.isneginf(lse).all(), "a row with no keys must get LSE = -inf"
