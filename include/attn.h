@@ -291,6 +291,30 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p,
                                     const int64_t o_stride[2], void* stream);
 
 /*
+ * attn_fwd_paged without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Arguments, layouts, results and errors are those of
+ * attn_fwd_paged (the same kernels, bit-identical results). The split-KV
+ * partials go to a 64 MiB array that the library keeps on each GPU it runs on
+ * until the process ends (its address is looked up on the first call on a
+ * device); the call itself allocates nothing. A shape whose partials need more
+ * than 64 MiB (attn_workspace_bytes() > 64 MiB) is refused with
+ * ATTN_EWORKSPACE before any launch. Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (work queued on two streams, or from
+ * two threads) race on it and must be serialised by the caller. The array
+ * keeps the last call's contents; each call writes every partial it reads.
+ */
+attn_status_t attn_fwd_paged_noalloc(const attn_params_t* p,
+                                     const void* q, const void* k_pool, const void* v_pool,
+                                     void* o, float* lse,
+                                     const int32_t* block_table, int block_table_stride,
+                                     const int32_t* seqlens_k,
+                                     int B, int sq, int Hq, int Hkv, int d,
+                                     int page_size, int num_pages,
+                                     const int64_t q_stride[3], const int64_t kv_stride[3],
+                                     const int64_t o_stride[3], void* stream);
+
+/*
  * Workspace bytes needed by attn_fwd / attn_fwd_paged for this shape (0 when
  * the shape takes the prefill path). max_seqlen_k is sk for attn_fwd and
  * block_table_stride * page_size for attn_fwd_paged. Returns 0 for invalid

@@ -65,6 +65,8 @@ _SIGNATURES = {
                             _I, _I, _I, _I, _I64P, _I64P, _I64P, _P, _SZ, _P]),
     "attn_fwd_varlen_paged": (_I, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
                                    _I, _I, _I, _I, _I, _I, _I64P, _I64P, _I64P, _P]),
+    "attn_fwd_paged_noalloc": (_I, [ctypes.POINTER(AttnParams), _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I,
+                                    _I, _I, _I, _I, _I64P, _I64P, _I64P, _P]),
     "attn_workspace_bytes": (_SZ, [ctypes.POINTER(AttnParams), _I, _I, _I, _I, _I, _I]),
     "attn_num_splits": (_I, [ctypes.POINTER(AttnParams), _I, _I, _I, _I, _I]),
     "attn_last_error": (ctypes.c_char_p, []),

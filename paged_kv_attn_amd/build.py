@@ -21,7 +21,8 @@ OUT = os.path.join(PKG, "libattn.so")
 OBJ = os.path.join(PKG, "_build")
 # (source, object, extra defines): the prefill kernel's instantiations compile
 # in four parts, one per (input type, head dim), in parallel
-SOURCES = [("api.cpp", "api", []), ("decode.hip", "decode", []), ("f32.hip", "f32", [])] + \
+SOURCES = [("api.cpp", "api", []), ("noalloc.cpp", "noalloc", []), ("decode.hip", "decode", []),
+           ("f32.hip", "f32", [])] + \
     [("prefill.hip", f"prefill_p{k}", [f"-DATTN_PREFILL_PART={k}"]) for k in range(4)]
 # Per-source code-generation options. The decode kernel keeps its MFMA
 # accumulators in ordinary VGPRs: its online-softmax rescale touches them

@@ -310,6 +310,18 @@ attn_status_t validate_pages(const int32_t* table_dev, int rows, int stride, int
 
 }  // namespace
 
+namespace attn {
+// Sets the calling thread's attn_last_error() text (for entry points defined
+// in other sources of the library) and returns st.
+attn_status_t set_error(attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace attn
+
 extern "C" {
 
 const char* attn_last_error(void) { return g_err; }

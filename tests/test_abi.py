@@ -383,3 +383,20 @@ def test_attn_log_prints_one_line_per_accepted_call():
     env["ATTN_LOG"] = "0"
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert not [ln for ln in r.stderr.splitlines() if ln.startswith("attn: ")]
+
+
+def test_noalloc_refuses_partials_beyond_its_scratch_before_any_device_call():
+    """attn_fwd_paged_noalloc keeps the split-KV partials in a 64 MiB per-GPU
+    array: a shape needing more is refused (ATTN_EWORKSPACE) on the host."""
+    p = _params(kv_split_tokens=64)
+    need = lib().attn_workspace_bytes(ctypes.byref(p), 64, 32, 8, 1, 128, 512 * 128)
+    assert need > 64 << 20
+    st = [32 * 128, 128, 128]
+    kv = [128 * 8 * 128, 128, 8 * 128]
+    r = lib().attn_fwd_paged_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 512, FAKE, 64, 1, 32, 8,
+                                     128, 128, 100, i64_array(st), i64_array(kv), i64_array(st), NULL)
+    assert r == 3 and str(64 << 20) in _err()
+    # argument errors are attn_fwd_paged's own (a prefill shape needs no scratch)
+    r = lib().attn_fwd_paged_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, NULL, 4, FAKE, 2, 64, 32, 8,
+                                     128, 128, 100, i64_array(st), i64_array(kv), i64_array(st), NULL)
+    assert r == 1 and "block_table" in _err()
