@@ -97,9 +97,16 @@ __host__ __device__ inline int group_units(int n_qtiles) {
   return n_qtiles >= kGroupTiles ? 1 : kGroupTiles / n_qtiles;
 }
 
-template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
+// Mask kinds (a template parameter, so the common causal mask costs one
+// compare per score on the tiles it cuts): none; a right bound only (causal,
+// or any window with window_left < 0); a window with a left bound (and sinks).
+enum MaskKind : int { kMaskNone = 0, kMaskRight = 1, kMaskWindow = 2 };
+
+template <int D, int DV, bool FP8, int MODE, int MK, bool SOFTCAP, int BIAS, bool VT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   static_assert(!VT || (!FP8 && D == DV), "column-major V: bf16 with equal head dims");
+  constexpr bool MASK = MK != kMaskNone;
+  constexpr bool TWO_SIDED = MK == kMaskWindow;   // the host guarantees a.wl >= 0
   using Tr = Traits<D, DV, FP8>;
   // Separate LDS objects per slot: the compiler can then prove that reads of
   // one slot do not alias the HBM->LDS loads in flight into the other, and
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       const int hi = lim_hi - j0 - kHStep * h;
       const int lo = lim_lo - j0 - kHStep * h;
       const int sk = a.sink_size - j0 - kHStep * h;
-      const bool two_sided = MASK && a.wl >= 0;
+      constexpr bool two_sided = TWO_SIDED;
       float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -537,13 +544,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       const int hi = lim_hi - j0 - kHStep * h;
       const int lo = lim_lo - j0 - kHStep * h;
       const int sk = a.sink_size - j0 - kHStep * h;  // sink keys ignore the left bound
-      const bool two_sided = MASK && a.wl >= 0;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jr = key_rel(b, r);
-          const bool vis = (jr <= hi) && (!two_sided || jr >= lo || jr < sk);
+          const bool vis = (jr <= hi) && (!TWO_SIDED || jr >= lo || jr < sk);
           s[b][r] = vis ? s[b][r] : kNegInf;
         }
     }
@@ -779,21 +785,27 @@ int64_t grid_size(const PrefillArgs& a, int nz) {
   return kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
 }
 
-template <int D, int DV, bool FP8, int MODE, bool MASK, bool SOFTCAP, int BIAS, bool VT>
+template <int D, int DV, bool FP8, int MODE, int MK, bool SOFTCAP, int BIAS, bool VT>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
   const int64_t grid = grid_size(a, nz);
-  hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MASK, SOFTCAP, BIAS, VT>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MK, SOFTCAP, BIAS, VT>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, b);
   return hipGetLastError();
 }
 
+template <int D, int DV, bool FP8, int MODE, int MK, int BIAS, bool VT>
+hipError_t launch_s(const PrefillArgs& a, int nz, bool softcap, hipStream_t s) {
+  return softcap ? launch_t<D, DV, FP8, MODE, MK, true, BIAS, VT>(a, nz, s)
+                 : launch_t<D, DV, FP8, MODE, MK, false, BIAS, VT>(a, nz, s);
+}
+
 template <int D, int DV, bool FP8, int MODE, int BIAS, bool VT>
 hipError_t launch_b(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if (mask)
-    return softcap ? launch_t<D, DV, FP8, MODE, true, true, BIAS, VT>(a, nz, s) : launch_t<D, DV, FP8, MODE, true, false, BIAS, VT>(a, nz, s);
-  return softcap ? launch_t<D, DV, FP8, MODE, false, true, BIAS, VT>(a, nz, s) : launch_t<D, DV, FP8, MODE, false, false, BIAS, VT>(a, nz, s);
+  if (!mask) return launch_s<D, DV, FP8, MODE, kMaskNone, BIAS, VT>(a, nz, softcap, s);
+  if (a.wl >= 0) return launch_s<D, DV, FP8, MODE, kMaskWindow, BIAS, VT>(a, nz, softcap, s);
+  return launch_s<D, DV, FP8, MODE, kMaskRight, BIAS, VT>(a, nz, softcap, s);
 }
 
 template <int D, int DV, bool FP8, int MODE, bool VT>
