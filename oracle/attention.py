@@ -243,7 +243,7 @@ def attention_batch(q, k, v, scale, softcap=0.0, window_left=-1, window_right=-1
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
                      window_left=-1, window_right=-1, workers=1, sink_size=0, sink_logits=None,
-                     alibi_slopes=None, min_seqlen_q=0):
+                     alibi_slopes=None, min_seqlen_q=0, bias=None):
     """Varlen / group mode: sequences packed along the token axis.
 
     q [Tq, Hq, d], k/v [Tk, Hkv, d]; sequence s owns query tokens
@@ -252,6 +252,11 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
     arguments). Each sequence is sliced out and the batch definition applied.
     A sequence with Lq <= ``min_seqlen_q`` is skipped (the page's group-mode
     ``min_seqlen_q`` early exit): its rows stay NaN, i.e. not computed.
+    ``bias`` (elementwise, [Hq, Tq, Kmax] or None): the bias of q-head h, query
+    token t of sequence s and the sequence's key j is bias[h, t, j]; the rows
+    follow the packed query tokens (the group-mode bias offset
+    ``query_start * stride_bias`` of the Composable Kernel page's
+    ``operator()``), the columns are the sequence's own key index.
     Returns O [Tq, Hq, dv] and LSE [Hq, Tq].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -272,9 +277,12 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, softcap=0.0,
         if alibi_slopes is not None:
             sl = np.asarray(alibi_slopes, dtype=np.float64)
             sl = sl if sl.ndim == 1 else sl[s]
+        bs = None
+        if bias is not None:
+            bs = np.asarray(bias, dtype=np.float64)[:, cq[s]:cq[s + 1], :ck[s + 1] - ck[s]][None]
         os_, ls_ = attention_batch(qs, ks, vs, scale, softcap, window_left, window_right,
                                    workers=workers, sink_size=sink_size, sink_logits=sink_logits,
-                                   alibi_slopes=sl)
+                                   alibi_slopes=sl, bias=bs)
         o[cq[s]:cq[s + 1]] = os_[0].transpose(1, 0, 2)
         lse[:, cq[s]:cq[s + 1]] = ls_[0]
     return o, lse
@@ -299,7 +307,7 @@ def gather_paged(pool, block_table_row, seqlen, start=0):
 
 def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.0,
                     window_left=-1, window_right=-1, workers=1, decode=None, sink_size=0, sink_logits=None,
-                    alibi_slopes=None):
+                    alibi_slopes=None, bias=None):
     """Paged-KV mode: q [B, Hq, sq, d]; pools [num_pages, page_size, Hkv, d];
     block_table [B, max_pages] int; seqlens_k [B].
 
@@ -308,7 +316,10 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
     (default: cast to fp64) maps the gathered stored values to exact fp64, so a
     large pool can stay in its stored format and only the used pages are
     decoded; a (decode_k, decode_v) pair decodes the two pools differently
-    (per-tensor fp8 scales). Returns O [B, Hq, sq, dv] and LSE [B, Hq, sq].
+    (per-tensor fp8 scales). ``bias`` (elementwise, [B, Hq, sq, Kmax] or None):
+    the batch-mode bias of the Composable Kernel page, indexed by the request,
+    q-head, query row and the LOGICAL key index (token position), whatever page
+    holds the key. Returns O [B, Hq, sq, dv] and LSE [B, Hq, sq].
     """
     if decode is None:
         decode = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
@@ -325,8 +336,9 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
         if alibi_slopes is not None:
             sl = np.asarray(alibi_slopes, dtype=np.float64)
             sl = sl if sl.ndim == 1 else sl[b]
+        bb = None if bias is None else np.asarray(bias, dtype=np.float64)[b:b + 1]
         return b, attention_batch(q[b:b + 1], ks, vs, scale, softcap, window_left, window_right,
-                                  sink_size=sink_size, sink_logits=sink_logits, alibi_slopes=sl)
+                                  sink_size=sink_size, sink_logits=sink_logits, alibi_slopes=sl, bias=bb)
 
     for b, (ob, lb) in _map_pool(job, list(range(b_)), workers):
         o[b] = ob[0]
@@ -336,14 +348,16 @@ def attention_paged(q, k_pool, v_pool, block_table, seqlens_k, scale, softcap=0.
 
 def attention_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, scale, softcap=0.0,
                            window_left=-1, window_right=-1, kv_start=None, workers=1, decode=None, sink_size=0,
-                           sink_logits=None, alibi_slopes=None, min_seqlen_q=0):
+                           sink_logits=None, alibi_slopes=None, min_seqlen_q=0, bias=None):
     """Group mode over a paged KV cache (the group-mode page-block navigator of
     the Composable Kernel page, with ``is_gappy``: ``seqstart_k[b]`` then holds
     the logical position ``kv_l2p_offset`` of sequence b's first key in its page
     list). q [Tq, Hq, d] packed by cu_seqlens_q; sequence s reads seqlens_k[s]
     keys starting at token kv_start[s] (None: 0) of block table row s. Each
     sequence's keys are gathered into a contiguous copy and the varlen
-    definition applied. Returns O [Tq, Hq, dv] and LSE [Hq, Tq]."""
+    definition applied (``bias`` as there: [Hq, Tq, Kmax], columns the
+    sequence's own key index j, whatever its token position). Returns
+    O [Tq, Hq, dv] and LSE [Hq, Tq]."""
     n = len(cu_seqlens_q) - 1
     dec_k, dec_v = (decode, decode) if not isinstance(decode, tuple) else decode
     ks, vs, ck = [], [], [0]
@@ -360,4 +374,4 @@ def attention_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_tab
     v = np.concatenate(vs, 0) if vs else np.zeros((0,) + np.asarray(v_pool).shape[2:])
     return attention_varlen(q, k, v, cu_seqlens_q, np.array(ck), scale, softcap, window_left, window_right,
                             workers=workers, sink_size=sink_size, sink_logits=sink_logits,
-                            alibi_slopes=alibi_slopes, min_seqlen_q=min_seqlen_q)
+                            alibi_slopes=alibi_slopes, min_seqlen_q=min_seqlen_q, bias=bias)

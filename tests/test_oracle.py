@@ -643,3 +643,81 @@ def test_varlen_paged_fp8_pools_decoded_with_their_own_descales():
             bo, bl = brute_head(q[rows, h].tolist(), keys[:, 0].tolist(), vals[:, 0].tolist(), 0.6, 0.0, -1, 0)
             np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
             np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Elementwise bias in group (varlen) mode and over a paged pool: rows follow
+# the packed query tokens (group mode) or (request, row) (paged), columns the
+# sequence's own key index.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_varlen_bias_matches_brute_force(seed):
+    rng = np.random.default_rng(3000 + seed)
+    Hkv, ratio, d = 2, int(rng.integers(1, 3)), 3
+    Hq = Hkv * ratio
+    lq = [int(x) for x in rng.integers(0, 6, size=3)]
+    lk = [int(x) for x in rng.integers(0, 8, size=3)]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((cq[-1], Hq, d))
+    k = rng.standard_normal((ck[-1], Hkv, d))
+    v = rng.standard_normal((ck[-1], Hkv, d))
+    bias = rng.standard_normal((Hq, cq[-1], 9))
+    wl, wr = int(rng.choice([-1, 2])), int(rng.choice([-1, 0]))
+    o, lse = oracle.attention_varlen(q, k, v, cq, ck, 0.8, 0.0, wl, wr, bias=bias)
+    for s in range(3):
+        for h in range(Hq):
+            rows = slice(cq[s], cq[s + 1])
+            if lq[s]:
+                bo, bl = brute_head(q[rows, h].tolist(), k[ck[s]:ck[s + 1], h // ratio].tolist(),
+                                    v[ck[s]:ck[s + 1], h // ratio].tolist(), 0.8, 0.0, wl, wr, dv=d,
+                                    bias=[[float(bias[h, cq[s] + i, j]) for j in range(lk[s])] for i in range(lq[s])])
+                np.testing.assert_allclose(o[rows, h], np.array(bo).reshape(lq[s], d), atol=1e-12, rtol=0)
+                fin = np.isfinite(bl)
+                np.testing.assert_array_equal(np.isinf(lse[h, rows]), ~fin)
+                np.testing.assert_allclose(lse[h, rows][fin], np.array(bl)[fin], atol=1e-12, rtol=0)
+
+
+def test_paged_bias_follows_logical_key_positions():
+    rng = np.random.default_rng(3100)
+    P, Hq, Hkv, d, sq, lens = 3, 4, 2, 4, 2, [7, 4]
+    n = sum(-(-L // P) for L in lens)
+    kp = rng.standard_normal((n, P, Hkv, d))
+    vp = rng.standard_normal((n, P, Hkv, d))
+    perm = rng.permutation(n)
+    table = np.zeros((2, 3), dtype=np.int64)
+    table[0, :3], table[1, :2] = perm[:3], perm[3:5]
+    q = rng.standard_normal((2, Hq, sq, d))
+    bias = rng.standard_normal((2, Hq, sq, 8))
+    o, lse = oracle.attention_paged(q, kp, vp, table, lens, 0.5, 0.0, -1, 0, bias=bias)
+    for b, L in enumerate(lens):
+        keys = [kp[table[b, t // P], t % P] for t in range(L)]
+        vals = [vp[table[b, t // P], t % P] for t in range(L)]
+        for h in range(Hq):
+            bo, bl = brute_head(q[b, h].tolist(), [x[h // 2].tolist() for x in keys], [x[h // 2].tolist() for x in vals],
+                                0.5, 0.0, -1, 0, bias=bias[b, h, :, :L].tolist())
+            np.testing.assert_allclose(o[b, h], np.array(bo), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[b, h], np.array(bl), atol=1e-12, rtol=0)
+
+
+def test_varlen_paged_bias_uses_the_sequence_key_index():
+    rng = np.random.default_rng(3200)
+    P, n_pages, Hq, Hkv, d = 4, 16, 2, 1, 3
+    k_pool = rng.standard_normal((n_pages, P, Hkv, d))
+    v_pool = rng.standard_normal((n_pages, P, Hkv, d))
+    lens_q, lens_k, starts = [3, 2], [6, 5], [5, 2]
+    table = np.stack([rng.permutation(n_pages)[:4] for _ in range(2)])
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    q = rng.standard_normal((cq[-1], Hq, d))
+    bias = rng.standard_normal((Hq, cq[-1], 7))
+    o, lse = oracle.attention_varlen_paged(q, k_pool, v_pool, cq, lens_k, table, 0.6, 0.0, -1, 0, kv_start=starts,
+                                           bias=bias)
+    for s in range(2):
+        keys = [k_pool[table[s, (starts[s] + j) // P], (starts[s] + j) % P, 0] for j in range(lens_k[s])]
+        vals = [v_pool[table[s, (starts[s] + j) // P], (starts[s] + j) % P, 0] for j in range(lens_k[s])]
+        rows = slice(cq[s], cq[s + 1])
+        for h in range(Hq):
+            bo, bl = brute_head(q[rows, h].tolist(), [x.tolist() for x in keys], [x.tolist() for x in vals], 0.6, 0.0,
+                                -1, 0, bias=bias[h, rows, :lens_k[s]].tolist())
+            np.testing.assert_allclose(o[rows, h], np.array(bo), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse[h, rows], np.array(bl), atol=1e-12, rtol=0)

@@ -65,6 +65,13 @@ MUTANTS = {
         "vs = dec_v(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]",
         "vs = dec_k(gather_paged(v_pool, block_table[b], seqlens_k[b]))[None]"),
     "varlen-paged V pool decoded with the K decoder": ("kk, vv = dec_k(kk), dec_v(vv)", "kk, vv = dec_k(kk), dec_k(vv)"),
+    "varlen bias rows from the sequence's own row 0": (
+        "bs = np.asarray(bias, dtype=np.float64)[:, cq[s]:cq[s + 1], :ck[s + 1] - ck[s]][None]",
+        "bs = np.asarray(bias, dtype=np.float64)[:, 0:cq[s + 1] - cq[s], :ck[s + 1] - ck[s]][None]"),
+    "paged bias dropped": ("        bb = None if bias is None else np.asarray(bias, dtype=np.float64)[b:b + 1]\n",
+                           "        bb = None\n"),
+    "varlen-paged bias dropped": ("alibi_slopes=alibi_slopes, min_seqlen_q=min_seqlen_q, bias=bias)",
+                                  "alibi_slopes=alibi_slopes, min_seqlen_q=min_seqlen_q, bias=None)"),
     "paged K pool decoded with the V decoder": (
         "ks = dec_k(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]",
         "ks = dec_v(gather_paged(k_pool, block_table[b], seqlens_k[b]))[None]"),
