@@ -150,10 +150,18 @@ typedef struct {
                           bias[b*bias_stride[0] + h] (bias_stride[0] = 0: one slope per head
                           for every b); the bias of key j for query row i is
                           -slope * |i + Lk - Lq - j| (bottom-right aligned). In varlen mode b
-                          is the sequence index. ELEMENTWISE: batch-mode prefill shapes only
-                          (attn_fwd with sq*Hq/Hkv > 16); the bias of (b, h, i, j) at
+                          is the sequence index. ELEMENTWISE (every entry point and path,
+                          the bias kernel arguments of the Composable Kernel page): in batch
+                          and paged modes the bias of (b, h, i, j) is at
                           bias[b*bias_stride[0] + h*bias_stride[1] + i*bias_stride[2] + j],
-                          16-byte aligned with bias_stride[2] a multiple of 4. */
+                          j the logical key index (its token position; paged: whatever page
+                          holds it); in the varlen modes (group mode) the bias of q-head h,
+                          packed query token t and the sequence's key j is at
+                          bias[h*bias_stride[1] + t*bias_stride[2] + j] (the page's
+                          query_start * stride_bias row offset; bias_stride[0] unused). Only
+                          elements of used rows (i < Lq) and keys (j < Lk) are read, as
+                          aligned 16-byte blocks of 4 keys: the base must be 16-byte aligned
+                          and every stride a multiple of 4 (0 broadcasts that index). */
   int64_t bias_stride[3];
   float o_scale;       /* FP8 output only: O is stored as the saturating E4M3FN conversion
                           (round to nearest even, clamped to +-448) of O * o_scale, the

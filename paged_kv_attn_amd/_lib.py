@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_LIBRARY, when set, names another build of the same library to load
+# instead (for example a host-sanitizer build of the C ABI)
+LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
 ATTN_BIAS_NONE, ATTN_BIAS_ELEMENTWISE, ATTN_BIAS_ALIBI = 0, 1, 2
@@ -76,18 +78,23 @@ _SIGNATURES = {
 _lib = None
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Load a build of libattn at path with the C ABI's signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_attn_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_attn_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(LIB_PATH)
     return _lib
 
 

@@ -50,12 +50,15 @@ def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, 
         p.bias = alibi_slopes.data_ptr()
         p.bias_stride[0] = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
     if bias is not None:
-        if bias.dtype != torch.float32 or bias.dim() != 4 or bias.stride(-1) != 1:
-            raise TypeError("bias must be float32 [B|1, Hq|1, sq, sk] with unit stride over keys")
+        if bias.dtype != torch.float32 or bias.dim() not in (3, 4) or bias.stride(-1) != 1:
+            raise TypeError("bias must be float32 [B|1, Hq|1, sq, Kmax] (batch, paged) or [Hq|1, Tq, Kmax] (varlen) "
+                            "with unit stride over keys")
         p.bias_type = _lib.ATTN_BIAS_ELEMENTWISE
         p.bias = bias.data_ptr()
-        for i in range(3):   # broadcast (size-1) dims read with stride 0
-            p.bias_stride[i] = 0 if bias.shape[i] == 1 else bias.stride(i)
+        # broadcast (size-1) dims read with stride 0; a 3-d (varlen) bias has no batch stride
+        dims = range(3) if bias.dim() == 4 else range(1, 3)
+        for i, ax in zip(dims, range(bias.dim() - 1)):
+            p.bias_stride[i] = 0 if bias.shape[ax] == 1 else bias.stride(ax)
     return p
 
 
@@ -200,6 +203,7 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
     _check_index("seqused_q", seqused_q, q, B)
     _check_index("seqused_k", seqused_k, q, B)
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
+    _need(bias is None or bias.dim() == 4, "a batch-mode bias is 4-d [B|1, Hq|1, sq, sk]")
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (B, Hq, sq, dv), out_dtype, q)
     _check_lse(lse, (B, Hq, sq), q)
@@ -233,11 +237,13 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
                     causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
                     return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None,
-                    o_scale=1.0, min_seqlen_q=0):
+                    o_scale=1.0, min_seqlen_q=0, bias=None):
     """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
     on the device. Sequences with at most ``min_seqlen_q`` query tokens are
-    skipped: their rows of out / lse are left as they were. Returns
-    (out [Tq, Hq, d], lse [Hq, Tq] or None)."""
+    skipped: their rows of out / lse are left as they were. ``bias`` (fp32
+    [Hq|1, Tq, Kmax]): the bias of q-head h, packed query token t and the
+    sequence's key j at bias[h, t, j]. Returns (out [Tq, Hq, d], lse [Hq, Tq]
+    or None)."""
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
@@ -249,13 +255,14 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     _need(n >= 0, "cu_seqlens_q needs at least one entry")
     _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
     _check_index("cu_seqlens_k", cu_seqlens_k, q, n + 1)
-    _check_params_tensors(q, sink_logits, None, alibi_slopes)
+    _check_params_tensors(q, sink_logits, bias, alibi_slopes)
+    _need(bias is None or bias.dim() == 3, "a varlen bias is 3-d [Hq|1, Tq, Kmax]")
     dv = v.shape[2]
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (Tq, Hq, dv), out_dtype, q)
     _check_lse(lse, (Hq, Tq), q)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
-                alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
+                bias=bias, alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     p.min_seqlen_q = int(min_seqlen_q)
     if dv != d:
         p.head_dim_v = dv
@@ -300,12 +307,14 @@ def _set_v_pool(p, d, k_pool, v_pool):
 
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
                    softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
-                   workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None, o_scale=1.0):
+                   workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None, o_scale=1.0,
+                   bias=None):
     """Paged KV cache. q [B, Hq, sq, d]; k_pool [num_pages, page_size, Hkv, d],
     v_pool [num_pages, page_size, Hkv, dv] (any strides, last dim contiguous);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
     (sq * Hq / Hkv <= 16, bf16 or fp8) run the split-KV decode kernel; longer ones
-    (bf16 or fp8, page_size a multiple of 64) the prefill kernel. Returns (out, lse)."""
+    (bf16 or fp8, page_size a multiple of 64) the prefill kernel. ``bias`` (fp32
+    [B|1, Hq|1, sq, Kmax]) is indexed by the logical key position. Returns (out, lse)."""
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     dv = v_pool.shape[3]
@@ -315,7 +324,8 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     _check_pools(q, d, k_pool, v_pool)
     _check_table(block_table, q, B)
     _check_index("seqlens_k", seqlens_k, q, B)
-    _check_params_tensors(q, sink_logits, None, alibi_slopes)
+    _check_params_tensors(q, sink_logits, bias, alibi_slopes)
+    _need(bias is None or bias.dim() == 4, "a paged bias is 4-d [B|1, Hq|1, sq, Kmax]")
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (B, Hq, sq, dv), out_dtype, q)
     _check_lse(lse, (B, Hq, sq), q)
@@ -323,7 +333,7 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     # request by stride(0) * page_size keys (its split plan too)
     W = block_table.stride(0)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
-                alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
+                bias=bias, alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     _set_v_pool(p, d, k_pool, v_pool)
     if out is None:
         out = torch.empty((B, Hq, sq, dv), dtype=out_dtype, device=q.device)
@@ -343,12 +353,13 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
 def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_table, max_seqlen_q, *, kv_start=None,
                           scale=None, causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None,
                           lse=None, return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None,
-                          out_dtype=None, o_scale=1.0, min_seqlen_q=0):
+                          out_dtype=None, o_scale=1.0, min_seqlen_q=0, bias=None):
     """Varlen queries over a paged KV cache. q [Tq, Hq, d] with cu_seqlens_q
     int32 [n+1]; k_pool [num_pages, page_size, Hkv, d], v_pool [.., dv] (any strides);
     block_table int32 [n, W]; seqlens_k int32 [n]; kv_start (int32 [n] or
     None): logical position of each sequence's first key in its page list
-    (a negative start gives that sequence NaN rows). Returns
+    (a negative start gives that sequence NaN rows). ``bias`` as for
+    attn_fwd_varlen ([Hq|1, Tq, Kmax], the sequence's key index j). Returns
     (out [Tq, Hq, dv], lse [Hq, Tq] or None)."""
     Tq, Hq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
@@ -364,12 +375,13 @@ def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_tabl
     _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
     _check_index("seqlens_k", seqlens_k, q, n)
     _check_index("kv_start", kv_start, q, n)
-    _check_params_tensors(q, sink_logits, None, alibi_slopes)
+    _check_params_tensors(q, sink_logits, bias, alibi_slopes)
+    _need(bias is None or bias.dim() == 3, "a varlen bias is 3-d [Hq|1, Tq, Kmax]")
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (Tq, Hq, v_pool.shape[3]), out_dtype, q)
     _check_lse(lse, (Hq, Tq), q)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, 0, sink_size, sink_logits,
-                alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
+                bias=bias, alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
     p.min_seqlen_q = int(min_seqlen_q)
     _set_v_pool(p, d, k_pool, v_pool)
     if out is None:

@@ -76,6 +76,8 @@ void set_bias(const attn_params_t* p, float c_exp2, attn::PrefillArgs* a) {
 void set_bias(const attn_params_t* p, float c_exp2, attn::DecodeArgs* a) {
   a->alibi = p->bias_type == ATTN_BIAS_ALIBI ? p->bias : nullptr;
   a->alibi_sb = p->bias_stride[0];
+  a->bias = p->bias_type == ATTN_BIAS_ELEMENTWISE ? p->bias : nullptr;
+  a->bias_sb = p->bias_stride[0]; a->bias_sh = p->bias_stride[1]; a->bias_sr = p->bias_stride[2];
   a->bias_mul = 1.4426950408889634f / c_exp2;
 }
 
@@ -121,8 +123,9 @@ attn_status_t check_params(const attn_params_t* p, int d) {
     if (p->bias_stride[0] < 0 || p->bias_stride[1] < 0 || p->bias_stride[2] < 0)
       return fail(ATTN_EINVAL, "bias strides must be >= 0");
     if ((uintptr_t)p->bias & 3u) return fail(ATTN_EINVAL, "bias is not 4-byte aligned");
-    if (p->bias_type == ATTN_BIAS_ELEMENTWISE && (((uintptr_t)p->bias & 15u) || p->bias_stride[2] % 4))
-      return fail(ATTN_EINVAL, "an elementwise bias needs a 16-byte aligned base and a row stride multiple of 4");
+    if (p->bias_type == ATTN_BIAS_ELEMENTWISE &&
+        (((uintptr_t)p->bias & 15u) || p->bias_stride[0] % 4 || p->bias_stride[1] % 4 || p->bias_stride[2] % 4))
+      return fail(ATTN_EINVAL, "an elementwise bias needs a 16-byte aligned base and strides that are multiples of 4");
   }
   if (p->min_seqlen_q < 0) return fail(ATTN_EINVAL, "min_seqlen_q must be >= 0");
   if (p->head_dim_v != 0 && p->head_dim_v != 64 && p->head_dim_v != 128)
@@ -424,8 +427,6 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   }
 
   if (takes_decode_path(p->in_dtype, sq, ratio)) {
-    if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
-      return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
     TRY(check_row_span("k", k_stride[2], eb, kDecodeGranRows));
     if (p->v_layout == ATTN_V_ROW_MAJOR) TRY(check_row_span("v", v_stride[2], eb, kDecodeGranRows));
     const int dv = dim_v(p, d);
@@ -489,12 +490,6 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.wl = p->window_left; a.wr = p->window_right;
   a.sink_size = p->sink_size; a.sink_logits = p->sink_logits;
   set_bias(p, c_exp2, &a);
-  if (p->bias_type == ATTN_BIAS_ELEMENTWISE) {
-    // bytes from one batch entry's bias base to its last element (32-bit offsets in the kernel)
-    const int64_t ext = ((int64_t)(Hq - 1) * p->bias_stride[1] + (int64_t)(sq - 1) * p->bias_stride[2] + sk) * 4;
-    if (ext >= ((int64_t)1 << 31)) return fail(ATTN_EINVAL, "elementwise bias spans more than 2 GiB per batch entry");
-    a.bias_bytes = (uint32_t)ext;
-  }
   log_prefill("attn_fwd", p, a, d, dim_v(p, d), B, sq, sk);
   return launched(attn::launch_prefill(a, d, dim_v(p, d), p->in_dtype, attn::kPrefillBatch, B, s));
 }
@@ -509,8 +504,6 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   (void)max_seqlen_k;
   TRY(check_params(p, d));
   TRY(check_mode_fields(p, false, true));
-  if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
-    return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "fp32 inputs are supported in batch mode only");
   if (n < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0)
     return fail(ATTN_EINVAL, "bad sizes n=%d total_q=%d max_q=%d max_k=%d Hq=%d Hkv=%d", n, total_q, max_seqlen_q,
@@ -576,8 +569,6 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
   if (page_size <= 0 || page_size % 32) return fail(ATTN_ENOTSUP, "page_size %d is not a positive multiple of 32", page_size);
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "paged KV supports bf16 and fp8 inputs");
-  if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
-    return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   const int ratio = Hq / Hkv;
   const bool decode_shape = takes_decode_path(p->in_dtype, sq, ratio);
   if (!decode_shape && page_size % 64)
@@ -681,8 +672,6 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
   if (dv != d && v_st == kv_stride)
     return fail(ATTN_EINVAL, "head_dim_v != d in paged mode needs v_pool_stride (the V pool's strides)");
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "paged KV supports bf16 and fp8 inputs");
-  if (p->bias_type == ATTN_BIAS_ELEMENTWISE)
-    return fail(ATTN_ENOTSUP, "an elementwise bias is supported on batch-mode prefill shapes only");
   if (n < 0 || total_q < 0 || max_seqlen_q < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
     return fail(ATTN_EINVAL, "bad sizes n=%d total_q=%d max_q=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", n,
                 total_q, max_seqlen_q, Hq, Hkv, block_table_stride, num_pages);

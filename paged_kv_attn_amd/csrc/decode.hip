@@ -151,6 +151,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   // ALiBi slope of this lane's (request, q-head), in kernel logit units
   const float alibi_k = a.alibi ? a.alibi[(int64_t)b * a.alibi_sb + hq] * a.bias_mul : 0.0f;
+  // elementwise bias: this lane's row (lanes past the used rows read row 0 of
+  // their head, never stored); keys are read as aligned 16-byte blocks of 4,
+  // clamped to the block holding key Lk - 1
+  const float* bias_row =
+      a.bias ? a.bias + (int64_t)b * a.bias_sb + (int64_t)hq * a.bias_sh + (int64_t)(row_ok ? pos : 0) * a.bias_sr
+             : nullptr;
+  const int bias_last = (Lk - 1) & ~3;
 
   // The split's page ids, one per lane (a split spans at most 64 pages).
   const int p_first = PAGED ? t0 / a.page_size : 0;
@@ -300,6 +307,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       }
     }
     // lane (column qc, group j4) holds keys gs + 16 kb + 4 j4 + r
+    U128 bv[2] = {};
+    if (bias_row) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) bv[kb] = *(const U128*)(bias_row + min(gs + 16 * kb + 4 * j4, bias_last));
+    }
     float mt = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -309,6 +321,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         if (SOFTCAP) x = softcap_logit(x, 2.0f * kLog2e * a.softcap_pre, a.softcap_post);
         const int j = gs + 16 * kb + 4 * j4 + r;
         if (a.alibi) x = __builtin_fmaf(-alibi_k, __builtin_fabsf((float)(pos + off - j)), x);
+        if (bias_row) x = __builtin_fmaf(__builtin_bit_cast(float, (&bv[kb].x)[r]), a.bias_mul, x);
         x = ((j >= lim_lo || j < a.sink_size) && j <= lim_hi) ? x : kNegInf;
         st[kb][r] = x;
         mt = __builtin_fmaxf(mt, x);

@@ -48,8 +48,7 @@ struct PrefillArgs {
   const float* sink_logits;   // nullable [hq]: extra softmax-denominator term per q-head
   int bias_type;              // attn_bias_t
   const float* bias;          // ALiBi slopes or elementwise values (see attn.h)
-  int64_t bias_sb, bias_sh, bias_sr;
-  uint32_t bias_bytes;        // elementwise: bytes of one batch entry's bias (reads past it return 0)
+  int64_t bias_sb, bias_sh, bias_sr;  // elementwise: batch (group mode: unused), head, query row
   float bias_mul;             // natural-log logit units -> the kernel's logit units
   const int32_t* cache_idx;   // batch mode, nullable: K/V batch entry of each batch entry
   int cache_count;            // K/V batch entries (indices outside [0, cache_count) read no keys)
@@ -81,6 +80,8 @@ struct DecodeArgs {
   int sink_size;              // keys j < sink_size ignore the left bound
   const float* alibi;         // nullable: ALiBi slope of (b, q-head) at alibi[b*alibi_sb + hq]
   int64_t alibi_sb;
+  const float* bias;          // nullable: elementwise bias of (b, q-head, query row, key) at
+  int64_t bias_sb, bias_sh, bias_sr;  // bias[b*bias_sb + hq*bias_sh + row*bias_sr + key]
   float bias_mul;             // natural-log logit units -> the kernel's logit units
   float* part_o;              // [B][hkv][n_splits][m_rows][dv] fp32
   float* part_lse;            // [B][hkv][n_splits][m_rows]

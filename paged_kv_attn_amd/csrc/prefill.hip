@@ -151,6 +151,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   constexpr bool PAGED = MODE == kPrefillPaged || VPAGED;     // K/V rows through the block table
   int Lq, Lk;
   int64_t q_off, k_off, v_off, o_off, lse_off;
+  int64_t bias_off = 0;  // elementwise bias: element offset of this sequence's row 0 (all heads)
   int kv0 = 0;       // logical position of key 0 in the sequence's page list
   bool bad = false;  // varlen-paged: a negative key start -> NaN rows, nothing read
   if (VARLEN) {
@@ -163,6 +164,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     v_off = (int64_t)k0 * a.v_sr;
     o_off = (int64_t)q0 * a.o_sr;
     lse_off = q0;
+    bias_off = (int64_t)q0 * a.bias_sr;  // group mode: rows follow the packed query tokens
   } else if (VPAGED) {
     const int q0 = a.cu_q[z];
     Lq = a.cu_q[z + 1] - q0;
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     v_off = 0;
     o_off = (int64_t)q0 * a.o_sr;
     lse_off = q0;
+    bias_off = (int64_t)q0 * a.bias_sr;
   } else if (PAGED) {
     Lq = a.sq;
     Lk = a.seqused_k[z];
@@ -187,6 +190,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     v_off = 0;
     o_off = (int64_t)z * a.o_sb;
     lse_off = (int64_t)z * a.lse_sb;
+    bias_off = (int64_t)z * a.bias_sb;
   } else {
     Lq = a.seqused_q ? a.seqused_q[z] : a.sq;
     Lk = a.seqused_k ? a.seqused_k[z] : a.sk;
@@ -201,6 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     v_off = (int64_t)kz * a.v_sb;
     o_off = (int64_t)z * a.o_sb;
     lse_off = (int64_t)z * a.lse_sb;
+    bias_off = (int64_t)z * a.bias_sb;
   }
   if (!a.k || !a.v) Lk = 0;  // NULL K or V: no keys, whatever the length arrays say
   const int ratio = a.ratio;
@@ -234,8 +239,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
   // ALiBi slope of this row's (batch entry or sequence, q-head), in kernel logit units
   const float alibi_k = BIAS == kBiasAlibi ? a.bias[(int64_t)z * a.bias_sb + hq] * a.bias_mul : 0.0f;
-  // elementwise bias: this row's values, addressed from the batch entry's base
-  const int bias_lane = BIAS == kBiasElem ? (int)((int64_t)hq * a.bias_sh + (int64_t)pos * a.bias_sr) * 4 : 0;
+  // elementwise bias: this lane's row (64-bit address). Lanes past the tile's
+  // used rows read row 0 of their head (in the tensor; never stored). Keys are
+  // read as aligned 16-byte blocks of 4, clamped to the block holding key
+  // Lk - 1, so every load lies in a block that holds a used element.
+  const float* bias_row = BIAS == kBiasElem
+                              ? a.bias + bias_off + (int64_t)hq * a.bias_sh + (int64_t)(row_ok ? pos : 0) * a.bias_sr
+                              : nullptr;
+  const int bias_last = (Lk - 1) & ~3;
 
   // ---- Q fragment, resident in registers for the whole key loop ----
   // B operand of S^T = K Q^T. bf16: lane (row lane%32, half h) holds Q[row][16s + 8h .. +7] for step s of
@@ -525,14 +536,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
     }
     if (BIAS == kBiasElem) {
-      // 16-byte loads of 4 consecutive keys; reads past the bias tensor return 0
-      const __amdgpu_buffer_rsrc_t br =
-          make_rsrc((const char*)a.bias + (int64_t)z * a.bias_sb * 4, a.bias_bytes);
+      // 16-byte loads of 4 consecutive keys (keys at or past Lk are masked below)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         U128 bv[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) bv[g4] = buf_load16(br, bias_lane + 4 * (j0 + kHStep * h + key_rel(b, 4 * g4)));
+        for (int g4 = 0; g4 < 4; ++g4)
+          bv[g4] = *(const U128*)(bias_row + min(j0 + kHStep * h + key_rel(b, 4 * g4), bias_last));
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t w = (&bv[r >> 2].x)[r & 3];
@@ -811,8 +821,7 @@ hipError_t launch_b(const PrefillArgs& a, int nz, bool mask, bool softcap, hipSt
 template <int D, int DV, bool FP8, int MODE, bool VT>
 hipError_t launch_v(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
   if (a.bias_type == kBiasAlibi) return launch_b<D, DV, FP8, MODE, kBiasAlibi, VT>(a, nz, mask, softcap, s);
-  if (MODE == kPrefillBatch && a.bias_type == kBiasElem)
-    return launch_b<D, DV, FP8, MODE, (MODE == kPrefillBatch ? kBiasElem : kBiasNone), VT>(a, nz, mask, softcap, s);
+  if (a.bias_type == kBiasElem) return launch_b<D, DV, FP8, MODE, kBiasElem, VT>(a, nz, mask, softcap, s);
   return launch_b<D, DV, FP8, MODE, kBiasNone, VT>(a, nz, mask, softcap, s);
 }
 

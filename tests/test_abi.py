@@ -205,11 +205,13 @@ def test_bias_validation():
     assert _fwd(p) == 1 and "16-byte" in _err()
     p = _params(bias_type=_lib.ATTN_BIAS_ELEMENTWISE, bias=0x10000)
     p.bias_stride[2] = 6
-    assert _fwd(p) == 1 and "multiple of 4" in _err()
+    assert _fwd(p) == 1 and "multiples of 4" in _err()
     p = _params(in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32, bias_type=_lib.ATTN_BIAS_ALIBI, bias=0x10000)
     assert _fwd(p) == 2 and "bf16 or fp8" in _err()
-    p = _params(bias_type=_lib.ATTN_BIAS_ELEMENTWISE, bias=0x10000)       # decode shape
-    assert _paged(p) == 2 and "batch-mode prefill" in _err()
+    for i in (0, 1):      # every stride a multiple of 4 (rows stay 16-byte aligned)
+        p = _params(bias_type=_lib.ATTN_BIAS_ELEMENTWISE, bias=0x10000)
+        p.bias_stride[i] = 2
+        assert _paged(p) == 1 and "multiples of 4" in _err()
 
 
 def test_sink_validation():

@@ -1,6 +1,7 @@
-"""GPU parity of the additive logit bias: ALiBi on every path (batch, varlen and
-paged prefill, split-KV decode) and the elementwise bias on batch-mode prefill
-(full and broadcast tensors), against the fp64 oracle."""
+"""GPU parity of the additive logit bias against the fp64 oracle: ALiBi and the
+elementwise bias on every path (batch, varlen, paged and varlen-over-paged
+prefill, split-KV decode, contiguous and paged), with full and broadcast
+bias tensors."""
 
 import numpy as np
 import pytest
@@ -69,3 +70,66 @@ def test_prefill_elementwise_bias(shape, causal):
     out, lse = C.run_dense(case, bias=store)
     O, LSE = C.oracle_dense(case, bias=bias.double().cpu().numpy())
     C.assert_parity(out, lse, O, LSE, "bf16", f"elementwise bias {shape}")
+
+
+# ---------------------------------------------------------------------------
+# The elementwise bias on every other path: split-KV decode (contiguous and
+# paged), varlen (group mode: rows follow the packed query tokens), paged
+# prefill and varlen over a paged pool (columns: the sequence's key index).
+# ---------------------------------------------------------------------------
+
+def _padded_bias(shape, seed, broadcast_dim=None):
+    """fp32 bias of `shape` whose key axis is stored with a row stride padded
+    to a multiple of 4 floats (and +4), optionally broadcast along one dim."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    store_shape = list(shape)
+    if broadcast_dim is not None:
+        store_shape[broadcast_dim] = 1
+    kpad = -(-shape[-1] // 4) * 4 + 4
+    store = torch.randn(store_shape[:-1] + [kpad], generator=g, device=DEV)[..., :shape[-1]]
+    full = store.expand(*shape)
+    return store, full.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,sq,Hq,Hkv,window", [("bf16", 1, 32, 8, (-1, -1)), ("bf16", 3, 16, 4, (-1, 0)),
+                                                    ("fp8", 2, 8, 2, (100, 0))])
+def test_decode_elementwise_bias(dtype, sq, Hq, Hkv, window):
+    su_k = [1500, 33, 700]
+    case = synth.dense_case(3, Hq, Hkv, sq, 1500, 128, dtype, seed=70 + sq, window=window, seqused_k=su_k, device=DEV)
+    store, full = _padded_bias((3, Hq, sq, 1500), 71)
+    out, lse = C.run_dense(case, bias=store, kv_split_tokens=256)
+    O, LSE = C.oracle_dense(case, bias=full)
+    C.assert_parity(out, lse, O, LSE, dtype, f"decode elementwise bias {dtype} sq={sq}")
+
+
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("fp8", False)])
+def test_varlen_elementwise_bias(dtype, causal):
+    lq, lk = [300, 0, 77, 640], [300, 5, 150, 640]
+    case = synth.varlen_case(lq, lk, 8, 2, 128, dtype, seed=72, causal=causal, device=DEV)
+    store, full = _padded_bias((8, sum(lq), max(lk)), 73)
+    out, lse = C.run_varlen(case, bias=store)
+    O, LSE = C.oracle_varlen(case, bias=full)
+    C.assert_parity(out, lse.T, O, LSE.T, dtype, f"varlen elementwise bias {dtype}")
+
+
+@pytest.mark.parametrize("sq,page,broadcast", [(1, 64, None), (4, 32, 1), (200, 64, None), (130, 128, 0)])
+def test_paged_elementwise_bias(sq, page, broadcast):
+    lens = [1500, 400, 65]
+    case = synth.paged_case(lens, sq, 32, 8, 128, page, "bf16", seed=74 + sq, causal=sq > 1, device=DEV)
+    W = case.meta["table_width"]
+    store, full = _padded_bias((3, 32, sq, W * page), 75, broadcast)
+    out, lse = C.run_paged(case, bias=store, kv_split_tokens=128)
+    O, LSE = C.oracle_paged(case, bias=full)
+    C.assert_parity(out, lse, O, LSE, "bf16", f"paged elementwise bias sq={sq} page={page} bcast={broadcast}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_varlen_paged_elementwise_bias(dtype):
+    from tests.test_gpu_varlen_paged import _oracle, _run
+    lq, lk = [300, 1, 77, 200], [300, 40, 200, 700]
+    case = synth.varlen_paged_case(lq, lk, [0, 70, 5, 127], 8, 2, 128, page_size=64, dtype=dtype, seed=76,
+                                   device=DEV)
+    store, full = _padded_bias((8, sum(lq), max(lk)), 77)
+    out, lse = _run(case, bias=store)
+    O, LSE = _oracle(case, bias=full)
+    C.assert_parity(out, lse.T, O, LSE.T, dtype, f"varlen-paged elementwise bias {dtype}")

@@ -4,8 +4,8 @@ Each case draws one combination: the mode (batch, varlen, paged, varlen over a
 paged pool), bf16 or fp8 inputs, d and head_dim_v from {64, 128}, the GQA ratio,
 ragged lengths on either side of the decode/prefill dispatch boundary, the
 mask (none, causal, two-sided window), the logit soft-cap, attention sinks
-(streaming sink keys and per-head sink logits), ALiBi slopes, head-major page
-storage and column-major V. The per-option
+(streaming sink keys and per-head sink logits), ALiBi slopes, an elementwise
+bias, head-major page storage and column-major V. The per-option
 tests pin each option alone; these catch interactions between them."""
 
 import numpy as np
@@ -53,6 +53,18 @@ def _extras(o):
     return gpu, ref
 
 
+def _bias(o, seed, shape):
+    """An elementwise bias of `shape` for a quarter of the draws (its own
+    generator, so the other draws stay as they were): (gpu tensor with a
+    padded key stride, fp64 array for the oracle), or (None, None)."""
+    rb = np.random.default_rng(20_000 + seed)
+    if rb.random() >= 0.25 or o["alibi"] is not None:
+        return None, None
+    kpad = -(-shape[-1] // 4) * 4 + 4
+    xp = rb.standard_normal(tuple(shape[:-1]) + (kpad,)).astype(np.float32)
+    return torch.tensor(xp, device=DEV)[..., :shape[-1]], xp[..., :shape[-1]].astype(np.float64)
+
+
 def _mask(o):
     return dict(causal=o["causal"], window=o["window"], softcap=o["softcap"])
 
@@ -75,6 +87,10 @@ def test_random_option_mix(seed):
         if colmajor:
             sk = 8 * max(1, sk // 8)
         c = synth.dense_case(B, hq, hkv, sq_max, sk, d, dtype, seed=seed, device=DEV, **_mask(o))
+        bg, br = _bias(o, seed, (B, hq, sq_max, sk))
+        if bg is not None:
+            gpu["bias"], ref["bias"] = bg, br
+            what += " bias"
         if dv != d:
             cv = synth.dense_case(B, hq, hkv, sq_max, sk, dv, dtype, seed=seed + 1, device=DEV, **_mask(o))
             c.t["v"], c.descale["v"] = cv.t["v"], cv.descale["v"]
@@ -97,6 +113,10 @@ def test_random_option_mix(seed):
             c.t["v"], c.descale["v"] = cv.t["v"], cv.descale["v"]
         if sum(lq) == 0:
             return
+        bg, br = _bias(o, seed, (hq, sum(lq), max(lk) + 1))
+        if bg is not None:
+            gpu["bias"], ref["bias"] = bg, br
+            what += " bias"
         out, lse = C.run_varlen(c, **gpu)
         O, LSE = C.oracle_varlen(c, **ref)
         C.assert_parity(out, lse.T, O, LSE.T, dtype, what)
@@ -111,6 +131,10 @@ def test_random_option_mix(seed):
             cv = synth.paged_case(lens, sq_max, hq, hkv, dv, page, dtype, seed=seed, device=DEV, head_major=hm,
                                   **_mask(o))
             c.t["v_pool"], c.descale["v"] = cv.t["v_pool"], cv.descale["v"]
+        bg, br = _bias(o, seed, (B, hq, sq_max, c.meta["table_width"] * page))
+        if bg is not None:
+            gpu["bias"], ref["bias"] = bg, br
+            what += " bias"
         out, lse = C.run_paged(c, kv_split_tokens=int(r.choice([0, 64, 256])), **gpu)
         O, LSE = C.oracle_paged(c, **ref)
         C.assert_parity(out, lse, O, LSE, dtype, what)
@@ -129,6 +153,10 @@ def test_random_option_mix(seed):
             cv = synth.varlen_paged_case(lq, lk, starts, hq, hkv, dv, page_size=page, dtype=dtype, seed=seed,
                                          device=DEV, head_major=hm, **_mask(o))
             vp, dsv = cv.t["v_pool"], cv.descale["v"]
+        bg, br = _bias(o, seed, (hq, sum(lq), max(lk) + 1))
+        if bg is not None:
+            gpu["bias"], ref["bias"] = bg, br
+            what += " bias"
         t, ds = c.t, c.descale
         out, lse = pk.attn_fwd_varlen_paged(t["q"], t["k_pool"], vp, t["cu_seqlens_q"], t["seqlens_k"],
                                             t["block_table"], c.meta["max_q"], kv_start=t["kv_start"],
