@@ -182,11 +182,18 @@ typedef struct {
                           and split-KV decode shapes alike) and by attn_fwd_varlen, BF16 / FP8
                           only; V's rows then have head_dim_v elements and O's rows too. The
                           paged entry points need v_pool_stride for it (the pools' rows differ). */
-  int v_layout;        /* attn_v_layout_t. ATTN_V_COL_MAJOR (keys contiguous, v_stride[2] the
-                          stride between head-dim rows) is supported by attn_fwd (prefill and
-                          split-KV decode shapes) with BF16 inputs and head_dim_v = d; sk must be a multiple of 8
-                          and (head_dim_v - 1) * v_stride[2] * 2 + 128 < 2^31. Keys past
-                          seqused_k may hold any bits: they are never used. */
+  int v_layout;        /* attn_v_layout_t. ATTN_V_COL_MAJOR (keys contiguous, the V stride[2]
+                          the stride between head-dim rows; the page's non-row-major VLayout)
+                          is supported by attn_fwd (prefill and split-KV decode shapes) and by
+                          attn_fwd_paged (prefill and decode shapes: each V page of each
+                          kv-head is [head_dim_v, page_size], keys contiguous, addressed as
+                          pool + page*v_pool_stride[0] + head*v_pool_stride[1] +
+                          c*v_pool_stride[2] + slot; v_pool_stride is required), with BF16 or
+                          FP8_E4M3 inputs and head_dim_v = d. The row length (sk, or
+                          page_size) must be a multiple of 8 keys (BF16) or 16 keys (FP8),
+                          and (head_dim_v - 1) * row stride * elem + 64 * elem < 2^31. Keys
+                          past the used length may hold any bits: they are never used.
+                          Not supported by the varlen entry points (ATTN_ENOTSUP). */
   int64_t v_pool_stride[3]; /* attn_fwd_paged / attn_fwd_varlen_paged: the V pool's {page, head,
                           slot} element strides when they differ from the K pool's (required with
                           head_dim_v != d); all zero = kv_stride for both pools. Same rules as

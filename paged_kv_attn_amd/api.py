@@ -278,10 +278,11 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     return out, lse
 
 
-def _check_pools(q, d, k_pool, v_pool):
+def _check_pools(q, d, k_pool, v_pool, v_colmajor=False):
     _need(k_pool.dim() == 4 and v_pool.dim() == 4, "pools must be 4-d [num_pages, page_size, Hkv, dim]")
     _check_like("k_pool", k_pool, q)
-    _check_like("v_pool", v_pool, q)
+    if not v_colmajor:
+        _check_like("v_pool", v_pool, q)
     _need(k_pool.shape[3] == d, f"k_pool has head dim {k_pool.shape[3]}, q has {d}")
     _need(v_pool.shape[:3] == k_pool.shape[:3], "v_pool's [num_pages, page_size, Hkv] differ from k_pool's")
 
@@ -308,20 +309,31 @@ def _set_v_pool(p, d, k_pool, v_pool):
 def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
                    softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True, kv_split_tokens=0,
                    workspace=None, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None, o_scale=1.0,
-                   bias=None):
+                   bias=None, v_colmajor=False):
     """Paged KV cache. q [B, Hq, sq, d]; k_pool [num_pages, page_size, Hkv, d],
     v_pool [num_pages, page_size, Hkv, dv] (any strides, last dim contiguous);
     block_table int32 [B, W]; seqlens_k int32 [B]. Short query blocks
     (sq * Hq / Hkv <= 16, bf16 or fp8) run the split-KV decode kernel; longer ones
     (bf16 or fp8, page_size a multiple of 64) the prefill kernel. ``bias`` (fp32
-    [B|1, Hq|1, sq, Kmax]) is indexed by the logical key position. Returns (out, lse)."""
+    [B|1, Hq|1, sq, Kmax]) is indexed by the logical key position. With
+    ``v_colmajor`` v_pool is [num_pages, Hkv, d, page_size] (each V page of
+    each kv-head stored head-dim-major, keys contiguous). Returns (out, lse)."""
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
-    dv = v_pool.shape[3]
+    if v_colmajor:
+        _need(v_pool.dim() == 4 and v_pool.shape[0] == num_pages and v_pool.shape[1] == Hkv and
+              v_pool.shape[3] == page_size and v_pool.stride(3) == 1,
+              "column-major v_pool must be [num_pages, Hkv, d, page_size] with unit stride over keys")
+        _need(v_pool.dtype == q.dtype and v_pool.device == q.device, "v_pool must share q's dtype and device",
+              TypeError)
+        v_view = v_pool.permute(0, 3, 1, 2)          # the [num_pages, page_size, Hkv, d] logical view
+    else:
+        v_view = v_pool
+    dv = v_view.shape[3]
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
     _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
-    _check_pools(q, d, k_pool, v_pool)
+    _check_pools(q, d, k_pool, v_view, v_colmajor)
     _check_table(block_table, q, B)
     _check_index("seqlens_k", seqlens_k, q, B)
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
@@ -334,7 +346,14 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     W = block_table.stride(0)
     p = _params(q.dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size, sink_logits,
                 bias=bias, alibi_slopes=alibi_slopes, out_dtype=out_dtype, o_scale=o_scale)
-    _set_v_pool(p, d, k_pool, v_pool)
+    if v_colmajor:
+        p.v_layout = _lib.ATTN_V_COL_MAJOR
+        for i, s in enumerate((v_pool.stride(0), v_pool.stride(1), v_pool.stride(2))):
+            p.v_pool_stride[i] = s           # {page, head, head-dim row}
+        if dv != d:
+            p.head_dim_v = dv
+    else:
+        _set_v_pool(p, d, k_pool, v_pool)
     if out is None:
         out = torch.empty((B, Hq, sq, dv), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:

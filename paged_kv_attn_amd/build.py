@@ -20,10 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
 OBJ = os.path.join(PKG, "_build")
 # (source, object, extra defines): the prefill kernel's instantiations compile
-# in four parts, one per (input type, head dim), in parallel
+# in eight parts, one per (input type, head dim, value head dim), in parallel
 SOURCES = [("api.cpp", "api", []), ("noalloc.cpp", "noalloc", []), ("decode.hip", "decode", []),
            ("f32.hip", "f32", [])] + \
-    [("prefill.hip", f"prefill_p{k}", [f"-DATTN_PREFILL_PART={k}"]) for k in range(4)]
+    [("prefill.hip", f"prefill_p{k}", [f"-DATTN_PREFILL_PART={k}"]) for k in range(8)]
 # Per-source code-generation options. The decode kernel keeps its MFMA
 # accumulators in ordinary VGPRs: its online-softmax rescale touches them
 # between matrix ops, and accumulation registers would cost a copy each way.

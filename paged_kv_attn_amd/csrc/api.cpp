@@ -150,8 +150,8 @@ attn_status_t check_mode_fields(const attn_params_t* p, bool batch_mode, bool va
   }
   if (p->min_seqlen_q != 0 && !varlen_mode)
     return fail(ATTN_EINVAL, "min_seqlen_q applies to attn_fwd_varlen only");
-  if (p->v_layout == ATTN_V_COL_MAJOR && !batch_mode)
-    return fail(ATTN_ENOTSUP, "column-major V is supported by attn_fwd (batch mode) only");
+  if (p->v_layout == ATTN_V_COL_MAJOR && varlen_mode)
+    return fail(ATTN_ENOTSUP, "column-major V is supported by attn_fwd and attn_fwd_paged only");
   return ATTN_OK;
 }
 
@@ -167,6 +167,20 @@ attn_status_t check_strides(const char* name, const int64_t* st, int n, int eb) 
 attn_status_t check_ptr(const char* name, const void* ptr) {
   if (!ptr) return fail(ATTN_EINVAL, "%s is NULL", name);
   if (!aligned16(ptr)) return fail(ATTN_EINVAL, "%s is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+// Column-major V (keys contiguous, `row_stride` elements between head-dim
+// rows): head_dim_v = d; the keys of one row come in 16-byte chunks (8 bf16 or
+// 16 fp8 keys), so the row length (sk, or page_size) must be a multiple of
+// that chunk; a tile's span of rows is addressed with 32-bit offsets.
+attn_status_t check_colmajor_v(const attn_params_t* p, int d, int len, const char* what, int64_t row_stride) {
+  if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "column-major V needs bf16 or fp8 inputs");
+  if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "column-major V needs head_dim_v = d");
+  const int eb = elem_bytes(p->in_dtype), chunk = 16 / eb;
+  if (len % chunk) return fail(ATTN_EINVAL, "column-major V needs %s a multiple of %d (got %d)", what, chunk, len);
+  if ((int64_t)(d - 1) * row_stride * eb + 64 * eb >= ((int64_t)1 << 31))
+    return fail(ATTN_EINVAL, "column-major V: head-dim row stride too large");
   return ATTN_OK;
 }
 
@@ -389,13 +403,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   TRY(check_strides("k", k_stride, 3, eb));
   TRY(check_strides("v", v_stride, 3, eb));
   TRY(check_strides("o", o_stride, 3, ob));
-  if (p->v_layout == ATTN_V_COL_MAJOR) {
-    if (p->in_dtype != ATTN_BF16) return fail(ATTN_ENOTSUP, "column-major V needs bf16 inputs");
-    if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "column-major V needs head_dim_v = d");
-    if (sk % 8) return fail(ATTN_EINVAL, "column-major V needs sk a multiple of 8 (got %d)", sk);
-    if ((int64_t)(d - 1) * v_stride[2] * 2 + 128 >= ((int64_t)1 << 31))
-      return fail(ATTN_EINVAL, "column-major V: head-dim row stride too large");
-  }
+  if (p->v_layout == ATTN_V_COL_MAJOR) TRY(check_colmajor_v(p, d, sk, "sk", v_stride[2]));
   if (B == 0 || sq == 0) return ATTN_OK;
   const int ratio = Hq / Hkv;
   hipStream_t s = (hipStream_t)stream;
@@ -563,6 +571,9 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   const int64_t* v_st = v_pool_strides(p, kv_stride);
   if (dv != d && v_st == kv_stride)
     return fail(ATTN_EINVAL, "head_dim_v != d in paged mode needs v_pool_stride (the V pool's strides)");
+  const bool v_cm = p->v_layout == ATTN_V_COL_MAJOR;
+  if (v_cm && v_st == kv_stride)
+    return fail(ATTN_EINVAL, "column-major V pages need v_pool_stride ({page, head, head-dim row})");
   if (B < 0 || sq < 0 || Hq <= 0 || Hkv <= 0 || block_table_stride <= 0 || num_pages <= 0)
     return fail(ATTN_EINVAL, "bad sizes B=%d sq=%d Hq=%d Hkv=%d table_stride=%d num_pages=%d", B, sq, Hq, Hkv,
                 block_table_stride, num_pages);
@@ -585,7 +596,8 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   TRY(check_strides("v_pool_stride", v_st, 3, eb));
   TRY(check_strides("o", o_stride, 3, elem_bytes(p->out_dtype)));
   TRY(check_row_span("k_pool", kv_stride[2], eb, decode_shape ? kDecodeGranRows : kPrefillTileRows));
-  TRY(check_row_span("v_pool", v_st[2], eb, decode_shape ? kDecodeGranRows : kPrefillTileRows));
+  if (v_cm) TRY(check_colmajor_v(p, d, page_size, "page_size", v_st[2]));
+  else TRY(check_row_span("v_pool", v_st[2], eb, decode_shape ? kDecodeGranRows : kPrefillTileRows));
   if (B == 0 || sq == 0) return ATTN_OK;
   const int64_t max_len64 = (int64_t)block_table_stride * page_size;
   if (max_len64 > (1 << 30)) return fail(ATTN_EINVAL, "block_table_stride * page_size is too large");
@@ -611,6 +623,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
     a.lse_sb = (int64_t)Hq * sq; a.lse_sh = sq;
     a.seqused_q = nullptr; a.seqused_k = seqlens_k;
     a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
+    a.v_colmajor = v_cm;
     a.sq = sq; a.sk = max_len; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
     const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
     a.n_qtiles = (int)(((int64_t)sq * ratio + rows_tile - 1) / rows_tile);
@@ -637,6 +650,7 @@ attn_status_t attn_fwd_paged(const attn_params_t* p, const void* q, const void* 
   a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_sr = kv_stride[2];
   a.v_sb = v_st[0]; a.v_sh = v_st[1]; a.v_sr = v_st[2];
   a.seqlens_k = seqlens_k; a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
+  a.v_colmajor = v_cm;
   a.sk = max_len; a.sq = sq; a.hq = Hq; a.hkv = Hkv; a.ratio = ratio; a.m_rows = m_rows;
   a.split_tokens = split; a.n_splits = nsp;
   a.c_exp2 = c_exp2; a.softcap_pre = pre; a.softcap_post = post;

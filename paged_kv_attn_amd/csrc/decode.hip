@@ -93,7 +93,7 @@ __device__ __forceinline__ int vt_sw(int row) { return (row >> 2) & 3; }
 
 template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP, bool FP8, bool VT>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  static_assert(!VT || (!PAGED && !FP8), "column-major V: contiguous bf16 V only");
+  static_assert(!VT || D == DV, "column-major V: equal head dims");
   using Tr = DTr<D, DV, FP8>;
   // One LDS object per pipeline buffer, so the compiler can tell the
   // HBM->LDS copies into one buffer from the reads of the other.
@@ -193,10 +193,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     koff[q] = (int)(R * krow) + 16 * (sl ^ kswz<D, FP8>(R));
   }
   // V: bf16 rows straight to LDS; fp8 rows as 16-byte chunks into registers
-  // (load i of lane l: chunk 64 i + l = row R, fp8 chunk c8 of the row)
+  // (load i of lane l: chunk 64 i + l = row R, fp8 chunk c8 of the row; column-major
+  // fp8 V: head-dim row ch / 2, keys 16 (ch % 2) .. of the granule)
 #pragma unroll
   for (int q = 0; q < (FP8 ? Tr::kV8 : Tr::kVBlocks); ++q) {
-    if (FP8) {
+    if (FP8 && VT) {
+      const int ch = 64 * q + lane;
+      voff[q] = (int)((ch >> 1) * vrow) + 16 * (ch & 1);
+    } else if (FP8) {
       const int ch = 64 * q + lane, R = ch / (DV / 16), c8 = ch % (DV / 16);
       voff[q] = (int)(R * vrow) + 16 * c8;
     } else if (VT) {  // block q: V^T rows 16 q .. 16 q + 15, lane l: row 16 q + l / 4, slot l % 4
@@ -210,7 +214,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   }
   // column-major V: keys of chunk (lane & 3) ^ vt_sw(row) of this lane's load rows
   const int vt_kc = VT ? (lane & 3) ^ vt_sw(lane >> 2) : 0;   // vt_sw(16 q + l / 4) = vt_sw(l / 4)
-  const char* const vt_head = VT ? (const char*)a.v + ((int64_t)kb * a.v_sb + (int64_t)g * a.v_sh) * 2 : nullptr;
+  const char* const vt_head =
+      VT ? (const char*)a.v + ((int64_t)(PAGED ? 0 : kb) * a.v_sb + (int64_t)g * a.v_sh) * Tr::kElem : nullptr;
   // K A-operand reads: lane (key 16 kb + L, group j4) takes K[key][32 st + 8 j4 .. +7],
   // chunk 4 st + j4 of row 16 kb + L, whose swizzle kswz(16 kb + L) = kswz(L) = ksw:
   // slot (4 st + j4) ^ ksw = ((4 st) ^ (ksw & ~3)) + ((j4 ^ ksw) & 3).
@@ -250,16 +255,28 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const int gp = rows > 0 ? gs : t0;  // any valid page for an empty range
     const __amdgpu_buffer_rsrc_t kr =
         make_rsrc(rows_base(gp, a.k, a.k_sb, a.k_sh, a.k_sr), (uint32_t)(rows * krow));
-    // column-major V: the granule's 32-key span of every head-dim row; chunks of keys
-    // at or past the range get an offset beyond it and arrive as zeros
+    // column-major V: the granule's 32-key span of every head-dim row (paged: in
+    // the granule's page, keys contiguous as in the page's [hdim_v, page_block_size]
+    // view of a V page); chunks of keys at or past the range get an offset beyond
+    // it and arrive as zeros
+    const char* vt_base = nullptr;
+    if (VT) {
+      if (PAGED) {
+        const int page = __builtin_amdgcn_readlane(pg, gp / a.page_size - p_first);
+        vt_base = vt_head + ((int64_t)page * a.v_sb + gp % a.page_size) * Tr::kElem;
+      } else {
+        vt_base = vt_head + (int64_t)gp * Tr::kElem;
+      }
+    }
     const __amdgpu_buffer_rsrc_t vr =
-        VT ? make_rsrc(vt_head + 2 * (int64_t)gp, (uint32_t)((DV - 1) * vrow + 2 * kGran))
+        VT ? make_rsrc(vt_base, (uint32_t)((DV - 1) * vrow + Tr::kElem * kGran))
            : make_rsrc(rows_base(gp, a.v, a.v_sb, a.v_sh, a.v_sr), (uint32_t)(rows * vrow));
 #pragma unroll
     for (int q = 0; q < Tr::kBlocks; ++q) buf_load16_lds_stream(kr, kb + 1024 * q, koff[q]);
     if (FP8) {
 #pragma unroll
-      for (int q = 0; q < Tr::kV8; ++q) v8[q] = buf_load16(vr, voff[q]);
+      for (int q = 0; q < Tr::kV8; ++q)
+        v8[q] = buf_load16(vr, (!VT || 16 * (lane & 1) < rows) ? voff[q] : 0x7FFFFFF0);
     } else {
 #pragma unroll
       for (int q = 0; q < Tr::kVBlocks; ++q)
@@ -267,7 +284,30 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
   };
   // fp8 V of one granule: widen (exactly) to bf16 into the LDS layout of bf16 V
-  auto store_v8 = [&](lds_char* vb, const U128 (&v8)[FP8 ? Tr::kV8 : 1]) {
+  // (column-major: of bf16 V^T; keys at or past min(t_hi, gs + 32) in the chunk
+  // holding the last one, any bits, are zeroed here)
+  auto store_v8 = [&](lds_char* vb, const U128 (&v8)[FP8 ? Tr::kV8 : 1], int gs) {
+    if (VT) {
+      const int rows = min(kGran, t_hi - gs);
+#pragma unroll
+      for (int q = 0; q < (FP8 ? Tr::kV8 : 0); ++q) {
+        const int ch = 64 * q + lane, R = ch >> 1, c = ch & 1;
+        U128 lo = fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}), hi = fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w});
+        const int nv = rows - 16 * c;
+        if (nv < 16) {
+          uint32_t* w = &lo.x;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) w[e / 2] &= (e < nv ? 0xFFFFu : 0u) | (e + 1 < nv ? 0xFFFF0000u : 0u);
+          w = &hi.x;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) w[e / 2] &= (8 + e < nv ? 0xFFFFu : 0u) | (9 + e < nv ? 0xFFFF0000u : 0u);
+        }
+        lds_char* row = vb + R * (2 * kGran);
+        lds_store16(row + 16 * ((2 * c) ^ vt_sw(R)), lo);
+        lds_store16(row + 16 * ((2 * c + 1) ^ vt_sw(R)), hi);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < (FP8 ? Tr::kV8 : 0); ++q) {
       const int ch = 64 * q + lane, R = ch / (DV / 16), c0 = 2 * (ch % (DV / 16));
@@ -376,7 +416,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   // used length, possibly not finite); zero them in LDS before the products read them
   auto vt_zero_tail = [&](int gs, lds_char* vb) {
     const int cs = Lk & ~7;
-    if (VT && (Lk & 7) && cs >= gs && cs < gs + kGran && cs < t_hi) {
+    if (VT && !FP8 && (Lk & 7) && cs >= gs && cs < gs + kGran && cs < t_hi) {
       const int kc = (cs - gs) >> 3;
       for (int R = lane; R < DV; R += 64) {
         lds_char* row = vb + R * (2 * kGran) + 16 * (kc ^ vt_sw(R));
@@ -391,14 +431,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (;;) {
       issue(gs + kGran, k1, v1, v8b);
       wait_vmem_le<Tr::kOps>();
-      if (FP8) store_v8(v0, v8a);
+      if (FP8) store_v8(v0, v8a, gs);
       vt_zero_tail(gs, v0);
       compute(gs, k0, v0);
       gs += kGran;
       if (gs >= t_hi) break;
       issue(gs + kGran, k0, v0, v8a);
       wait_vmem_le<Tr::kOps>();
-      if (FP8) store_v8(v1, v8b);
+      if (FP8) store_v8(v1, v8b, gs);
       vt_zero_tail(gs, v1);
       compute(gs, k1, v1);
       gs += kGran;
@@ -510,8 +550,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 template <int D, int DV, bool PAGED, bool MASK, bool SOFTCAP>
 hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_t s) {
   dim3 grid(a.hkv, a.n_splits, B);
-  if constexpr (!PAGED && D == DV) {
-    if (a.v_colmajor) {  // bf16 only (the host checks)
+  if constexpr (D == DV) {
+    if (a.v_colmajor && a.fp8) {
+      hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true, true>), grid, dim3(64), 0, s, a);
+    } else if (a.v_colmajor) {
       hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false, true>), grid, dim3(64), 0, s, a);
     } else if (a.fp8) {
       hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true, false>), grid, dim3(64), 0, s, a);
@@ -519,7 +561,7 @@ hipError_t launch_t(const DecodeArgs& a, const CombineArgs& c, int B, hipStream_
       hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false, false>), grid, dim3(64), 0, s, a);
     }
   } else {
-    if (a.v_colmajor) return hipErrorInvalidValue;  // contiguous V with head_dim_v = d only
+    if (a.v_colmajor) return hipErrorInvalidValue;  // head_dim_v = d only
     if (a.fp8) hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, true, false>), grid, dim3(64), 0, s, a);
     else hipLaunchKernelGGL((decode_kernel<D, DV, PAGED, MASK, SOFTCAP, false, false>), grid, dim3(64), 0, s, a);
   }

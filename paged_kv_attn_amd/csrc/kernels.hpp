@@ -53,7 +53,8 @@ struct PrefillArgs {
   const int32_t* cache_idx;   // batch mode, nullable: K/V batch entry of each batch entry
   int cache_count;            // K/V batch entries (indices outside [0, cache_count) read no keys)
   int min_seqlen_q;           // varlen mode: sequences with Lq <= min_seqlen_q are skipped
-  int v_colmajor;             // batch mode, bf16, equal head dims: V keys contiguous, v_sr = head-dim row stride
+  int v_colmajor;             // batch or paged mode, equal head dims: V keys contiguous (within a page),
+                              // v_sr = head-dim row stride
   const int32_t* kv_start;    // varlen-paged mode, nullable: logical position of each sequence's first key
 };
 
@@ -67,7 +68,7 @@ struct DecodeArgs {
   int64_t v_sb, v_sh, v_sr;
   const int32_t* seqlens_k;   // per-request Lk (paged: required; contiguous: nullable)
   const int32_t* seqused_q;   // contiguous only, nullable: per-request used query rows Lq <= sq
-  int v_colmajor;             // contiguous bf16 V with keys contiguous: v_sr = head-dim row stride
+  int v_colmajor;             // V keys contiguous (paged: within a page), v_sr = head-dim row stride
   const int32_t* block_table; // paged only
   int64_t bt_stride;
   int page_size;

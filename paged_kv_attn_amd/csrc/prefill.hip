@@ -104,7 +104,8 @@ enum MaskKind : int { kMaskNone = 0, kMaskRight = 1, kMaskWindow = 2 };
 
 template <int D, int DV, bool FP8, int MODE, int MK, bool SOFTCAP, int BIAS, bool VT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  static_assert(!VT || (!FP8 && D == DV), "column-major V: bf16 with equal head dims");
+  static_assert(!VT || (D == DV && MODE != kPrefillVarlen && MODE != kPrefillVarlenPaged),
+                "column-major V: equal head dims, batch or paged mode");
   constexpr bool MASK = MK != kMaskNone;
   constexpr bool TWO_SIDED = MK == kMaskWindow;   // the host guarantees a.wl >= 0
   using Tr = Traits<D, DV, FP8>;
@@ -353,12 +354,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // fp8 V: through registers, widened to bf16 on the way into LDS
   U128 v8[FP8 ? Tr::kV8Loads : 1];
   const int v8ch = threadIdx.x % Tr::kV8Ch, v8row = threadIdx.x / Tr::kV8Ch;
+  // column-major V: the tile's 64 keys of every head-dim row start here (batch:
+  // key j0 of the head; paged: the tile's page, keys contiguous within it as in
+  // the page's non-row-major V view [hdim_v, page_block_size])
+  auto vt_tile_base = [&](int j0) -> const char* {
+    if (PAGED) {
+      const int page = a.block_table[(int64_t)z * a.bt_stride + j0 / a.page_size];
+      return vh + ((int64_t)page * a.v_sb + (j0 % a.page_size)) * Tr::kElem;
+    }
+    return vh + (int64_t)j0 * Tr::kElem;
+  };
   auto load_v = [&](int t, int slot) {
     const int j0 = t * kBlockN;
     if (VT) {
       // rows are head-dim indices (row stride vrow); chunks of keys at or past Lk
       // get an offset beyond the range and arrive as zeros
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + 2 * j0, (uint32_t)((DV - 1) * vrow + 2 * kBlockN));
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(vt_tile_base(j0), (uint32_t)((DV - 1) * vrow + Tr::kElem * kBlockN));
+      if (FP8) {
+        // 16-key fp8 chunks into registers (chunk i of this thread: head-dim row
+        // ci / 4, keys 16 (ci % 4) .., ci = threadIdx.x + 256 i)
+#pragma unroll
+        for (int i = 0; i < Tr::kV8Loads; ++i) {
+          const int ci = threadIdx.x + kThreads * i;
+          const int c = ci & 3;
+          v8[i] = buf_load16(r, j0 + 16 * c < Lk ? (int)((ci >> 2) * vrow) + 16 * c : 0x7FFFFFF0);
+        }
+        return;
+      }
       lds_char* base = vslot(slot);
 #pragma unroll
       for (int i = 0; i < Tr::kVInstr; ++i)
@@ -401,8 +424,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < Tr::kVInstr; ++i) buf_load16_lds(r, base + 1024 * (wave + 4 * i), voff[i]);
     }
   };
-  auto store_v8 = [&](int slot) {  // fp8 only
+  auto store_v8 = [&](int slot, int t) {  // fp8 only: widen tile t's V into LDS slot `slot`
     lds_char* base = vslot(slot);
+    if (VT) {
+      // V^T rows of 64 keys as bf16 (the bf16 column-major layout); keys at or
+      // past Lk in the chunk holding key Lk - 1 (any bits) are zeroed here
+      const int j0 = t * kBlockN;
+#pragma unroll
+      for (int i = 0; i < (FP8 ? Tr::kV8Loads : 0); ++i) {
+        const int ci = threadIdx.x + kThreads * i;
+        const int R = ci >> 2, c = ci & 3;
+        U128 lo = fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y}), hi = fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w});
+        const int nv = Lk - (j0 + 16 * c);  // keys of this chunk below Lk
+        if (nv < 16) {
+          uint32_t* w = &lo.x;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            w[e / 2] &= (e < nv ? 0xFFFFu : 0u) | (e + 1 < nv ? 0xFFFF0000u : 0u);
+          }
+          w = &hi.x;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            w[e / 2] &= (8 + e < nv ? 0xFFFFu : 0u) | (9 + e < nv ? 0xFFFF0000u : 0u);
+          }
+        }
+        lds_store16(base + R * (2 * kBlockN) + 16 * ((2 * c) ^ vt_swz(R)), lo);
+        lds_store16(base + R * (2 * kBlockN) + 16 * ((2 * c + 1) ^ vt_swz(R)), hi);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < (FP8 ? Tr::kV8Loads : 0); ++i) {
       const int R = v8row + i * (kThreads / Tr::kV8Ch);
@@ -664,13 +714,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // other slot are in flight (HBM -> LDS) while tile t is computed.
     load_k(t_begin, 0);
     load_v(t_begin, 0);
-    if (FP8) store_v8(0);
+    if (FP8) store_v8(0, t_begin);
     wait_vmem();
     __syncthreads();
     auto step = [&](auto parity_tag, int t) {
       constexpr int P = decltype(parity_tag)::value ? 1 : 0;
       const bool has1 = t + 1 < t_end;
-      if (VT && !has1) {
+      if (VT && !FP8 && !has1) {
         // the chunk holding key Lk - 1 also brought keys Lk .. (past the used
         // length, possibly not finite): zero them before any product reads them
         const int rem = Lk - t * kBlockN;
@@ -695,7 +745,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             tile_needs_mask(t) ? softmax(MaskedT{}, t, s0, s1, pk) : softmax(PlainT{}, t, s0, s1, pk);
         pv(P, alpha, pk);
       }
-      if (FP8 && has1) store_v8(1 - P);
+      if (FP8 && has1) store_v8(1 - P, t + 1);
       wait_vmem();
       __syncthreads();
     };
@@ -827,10 +877,10 @@ hipError_t launch_v(const PrefillArgs& a, int nz, bool mask, bool softcap, hipSt
 
 template <int D, int DV, bool FP8, int MODE>
 hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if constexpr (MODE == kPrefillBatch && !FP8 && D == DV) {
+  if constexpr ((MODE == kPrefillBatch || MODE == kPrefillPaged) && D == DV) {
     if (a.v_colmajor) return launch_v<D, DV, FP8, MODE, true>(a, nz, mask, softcap, s);
   } else {
-    if (a.v_colmajor) return hipErrorInvalidValue;  // batch-mode bf16 with equal head dims only
+    if (a.v_colmajor) return hipErrorInvalidValue;  // batch or paged mode with equal head dims only
   }
   return launch_v<D, DV, FP8, MODE, false>(a, nz, mask, softcap, s);
 }
@@ -844,15 +894,15 @@ hipError_t launch_f(const PrefillArgs& a, int mode, int nz, bool mask, bool soft
 }
 
 
-// One (input type, d) combination per part, both head_dim_v values each. The
-// build compiles this file once per part (ATTN_PREFILL_PART = 0..3) so the
-// instantiations compile in parallel; without the macro one object holds all.
-template <int D, bool FP8>
-hipError_t launch_part(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
+// One (input type, d, head_dim_v) combination per part. The build compiles
+// this file once per part (ATTN_PREFILL_PART = 0..7: bit 2 fp8, bit 1 d = 64,
+// bit 0 head_dim_v = 64) so the instantiations compile in parallel; without
+// the macro one object holds all.
+template <int D, int DV, bool FP8>
+hipError_t launch_part(const PrefillArgs& a, int mode, int nz, hipStream_t s) {
   const bool mask = a.wl >= 0 || a.wr >= 0;
   const bool softcap = a.softcap_pre != 0.0f;
-  if (dv == 64) return launch_f<D, 64, FP8>(a, mode, nz, mask, softcap, s);
-  return launch_f<D, 128, FP8>(a, mode, nz, mask, softcap, s);
+  return launch_f<D, DV, FP8>(a, mode, nz, mask, softcap, s);
 }
 
 }  // namespace
@@ -862,31 +912,45 @@ hipError_t launch_part(const PrefillArgs& a, int dv, int mode, int nz, hipStream
 #define ATTN_PREFILL_PART -1
 #endif
 
+#define ATTN_PREFILL_PART_FN(K, NAME, D, DV, FP8)                                      \
+  hipError_t NAME(const PrefillArgs& a, int mode, int nz, hipStream_t s);                \
+  hipError_t NAME(const PrefillArgs& a, int mode, int nz, hipStream_t s) {               \
+    return launch_part<D, DV, FP8>(a, mode, nz, s);                                      \
+  }
+
 #if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 0
-hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
-  return launch_part<128, false>(a, dv, mode, nz, s);
-}
+ATTN_PREFILL_PART_FN(0, launch_prefill_bf16_d128_dv128, 128, 128, false)
 #endif
 #if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 1
-hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
-  return launch_part<64, false>(a, dv, mode, nz, s);
-}
+ATTN_PREFILL_PART_FN(1, launch_prefill_bf16_d128_dv64, 128, 64, false)
 #endif
 #if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 2
-hipError_t launch_prefill_fp8_d128(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
-  return launch_part<128, true>(a, dv, mode, nz, s);
-}
+ATTN_PREFILL_PART_FN(2, launch_prefill_bf16_d64_dv128, 64, 128, false)
 #endif
 #if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 3
-hipError_t launch_prefill_fp8_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s) {
-  return launch_part<64, true>(a, dv, mode, nz, s);
-}
+ATTN_PREFILL_PART_FN(3, launch_prefill_bf16_d64_dv64, 64, 64, false)
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 4
+ATTN_PREFILL_PART_FN(4, launch_prefill_fp8_d128_dv128, 128, 128, true)
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 5
+ATTN_PREFILL_PART_FN(5, launch_prefill_fp8_d128_dv64, 128, 64, true)
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 6
+ATTN_PREFILL_PART_FN(6, launch_prefill_fp8_d64_dv128, 64, 128, true)
+#endif
+#if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 7
+ATTN_PREFILL_PART_FN(7, launch_prefill_fp8_d64_dv64, 64, 64, true)
 #endif
 
 #if defined(ATTN_PREFILL_ALL) || ATTN_PREFILL_PART == 0
-hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
-hipError_t launch_prefill_fp8_d128(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
-hipError_t launch_prefill_fp8_d64(const PrefillArgs& a, int dv, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_bf16_d128_dv64(const PrefillArgs& a, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_bf16_d64_dv128(const PrefillArgs& a, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_bf16_d64_dv64(const PrefillArgs& a, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_fp8_d128_dv128(const PrefillArgs& a, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_fp8_d128_dv64(const PrefillArgs& a, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_fp8_d64_dv128(const PrefillArgs& a, int mode, int nz, hipStream_t s);
+hipError_t launch_prefill_fp8_d64_dv64(const PrefillArgs& a, int mode, int nz, hipStream_t s);
 
 int prefill_rows_per_tile(int) { return kBlockM; }
 
@@ -896,9 +960,13 @@ int64_t prefill_workgroups(const PrefillArgs& a, int nz) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int mode, int nz, hipStream_t stream) {
   if (a.n_qtiles <= 0 || nz <= 0 || a.hkv <= 0) return hipSuccess;
-  if (in_type == kInFP8)
-    return d == 128 ? launch_prefill_fp8_d128(a, dv, mode, nz, stream) : launch_prefill_fp8_d64(a, dv, mode, nz, stream);
-  return d == 128 ? launch_prefill_bf16_d128(a, dv, mode, nz, stream) : launch_prefill_bf16_d64(a, dv, mode, nz, stream);
+  typedef hipError_t (*Fn)(const PrefillArgs&, int, int, hipStream_t);
+  static const Fn fns[8] = {launch_prefill_bf16_d128_dv128, launch_prefill_bf16_d128_dv64,
+                            launch_prefill_bf16_d64_dv128,  launch_prefill_bf16_d64_dv64,
+                            launch_prefill_fp8_d128_dv128,  launch_prefill_fp8_d128_dv64,
+                            launch_prefill_fp8_d64_dv128,   launch_prefill_fp8_d64_dv64};
+  const int part = (in_type == kInFP8 ? 4 : 0) | (d == 64 ? 2 : 0) | (dv == 64 ? 1 : 0);
+  return fns[part](a, mode, nz, stream);
 }
 #endif
 

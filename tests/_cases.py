@@ -41,9 +41,10 @@ def run_varlen(case, **kw):
                               descale=(case.descale["q"], case.descale["k"], case.descale["v"]), **kw)
 
 
-def run_paged(case, **kw):
+def run_paged(case, v_pool=None, **kw):
     t = case.t
-    return pk.attn_fwd_paged(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"], scale=case.scale,
+    v_pool = t["v_pool"] if v_pool is None else v_pool
+    return pk.attn_fwd_paged(t["q"], t["k_pool"], v_pool, t["block_table"], t["seqlens_k"], scale=case.scale,
                              window=(case.window_left, case.window_right), softcap=case.softcap,
                              descale=(case.descale["q"], case.descale["k"], case.descale["v"]), **kw)
 

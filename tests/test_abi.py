@@ -277,9 +277,15 @@ def test_v_layout_validation():
     assert _fwd(p) == 1 and "v_layout" in _err()
     p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)
     assert _fwd(p, sk=60) == 1 and "multiple of 8" in _err()
-    assert _paged(p) == 2 and "batch mode" in _err()
+    # column-major pages need the V pool's own strides {page, head, head-dim row}
+    assert _paged(p) == 1 and "v_pool_stride" in _err()
+    p.v_pool_stride[0], p.v_pool_stride[1], p.v_pool_stride[2] = 2 * 128 * 64, 128 * 64, 64
+    assert _paged(p, page=48, sq=2) == 2 and "page_size" in _err()
+    # fp8 keys come 16 to a chunk
     p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, in_dtype=_lib.ATTN_FP8_E4M3, out_dtype=_lib.ATTN_BF16)
-    assert _fwd(p) == 2 and "bf16" in _err()
+    assert _fwd(p, sk=56, strides=[2 * 64 * 128, 64 * 128, 128]) == 1 and "multiple of 16" in _err()
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, in_dtype=_lib.ATTN_F32, out_dtype=_lib.ATTN_F32)
+    assert _fwd(p) == 2 and "bf16 or fp8" in _err()
     p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, head_dim_v=64)
     assert _fwd(p) == 2 and "head_dim_v" in _err()
     p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)             # decode shape: the same checks apply

@@ -35,7 +35,8 @@ def _draw(seed):
     o["sinks"] = r.uniform(-3, 3, size=o["hkv"] * o["ratio"]) if r.random() < 0.4 else None
     o["alibi"] = r.uniform(0.0, 0.08, size=o["hkv"] * o["ratio"]) if r.random() < 0.3 else None
     o["head_major"] = bool(r.random() < 0.5)      # paged: pool pages stored [Hkv, P, d]
-    o["colmajor"] = bool(r.random() < 0.3)        # batch, bf16, dv == d: V stored [B, Hkv, d, sk]
+    o["colmajor"] = bool(r.random() < 0.3)        # batch / paged, dv == d: V stored [B, Hkv, d, sk] / pages
+                                                  # [N, Hkv, d, P]
     o["rng"] = r
     return o
 
@@ -83,9 +84,10 @@ def test_random_option_mix(seed):
     if o["mode"] == "batch":
         B = int(r.integers(1, 4))
         sk = int(r.integers(1, 700))
-        colmajor = o["colmajor"] and dtype == "bf16" and dv == d
+        colmajor = o["colmajor"] and dv == d
         if colmajor:
-            sk = 8 * max(1, sk // 8)
+            ch = 8 if dtype == "bf16" else 16      # keys per 16-byte chunk
+            sk = ch * max(1, sk // ch)
         c = synth.dense_case(B, hq, hkv, sq_max, sk, d, dtype, seed=seed, device=DEV, **_mask(o))
         bg, br = _bias(o, seed, (B, hq, sq_max, sk))
         if bg is not None:
@@ -98,7 +100,7 @@ def test_random_option_mix(seed):
             t = c.t
             out, lse = pk.attn_fwd(t["q"], t["k"], t["v"].transpose(2, 3).contiguous(), scale=c.scale,
                                    window=(c.window_left, c.window_right), softcap=c.softcap, v_colmajor=True,
-                                   **gpu)
+                                   descale=(c.descale["q"], c.descale["k"], c.descale["v"]), **gpu)
         else:
             out, lse = C.run_dense(c, **gpu)
         O, LSE = C.oracle_dense(c, **ref)
@@ -135,6 +137,10 @@ def test_random_option_mix(seed):
         if bg is not None:
             gpu["bias"], ref["bias"] = bg, br
             what += " bias"
+        if o["colmajor"] and dv == d:       # V pages stored [N, Hkv, d, P], keys contiguous
+            gpu["v_colmajor"] = True
+            gpu["v_pool"] = c.t["v_pool"].permute(0, 2, 3, 1).contiguous()
+            what += " v_colmajor"
         out, lse = C.run_paged(c, kv_split_tokens=int(r.choice([0, 64, 256])), **gpu)
         O, LSE = C.oracle_paged(c, **ref)
         C.assert_parity(out, lse, O, LSE, dtype, what)

@@ -1,8 +1,11 @@
-"""GPU parity of column-major V (V stored [B, Hkv, d, sk], keys contiguous)
-on batch-mode bf16 prefill and the split-KV decode path against the fp64
-oracle, including used lengths that end inside a 16-byte chunk of keys with
-NaN-poisoned tails, windows, soft-cap, sinks, ALiBi and an elementwise bias;
-decode with column-major V is bit-identical to decode with row-major V."""
+"""GPU parity of column-major V against the fp64 oracle: V stored
+[B, Hkv, d, sk] (keys contiguous) in batch mode, bf16 and fp8, prefill and the
+split-KV decode path, and column-major V pages ([hdim_v, page_size] per
+kv-head) on paged decode and paged prefill; used lengths that end inside a
+16-byte chunk of keys with NaN-poisoned tails, windows, soft-cap, sinks, ALiBi
+and an elementwise bias. Decode with column-major V is bit-identical to decode
+with row-major V; paged prefill over column-major pages is bit-identical to
+batch-mode prefill with the same keys and column-major V."""
 
 import numpy as np
 import pytest
@@ -86,3 +89,76 @@ def test_colmajor_v_decode_sinks_alibi():
     out, lse = _run_vt(case, **kw)
     O, LSE = C.oracle_dense(case, sink_size=8, sink_logits=sinks, alibi_slopes=slopes)
     C.assert_parity(out, lse, O, LSE, "bf16", "column-major V decode with sinks and ALiBi")
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3FN) column-major V in batch mode, and column-major V pages
+# ([hdim_v, page_size] per kv-head, keys contiguous) on the paged paths.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sq,sk,kw", [
+    (300, 512, dict(causal=True, seqused_k=[333, 512])),     # prefill; Lk inside a 16-key chunk (NaN bytes past it)
+    (1, 3008, dict(seqused_k=[2997, 3008])),                 # decode
+    (3, 1024, dict(window=(200, 0), softcap=30.0, seqused_k=[1021, 64])),
+])
+def test_colmajor_v_fp8(sq, sk, kw):
+    case = synth.dense_case(2, 16, 4, sq, sk, 128, "fp8", seed=sq + sk, device=DEV, **kw)
+    ds = (case.descale["q"], case.descale["k"], case.descale["v"])
+    out, lse = _run_vt(case, descale=ds, kv_split_tokens=256)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "fp8", f"fp8 column-major V sq={sq} {kw}")
+    o_r, l_r = C.run_dense(case, kv_split_tokens=256)
+    if sq * 4 <= 16:   # split-KV decode: the same products in the same order
+        assert torch.equal(C.bits(out), C.bits(o_r)) and torch.equal(C.bits(lse), C.bits(l_r))
+    else:              # prefill: keys permuted within 16-key blocks, row sums in another order
+        assert (o_r.float() - out.float()).abs().max().item() <= 1e-2
+        assert (l_r - lse).abs().max().item() <= 1e-4
+
+
+def _colmajor_pages(case):
+    """The paged case's V pool as column-major pages: [N, Hkv, dv, P], keys contiguous."""
+    return case.t["v_pool"].permute(0, 2, 3, 1).contiguous()
+
+
+@pytest.mark.parametrize("dtype,sq,page,kw", [
+    ("bf16", 1, 64, dict()),
+    ("bf16", 4, 32, dict(causal=True)),
+    ("fp8", 1, 128, dict()),
+    ("fp8", 2, 64, dict(window=(300, 0), softcap=30.0)),
+])
+def test_paged_colmajor_v_decode(dtype, sq, page, kw):
+    case = synth.paged_case([1500, 129, 777, 1], sq, 32, 8, 128, page, dtype, seed=90 + sq + page, device=DEV, **kw)
+    vcm = _colmajor_pages(case)
+    out, lse = C.run_paged(case, kv_split_tokens=256, v_colmajor=True, v_pool=vcm)
+    O, LSE = C.oracle_paged(case)
+    C.assert_parity(out, lse, O, LSE, dtype, f"paged column-major V decode {dtype} sq={sq} page={page}")
+    o_r, l_r = C.run_paged(case, kv_split_tokens=256)
+    assert torch.equal(C.bits(out), C.bits(o_r)) and torch.equal(C.bits(lse), C.bits(l_r))
+
+
+@pytest.mark.parametrize("dtype,sq,page,head_major", [("bf16", 200, 64, False), ("bf16", 130, 128, True),
+                                                      ("fp8", 200, 128, False)])
+def test_paged_colmajor_v_prefill(dtype, sq, page, head_major):
+    lens = [700, 200, 333]
+    case = synth.paged_case(lens, sq, 8, 2, 128, page, dtype, seed=95 + sq, causal=True, device=DEV,
+                            head_major=head_major)
+    vcm = _colmajor_pages(case)
+    out, lse = C.run_paged(case, v_colmajor=True, v_pool=vcm)
+    O, LSE = C.oracle_paged(case)
+    C.assert_parity(out, lse, O, LSE, dtype, f"paged column-major V prefill {dtype} page={page}")
+    # the same keys and values contiguous (column-major V), through the batch-mode kernel: identical bits
+    t, P = case.t, page
+    W = case.meta["table_width"]
+    kc = torch.zeros((3, 2, W * P, 128), dtype=t["k_pool"].dtype, device=DEV)
+    vc = torch.zeros((3, 2, 128, W * P), dtype=t["k_pool"].dtype, device=DEV)
+    table = t["block_table"].cpu().numpy()
+    for b, L in enumerate(lens):
+        for i in range(-(-L // P)):
+            pg = int(table[b, i])
+            kc[b, :, i * P:(i + 1) * P] = t["k_pool"][pg].transpose(0, 1)
+            vc[b, :, :, i * P:(i + 1) * P] = vcm[pg]
+    ds = (case.descale["q"], case.descale["k"], case.descale["v"])
+    used = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o_c, l_c = pk.attn_fwd(t["q"], kc, vc, scale=case.scale, causal=True, seqused_k=used, descale=ds,
+                           v_colmajor=True)
+    assert torch.equal(C.bits(out), C.bits(o_c)) and torch.equal(C.bits(lse), C.bits(l_c))
