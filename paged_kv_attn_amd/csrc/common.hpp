@@ -184,22 +184,16 @@ __device__ __forceinline__ uint32_t pack_fp8x4_sat(float a, float b, float c, fl
   return (uint32_t)v;
 }
 
-// 8 fp8 bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
+// 8 fp8 bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value), two
+// values per v_cvt_scalef32_pk_bf16_fp8 with a unit scale (word_sel picks
+// bytes 0-1 or 2-3 of the source; byte 2k lands in the low half).
 __device__ __forceinline__ U128 fp8x8_to_bf16x8(U64 in) {
-  U128 r;
-  uint32_t* o = &r.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t w = h ? in.y : in.x;
-    float f0 = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-    float f1 = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-    float f2 = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
-    float f3 = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
-    // exact values: truncating the fp32 bits to their upper half is exact
-    o[2 * h + 0] = (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xFFFF0000u);
-    o[2 * h + 1] = (__builtin_bit_cast(uint32_t, f2) >> 16) | (__builtin_bit_cast(uint32_t, f3) & 0xFFFF0000u);
-  }
-  return r;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)in.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)in.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)in.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)in.y, 1.0f, true);
+  return U128{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+              __builtin_bit_cast(uint32_t, d)};
 }
 
 // K/V batch entry read by batch entry b: idx[b] with a cache batch index, else

@@ -311,8 +311,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int q = 0; q < (FP8 ? Tr::kV8 : 0); ++q) {
       const int ch = 64 * q + lane, R = ch / (DV / 16), c0 = 2 * (ch % (DV / 16));
-      lds_store16(vb + R * Tr::kVRow + 16 * (c0 ^ vswz<DV>(R)), fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}));
-      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1) ^ vswz<DV>(R)), fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w}));
+      const U128 lo = fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}), hi = fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w});
+      // odd rows store their odd chunk first: the 16 lanes of a store then hit
+      // 16 different 16-byte bank groups (the swizzle keeps chunk pairs adjacent)
+      const int odd = R & 1;
+      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + odd) ^ vswz<DV>(R)), odd ? hi : lo);
+      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1 - odd) ^ vswz<DV>(R)), odd ? lo : hi);
     }
   };
 

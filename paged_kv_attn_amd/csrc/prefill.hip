@@ -457,8 +457,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < (FP8 ? Tr::kV8Loads : 0); ++i) {
       const int R = v8row + i * (kThreads / Tr::kV8Ch);
       const int c0 = 2 * v8ch;  // bf16 chunks 2c, 2c+1 of the row
-      lds_store16(base + R * Tr::kVRow + 16 * (c0 ^ swz(R, Tr::kVCh)), fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y}));
-      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + 1) ^ swz(R, Tr::kVCh)), fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w}));
+      const U128 lo = fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y}), hi = fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w});
+      // odd rows store their odd chunk first: the 16 lanes of a store (two rows)
+      // then hit 16 different 16-byte bank groups
+      const int odd = R & 1;
+      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + odd) ^ swz(R, Tr::kVCh)), odd ? hi : lo);
+      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + 1 - odd) ^ swz(R, Tr::kVCh)), odd ? lo : hi);
     }
   };
 
@@ -542,7 +546,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     f32x16 s[2] = {s0, s1};
     if (SOFTCAP && BIAS == kBiasNone && capped) {
       // p = 2^(s' - post) with s' = post (1 - 2 r), r = 1 / (1 + e^(2y)): p = 2^(-2 post r)
-      const float k2 = 2.0f * kLog2e * a.softcap_pre, q2 = -2.0f * a.softcap_post;
+      // q2 r = q2 / (1 + e) = 1 / fma(e, 1/q2, 1/q2): one FMA instead of an add and a multiply
+      const float k2 = 2.0f * kLog2e * a.softcap_pre, iq2 = -0.5f / a.softcap_post;
       const int hi = lim_hi - j0 - kHStep * h;
       const int lo = lim_lo - j0 - kHStep * h;
       const int sk = a.sink_size - j0 - kHStep * h;
@@ -552,8 +557,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          float e0 = q2 * fast_rcp(1.0f + fast_exp2(s[b][r] * k2));
-          float e1 = q2 * fast_rcp(1.0f + fast_exp2(s[b][r + 1] * k2));
+          float e0 = fast_rcp(__builtin_fmaf(fast_exp2(s[b][r] * k2), iq2, iq2));
+          float e1 = fast_rcp(__builtin_fmaf(fast_exp2(s[b][r + 1] * k2), iq2, iq2));
           if (kMasked) {
             const int j0r = key_rel(b, r), j1r = key_rel(b, r + 1);
             e0 = ((j0r <= hi) && (!two_sided || j0r >= lo || j0r < sk)) ? e0 : kNegInf;

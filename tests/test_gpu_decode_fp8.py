@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_attn_amd as pk
 import synth
 from tests import _cases as C
@@ -72,3 +73,28 @@ def test_fp8_decode_bitexact_paged_vs_contiguous():
     used = torch.tensor(lens, dtype=torch.int32, device=DEV)
     o_c, l_c = pk.attn_fwd(t["q"], k, v, scale=case.scale, seqused_k=used, kv_split_tokens=128, descale=ds)
     assert torch.equal(C.bits(o_p), C.bits(o_c)) and torch.equal(C.bits(l_p), C.bits(l_c))
+
+
+@pytest.mark.parametrize("sq,colmajor", [(1, False), (1, True), (130, False), (130, True)])
+@pytest.mark.parametrize("half", [0, 1])
+def test_fp8_value_widening_is_exact(sq, colmajor, half):
+    """Q = K = 0 gives every key the same weight, so a column of V that holds
+    one E4M3FN code in every key row must come out as exactly that code's
+    value (every E4M3FN value, subnormals included, is a bf16 value). Column c
+    holds code c (half 0) or 128 + c (half 1); the NaN codes 0x7F / 0xFF are
+    replaced by 0. Split-KV decode (sq = 1) and prefill, row- and column-major V."""
+    B, H, sk, d = 1, 2, 256, 128
+    q = torch.zeros((B, H, sq, d), dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)
+    k = torch.zeros((B, H, sk, d), dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)
+    codes = torch.arange(128, dtype=torch.int32) + 128 * half
+    codes[(codes & 0x7F) == 0x7F] = 0
+    v8 = codes.to(torch.uint8).view(1, 1, 1, d).expand(B, H, sk, d).contiguous().to(DEV)
+    v = v8.view(torch.float8_e4m3fn)
+    if colmajor:
+        out, lse = pk.attn_fwd(q, k, v.transpose(2, 3).contiguous(), v_colmajor=True, kv_split_tokens=64)
+    else:
+        out, lse = pk.attn_fwd(q, k, v, kv_split_tokens=64)
+    want = torch.tensor(oracle.E4M3FN_TABLE[codes.numpy()], dtype=torch.float64)
+    got = out.double().cpu()
+    assert torch.equal(got, want.view(1, 1, 1, d).expand_as(got)), "fp8 V widening is not exact"
+    assert (lse.double().cpu() - np.log(sk)).abs().max().item() < 1e-5
