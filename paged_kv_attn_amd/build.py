@@ -56,6 +56,48 @@ def _compile(job) -> str:
     return obj
 
 
+# The host-sanitizer build of the C ABI: api.cpp and noalloc.cpp with
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the
+# -Xarch_host prefix keeps them off any device code), linked with launchers
+# that launch nothing (csrc/host_stubs.cpp). tests/test_abi_sanitized.py runs
+# the C-ABI tests against it with the ASan runtime preloaded.
+ASAN_OUT = os.path.join(OBJ, "asan", "libattn_asan.so")
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-fno-gpu-sanitize",
+       "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to preload into python)."""
+    import glob
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    hits = sorted(glob.glob(os.path.join(rocm, "lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise FileNotFoundError("no libclang_rt.asan-x86_64.so under the ROCm LLVM tree")
+    return hits[-1]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    out_dir = os.path.dirname(ASAN_OUT)
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in ("api.cpp", "noalloc.cpp", "host_stubs.cpp"):
+        obj = os.path.join(out_dir, src.replace(".cpp", ".o"))
+        cmd = [hipcc(), *_flags(), *SAN, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized compile failed for {src}:\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    tmp = ASAN_OUT + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", *SAN, "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_OUT)
+    if verbose:
+        print(f"built {ASAN_OUT}")
+    return ASAN_OUT
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
@@ -73,3 +115,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    if "--host-sanitized" in sys.argv:
+        build_host_sanitized(verbose=True)

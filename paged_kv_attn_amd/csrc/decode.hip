@@ -11,18 +11,19 @@
 // Source File": one table row per request, page_block_size tokens per page,
 // 64-bit page base + in-page offset).
 //
-// Math per granule, on v_mfma_f32_16x16x32_bf16 with the <= 16 packed query
-// rows (request position x q-heads of this kv-head) as the MFMA column
-// dimension: S^T = K Q^T with K fed straight from global memory into A-operand
-// registers (128-bit loads along d), online softmax over keys (max / sum across
-// the four 16-lane groups), O^T += V^T P^T with V copied HBM -> LDS by the
-// buffer unit (non-temporal: every V row is read once) and read back
-// transposed (ds_read_b64_tr_b16). K stays on the default cache policy: its
-// 64-byte halves of a 128-byte line arrive from two different loads.
+// Math per granule, on v_mfma_f32_16x16x32_bf16 (fp8: _fp8_fp8) with the <= 16
+// packed query rows (request position x q-heads of this kv-head) as the MFMA
+// column dimension: S^T = K Q^T, online softmax over keys (max / sum across
+// the four 16-lane groups), O^T += V^T P^T. K and V travel HBM -> LDS as whole
+// rows through the buffer unit's direct-to-LDS loads with the non-temporal
+// policy (every row is read once); K is read back into A-operand registers
+// (ds_read_b128, swizzled), V transposed (ds_read_b64_tr_b16). fp8 V goes
+// through registers instead and is widened exactly to bf16 on its way into
+// LDS; column-major V arrives as V^T rows and is read with plain 8-byte reads.
 //
-// Software pipeline: the next granule's K (registers) and V (the other LDS
-// buffer) are in flight while the current one is computed. There is no
-// barrier anywhere: all data a wave touches is its own.
+// Software pipeline: the next granule's K and V (the other LDS buffers, or
+// registers for fp8 V) are in flight while the current one is computed. There
+// is no barrier anywhere: all data a wave touches is its own.
 //
 // Each unit stores its (O, LSE) normalised (the num_splits axis of O / LSE in
 // the flash-attention epilogue page "hopper/epilogue_fwd.hpp"). The combine
