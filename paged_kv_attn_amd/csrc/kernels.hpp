@@ -38,6 +38,8 @@ struct PrefillArgs {
   int hq, hkv, ratio;
   int n_qtiles;               // packed-row tiles per (sequence, kv-head)
   int nz;                     // batch entries (batch mode) or sequences (varlen); set by the launcher
+  int items_x;                // workgroups per XCD of the launch; set by the launcher
+  int cu_per_xcd;             // CUs per XCD of the device; set by the launcher
   float c_exp2;               // multiplier taking the kernel's logit domain to log2 units
   float softcap_pre;          // softcap: raw dot * softcap_pre = (scaled logit) / cap
   float softcap_post;         // softcap: cap * log2(e)

@@ -138,8 +138,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int k_x = (int)(blockIdx.x / kXcds);       // position in this XCD's list
   const int G = group_units(a.n_qtiles);
   const int gsz = G * a.n_qtiles;
-  const int qt_i = (k_x % gsz) / G;                // rank: 0 = heaviest
-  const int unit = xcd + kXcds * ((k_x / gsz) * G + (k_x % gsz) % G);
+  // Balanced CU pairs. The dispatcher places positions c and c + C of an XCD's
+  // list (C = its CU count) on CU c, two workgroups per CU, and the older
+  // workgroup of a CU gets issue priority. Within every block of 4C positions
+  // (two rounds of the XCD's slots) the second quarter is taken in reverse, so
+  // each CU's first pair is (heavy, light) ranks, the heavier one older, and
+  // every CU carries about the same number of key tiles. Measured on causal
+  // B=4 H=16 s=2048: 82.7 -> 78.0 us; fewer than 256 of the 512 slots busy
+  // for 6 us of the end instead of 12.
+  int kk = k_x;
+  {
+    const int cx = a.cu_per_xcd, q = k_x % (4 * cx), b = k_x - q;
+    if (q >= cx && q < 2 * cx && b + 2 * cx <= a.items_x) kk = b + 3 * cx - 1 - q;
+  }
+  const int qt_i = (kk % gsz) / G;                 // rank: 0 = heaviest
+  const int unit = xcd + kXcds * ((kk / gsz) * G + (kk % gsz) % G);
   if (unit >= n_units) return;
   const int g = unit % a.hkv;                      // kv-head
   const int z = unit / a.hkv;                      // batch entry or sequence
@@ -850,11 +863,26 @@ int64_t grid_size(const PrefillArgs& a, int nz) {
   return kXcds * ((units_x + G - 1) / G) * G * a.n_qtiles;
 }
 
+// CUs per XCD of the current device (queried once per device; 32 on MI355X)
+int cus_per_xcd() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds) n = 256;
+    cache[dev] = n / kXcds;
+  }
+  return cache[dev];
+}
+
 template <int D, int DV, bool FP8, int MODE, int MK, bool SOFTCAP, int BIAS, bool VT>
 hipError_t launch_t(const PrefillArgs& a, int nz, hipStream_t stream) {
   PrefillArgs b = a;
   b.nz = nz;
   const int64_t grid = grid_size(a, nz);
+  b.items_x = (int)(grid / kXcds);
+  b.cu_per_xcd = cus_per_xcd();
   hipLaunchKernelGGL((prefill_kernel<D, DV, FP8, MODE, MK, SOFTCAP, BIAS, VT>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, b);
   return hipGetLastError();
