@@ -22,7 +22,8 @@
 // LDS; column-major V arrives as V^T rows and is read with plain 8-byte reads.
 //
 // Software pipeline: the next granule's K and V (the other LDS buffers, or
-// registers for fp8 V) are in flight while the current one is computed. There
+// registers for fp8 V) are in flight while the current one is computed; fp8,
+// whose granules carry half the bytes, keeps the next two in flight. There
 // is no barrier anywhere: all data a wave touches is its own.
 //
 // Each unit stores its (O, LSE) normalised (the num_splits axis of O / LSE in
@@ -102,16 +103,18 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char vbuf0[Tr::kVBuf];
   __shared__ __attribute__((aligned(1024))) char kbuf1[Tr::kBuf];
   __shared__ __attribute__((aligned(1024))) char vbuf1[Tr::kVBuf];
+  __shared__ __attribute__((aligned(1024))) char kbuf2[FP8 ? Tr::kBuf : 16];  // fp8's third K stage
   lds_char* const k0 = (lds_char*)kbuf0;
   lds_char* const v0 = (lds_char*)vbuf0;
   lds_char* const k1 = (lds_char*)kbuf1;
   // fp8 V is in flight in registers and widened into LDS just before its
-  // granule's products, so one bf16 V buffer serves both stages: this wave's
+  // granule's products, so one bf16 V buffer serves every stage: this wave's
   // LDS accesses stay in program order, and the widening of granule g+1 comes
-  // after the reads of granule g. 16 KB instead of 24 KB per wave lets 10
-  // waves share a CU instead of 6, which keeps as many bytes in flight per CU
-  // as the bf16 variant.
-  lds_char* const v1 = FP8 ? (lds_char*)vbuf0 : (lds_char*)vbuf1;
+  // after the reads of granule g. Three K stages and one V buffer take 20 KB
+  // per wave (8 waves per CU), with two 8 KB granules in flight per wave while
+  // a third is computed.
+  lds_char* const v1 = (lds_char*)vbuf1;  // bf16 only
+  lds_char* const k2 = (lds_char*)kbuf2;
 
   const int lane = threadIdx.x;
   const int g = blockIdx.x;      // kv-heads fastest: the units running together read the
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   // issue the loads of granule gs into the LDS buffers kb / vb (whole rows,
   // non-temporal: every K and V row is read once). A granule at or past t_hi is
   // issued with an empty range: no memory traffic, zeros everywhere.
-  U128 v8a[FP8 ? Tr::kV8 : 1], v8b[FP8 ? Tr::kV8 : 1];  // fp8 V of the two pipeline stages
+  U128 v8a[FP8 ? Tr::kV8 : 1], v8b[FP8 ? Tr::kV8 : 1], v8c[FP8 ? Tr::kV8 : 1];  // fp8 V of the pipeline stages
   auto issue = [&](int gs, lds_char* kb, lds_char* vb, U128 (&v8)[FP8 ? Tr::kV8 : 1]) {
     // readfirstlane keeps the clamp (a vector med3) from making the
     // descriptor look divergent
@@ -303,9 +306,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; e += 2) w[e / 2] &= (8 + e < nv ? 0xFFFFu : 0u) | (9 + e < nv ? 0xFFFF0000u : 0u);
         }
+        // a 16-byte LDS store resolves bank conflicts per 8 lanes over 128 bytes:
+        // rows 4m + 2, 4m + 3 store their high chunk first, so that the 8 lanes
+        // (rows 4m .. 4m + 3, two 64-byte rows per 128 bytes) hit 8 distinct slots
         lds_char* row = vb + R * (2 * kGran);
-        lds_store16(row + 16 * ((2 * c) ^ vt_sw(R)), lo);
-        lds_store16(row + 16 * ((2 * c + 1) ^ vt_sw(R)), hi);
+        const int f = (R >> 1) & 1;
+        lds_store16(row + 16 * ((2 * c + f) ^ vt_sw(R)), f ? hi : lo);
+        lds_store16(row + 16 * ((2 * c + 1 - f) ^ vt_sw(R)), f ? lo : hi);
       }
       return;
     }
@@ -313,11 +320,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (int q = 0; q < (FP8 ? Tr::kV8 : 0); ++q) {
       const int ch = 64 * q + lane, R = ch / (DV / 16), c0 = 2 * (ch % (DV / 16));
       const U128 lo = fp8x8_to_bf16x8(U64{v8[q].x, v8[q].y}), hi = fp8x8_to_bf16x8(U64{v8[q].z, v8[q].w});
-      // odd rows store their odd chunk first: the 16 lanes of a store then hit
-      // 16 different 16-byte bank groups (the swizzle keeps chunk pairs adjacent)
-      const int odd = R & 1;
-      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + odd) ^ vswz<DV>(R)), odd ? hi : lo);
-      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1 - odd) ^ vswz<DV>(R)), odd ? lo : hi);
+      // a 16-byte LDS store resolves bank conflicts per 8 lanes over 128 bytes;
+      // lanes 4 .. 7 of each 8 store their high chunk first, so the 8 lanes' 32-byte
+      // chunk pairs (256 contiguous bytes before the swizzle, which XORs the slot
+      // with a constant per 8 lanes) hit 8 distinct slots modulo 128 bytes
+      const int f = (ch >> 2) & 1;
+      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + f) ^ vswz<DV>(R)), f ? hi : lo);
+      lds_store16(vb + R * Tr::kVRow + 16 * ((c0 + 1 - f) ^ vswz<DV>(R)), f ? lo : hi);
     }
   };
 
@@ -431,19 +440,43 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   };
 
   int gs = t_lo;
-  if (gs < t_hi) {
+  if (FP8 && gs < t_hi) {
+    // three stages: granules g + 1 and g + 2 in flight while g is widened and
+    // computed (a granule at or past t_hi is issued empty)
+    issue(gs, k0, v0, v8a);
+    issue(gs + kGran, k1, v0, v8b);
+    for (;;) {
+      issue(gs + 2 * kGran, k2, v0, v8c);
+      wait_vmem_le<2 * Tr::kOps>();
+      store_v8(v0, v8a, gs);
+      compute(gs, k0, v0);
+      gs += kGran;
+      if (gs >= t_hi) break;
+      issue(gs + 2 * kGran, k0, v0, v8a);
+      wait_vmem_le<2 * Tr::kOps>();
+      store_v8(v0, v8b, gs);
+      compute(gs, k1, v0);
+      gs += kGran;
+      if (gs >= t_hi) break;
+      issue(gs + 2 * kGran, k1, v0, v8b);
+      wait_vmem_le<2 * Tr::kOps>();
+      store_v8(v0, v8c, gs);
+      compute(gs, k2, v0);
+      gs += kGran;
+      if (gs >= t_hi) break;
+    }
+    wait_vmem_le<0>();
+  } else if (gs < t_hi) {  // bf16: two stages
     issue(gs, k0, v0, v8a);
     for (;;) {
       issue(gs + kGran, k1, v1, v8b);
       wait_vmem_le<Tr::kOps>();
-      if (FP8) store_v8(v0, v8a, gs);
       vt_zero_tail(gs, v0);
       compute(gs, k0, v0);
       gs += kGran;
       if (gs >= t_hi) break;
       issue(gs + kGran, k0, v0, v8a);
       wait_vmem_le<Tr::kOps>();
-      if (FP8) store_v8(v1, v8b, gs);
       vt_zero_tail(gs, v1);
       compute(gs, k1, v1);
       gs += kGran;

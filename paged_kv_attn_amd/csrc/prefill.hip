@@ -461,8 +461,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             w[e / 2] &= (8 + e < nv ? 0xFFFFu : 0u) | (9 + e < nv ? 0xFFFF0000u : 0u);
           }
         }
-        lds_store16(base + R * (2 * kBlockN) + 16 * ((2 * c) ^ vt_swz(R)), lo);
-        lds_store16(base + R * (2 * kBlockN) + 16 * ((2 * c + 1) ^ vt_swz(R)), hi);
+        // a 16-byte LDS store resolves bank conflicts per 8 lanes over 128 bytes:
+        // odd rows store their high chunk first, so the 8 lanes (rows 2m, 2m + 1,
+        // 128 bytes each, same swizzle) hit 8 distinct slots
+        const int f = R & 1;
+        lds_store16(base + R * (2 * kBlockN) + 16 * ((2 * c + f) ^ vt_swz(R)), f ? hi : lo);
+        lds_store16(base + R * (2 * kBlockN) + 16 * ((2 * c + 1 - f) ^ vt_swz(R)), f ? lo : hi);
       }
       return;
     }
@@ -471,11 +475,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       const int R = v8row + i * (kThreads / Tr::kV8Ch);
       const int c0 = 2 * v8ch;  // bf16 chunks 2c, 2c+1 of the row
       const U128 lo = fp8x8_to_bf16x8(U64{v8[i].x, v8[i].y}), hi = fp8x8_to_bf16x8(U64{v8[i].z, v8[i].w});
-      // odd rows store their odd chunk first: the 16 lanes of a store (two rows)
-      // then hit 16 different 16-byte bank groups
-      const int odd = R & 1;
-      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + odd) ^ swz(R, Tr::kVCh)), odd ? hi : lo);
-      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + 1 - odd) ^ swz(R, Tr::kVCh)), odd ? lo : hi);
+      // a 16-byte LDS store resolves bank conflicts per 8 lanes over 128 bytes;
+      // threads 4 .. 7 of each 8 store their high chunk first, so the 8 threads'
+      // 32-byte chunk pairs (256 contiguous bytes before the swizzle, which XORs
+      // the slot with a constant per 8 threads) hit 8 distinct slots modulo 128 bytes
+      const int f = (threadIdx.x >> 2) & 1;
+      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + f) ^ swz(R, Tr::kVCh)), f ? hi : lo);
+      lds_store16(base + R * Tr::kVRow + 16 * ((c0 + 1 - f) ^ swz(R, Tr::kVCh)), f ? lo : hi);
     }
   };
 
