@@ -565,6 +565,8 @@ def other_workloads(steps, warmup, with_cpu):
                               "algorithmic_bytes", nb),
         "splits": pk.attn_num_splits(p8, 64, 32, 8, 1, W * 128)}
     log(f"fp8 paged decode {mean * 1e3:.1f} us, {gbs:.0f} GB/s")
+    if with_cpu:
+        out["paged_decode_fp8"]["cpu_baseline"] = cpu_baseline_decode(c8, 8)
     del c8, t8, o8, l8, ws8
     if with_cpu:
         out["tiny_fp32"]["cpu_baseline"] = cpu_baseline_tiny(c1)
