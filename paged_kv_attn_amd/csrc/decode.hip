@@ -346,9 +346,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       st[kb] = f32x4{};
       if (FP8) {
+        // an opaque block offset keeps the compiler from pairing the two key
+        // blocks' reads into one two-address read, whose halves (2 KB apart) hit
+        // the same banks
+        int kofs = 16 * kb * Tr::kRow;
+        asm volatile("" : "+v"(kofs));
         U64 kf[Tr::kSteps];
 #pragma unroll
-        for (int s = 0; s < Tr::kSteps; ++s) kf[s] = lds_load8(kbuf + k8_addr(kb, s));
+        for (int s = 0; s < Tr::kSteps; ++s) kf[s] = lds_load8(kbuf + kofs + k8_addr(0, s));
 #pragma unroll
         for (int s = 0; s < Tr::kSteps; ++s) st[kb] = mfma16_fp8(kf[s], qf8[s], st[kb]);
       } else {
