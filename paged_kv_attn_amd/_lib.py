@@ -103,6 +103,17 @@ def check(status: int):
         raise AttnError(status, lib().attn_last_error().decode(errors="replace"))
 
 
+_I64_CACHE: dict = {}
+
+
 def i64_array(vals):
-    arr = (ctypes.c_int64 * len(vals))(*[int(x) for x in vals])
+    """A ctypes int64 array holding vals. The library only reads these arrays
+    (const int64_t*), so equal stride tuples share one cached array."""
+    key = tuple(vals)
+    arr = _I64_CACHE.get(key)
+    if arr is None:
+        arr = (ctypes.c_int64 * len(key))(*map(int, key))
+        if len(_I64_CACHE) >= 1024:
+            _I64_CACHE.clear()
+        _I64_CACHE[key] = arr
     return arr

@@ -20,23 +20,35 @@ _IN_TYPES = {torch.float32: _lib.ATTN_F32, torch.bfloat16: _lib.ATTN_BF16,
              torch.float8_e4m3fn: _lib.ATTN_FP8_E4M3}
 
 
+# attn_params_t values built from the scalar options, by option tuple: a call
+# copies its template (a memcpy) instead of rebuilding it through the library
+_PARAMS_CACHE: dict = {}
+
+
 def _params(dtype, d, scale, causal, window, softcap, descale, kv_split_tokens, sink_size=0, sink_logits=None,
             bias=None, alibi_slopes=None, out_dtype=None, o_scale=1.0):
     if dtype not in _IN_TYPES:
         raise TypeError(f"unsupported input dtype {dtype}")
-    p = AttnParams()
-    lib().attn_params_init(ctypes.byref(p), float(scale if scale is not None else 1.0 / math.sqrt(d)))
-    p.in_dtype = _IN_TYPES[dtype]
-    p.out_dtype = _IN_TYPES[out_dtype_for(dtype, out_dtype)]
-    p.o_scale = float(o_scale)
-    p.softcap = float(softcap)
-    if window is not None:
-        p.window_left, p.window_right = int(window[0]), int(window[1])
-    elif causal:
-        p.window_left, p.window_right = -1, 0
-    p.q_descale, p.k_descale, p.v_descale = (float(x) for x in descale)
-    p.kv_split_tokens = int(kv_split_tokens)
-    p.sink_size = int(sink_size)
+    ds = tuple(float(x) for x in descale)
+    win = (int(window[0]), int(window[1])) if window is not None else ((-1, 0) if causal else None)
+    key = (dtype, d, scale, win, float(softcap), ds, int(kv_split_tokens), int(sink_size), out_dtype, float(o_scale))
+    base = _PARAMS_CACHE.get(key)
+    if base is None:
+        base = AttnParams()
+        lib().attn_params_init(ctypes.byref(base), float(scale if scale is not None else 1.0 / math.sqrt(d)))
+        base.in_dtype = _IN_TYPES[dtype]
+        base.out_dtype = _IN_TYPES[out_dtype_for(dtype, out_dtype)]
+        base.o_scale = float(o_scale)
+        base.softcap = float(softcap)
+        if win is not None:
+            base.window_left, base.window_right = win
+        base.q_descale, base.k_descale, base.v_descale = ds
+        base.kv_split_tokens = int(kv_split_tokens)
+        base.sink_size = int(sink_size)
+        if len(_PARAMS_CACHE) >= 256:
+            _PARAMS_CACHE.clear()
+        _PARAMS_CACHE[key] = base
+    p = AttnParams.from_buffer_copy(base)   # the caller's own copy: per-call fields go into it
     if sink_logits is not None:
         if sink_logits.dtype != torch.float32 or not sink_logits.is_contiguous():
             raise TypeError("sink_logits must be a contiguous float32 tensor [Hq]")
@@ -72,49 +84,62 @@ def out_dtype_for(dtype, out_dtype=None):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    """A tensor's data pointer as the integer ctypes passes for a void* (None: NULL)."""
+    return t.data_ptr() if t is not None else None
+
+
+# torch's raw current-stream lookup by device index (what torch.cuda.current_stream
+# wraps in a Stream object); the public call is the fallback
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t):
     """torch's current stream on t's device; t must be a GPU tensor (the
     library only ever receives device pointers)."""
-    _need(t.is_cuda, f"tensors must be on a GPU (got {t.device})")
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if not (t.is_cuda):
+        raise ValueError(f"tensors must be on a GPU (got {t.device})")
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 # ---- argument checks --------------------------------------------------------
 # The C ABI sees only pointers, element strides and sizes: it scales strides by
 # the element size of in_dtype / out_dtype and cannot tell a host pointer from a
 # device one. These checks run before any call, so a tensor of the wrong type,
-# shape or device never reaches a kernel.
-
-def _need(cond, msg, exc=ValueError):
-    if not cond:
-        raise exc(msg)
-
+# shape or device never reaches a kernel. Messages are formatted only on failure.
 
 def _check_like(name, t, q):
     """t shares q's dtype and device, and its last dim is contiguous."""
-    _need(t.dtype == q.dtype, f"{name} has dtype {t.dtype}, expected {q.dtype} (the dtype of q)", TypeError)
-    _need(t.device == q.device, f"{name} is on {t.device}, expected {q.device} (the device of q)")
-    _need(t.dim() == 0 or t.shape[-1] <= 1 or t.stride(-1) == 1, f"{name} must have unit stride in its last dim")
+    if not (t.dtype == q.dtype):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype} (the dtype of q)")
+    if not (t.device == q.device):
+        raise ValueError(f"{name} is on {t.device}, expected {q.device} (the device of q)")
+    if not (t.dim() == 0 or t.shape[-1] <= 1 or t.stride(-1) == 1):
+        raise ValueError(f"{name} must have unit stride in its last dim")
 
 
 def _check_index(name, t, q, n_min):
     """int32 metadata: contiguous, on q's device, at least n_min entries."""
     if t is None:
         return
-    _need(t.dtype == torch.int32, f"{name} must be int32 (got {t.dtype})", TypeError)
-    _need(t.device == q.device, f"{name} is on {t.device}, expected {q.device}")
-    _need(t.is_contiguous(), f"{name} must be contiguous")
-    _need(t.numel() >= n_min, f"{name} has {t.numel()} entries, at least {n_min} needed")
+    if not (t.dtype == torch.int32):
+        raise TypeError(f"{name} must be int32 (got {t.dtype})")
+    if not (t.device == q.device):
+        raise ValueError(f"{name} is on {t.device}, expected {q.device}")
+    if not (t.is_contiguous()):
+        raise ValueError(f"{name} must be contiguous")
+    if not (t.numel() >= n_min):
+        raise ValueError(f"{name} has {t.numel()} entries, at least {n_min} needed")
 
 
 def _check_f32(name, t, q):
     if t is None:
         return
-    _need(t.dtype == torch.float32, f"{name} must be float32 (got {t.dtype})", TypeError)
-    _need(t.device == q.device, f"{name} is on {t.device}, expected {q.device}")
+    if not (t.dtype == torch.float32):
+        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if not (t.device == q.device):
+        raise ValueError(f"{name} is on {t.device}, expected {q.device}")
 
 
 def _resolve_out_dtype(q, out, out_dtype):
@@ -127,20 +152,28 @@ def _resolve_out_dtype(q, out, out_dtype):
 def _check_out(out, shape, dtype, q):
     if out is None:
         return
-    _need(out.dtype == dtype, f"out has dtype {out.dtype}, expected {dtype}", TypeError)
-    _need(tuple(out.shape) == tuple(shape), f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
-    _need(out.device == q.device, f"out is on {out.device}, expected {q.device}")
-    _need(out.stride(-1) == 1 or shape[-1] <= 1, "out must have unit stride in its last dim")
+    if not (out.dtype == dtype):
+        raise TypeError(f"out has dtype {out.dtype}, expected {dtype}")
+    if not (tuple(out.shape) == tuple(shape)):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if not (out.device == q.device):
+        raise ValueError(f"out is on {out.device}, expected {q.device}")
+    if not (out.stride(-1) == 1 or shape[-1] <= 1):
+        raise ValueError("out must have unit stride in its last dim")
 
 
 def _check_lse(lse, shape, q):
     """lse is written as a dense fp32 array of this shape."""
     if lse is None:
         return
-    _need(lse.dtype == torch.float32, f"lse must be float32 (got {lse.dtype})", TypeError)
-    _need(tuple(lse.shape) == tuple(shape), f"lse has shape {tuple(lse.shape)}, expected {tuple(shape)}")
-    _need(lse.is_contiguous(), "lse must be contiguous")
-    _need(lse.device == q.device, f"lse is on {lse.device}, expected {q.device}")
+    if not (lse.dtype == torch.float32):
+        raise TypeError(f"lse must be float32 (got {lse.dtype})")
+    if not (tuple(lse.shape) == tuple(shape)):
+        raise ValueError(f"lse has shape {tuple(lse.shape)}, expected {tuple(shape)}")
+    if not (lse.is_contiguous()):
+        raise ValueError("lse must be contiguous")
+    if not (lse.device == q.device):
+        raise ValueError(f"lse is on {lse.device}, expected {q.device}")
 
 
 def _check_params_tensors(q, sink_logits, bias, alibi_slopes):
@@ -171,8 +204,10 @@ def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None
     if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
-        _need(workspace.device == device, f"workspace is on {workspace.device}, expected {device}")
-        _need(workspace.is_contiguous(), "workspace must be contiguous")
+        if not (workspace.device == device):
+            raise ValueError(f"workspace is on {workspace.device}, expected {device}")
+        if not (workspace.is_contiguous()):
+            raise ValueError("workspace must be contiguous")
         return workspace
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
@@ -190,20 +225,27 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
     B, Hq, sq, d = q.shape
     Hkv, sk = k.shape[1], k.shape[2]
     dv = v.shape[2] if v_colmajor else v.shape[3]
-    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
-    _need(k.dim() == 4 and v.dim() == 4, "k and v must be 4-d")
+    if not (q.stride(-1) == 1):
+        raise ValueError("q must have unit stride in its last dim")
+    if not (k.dim() == 4 and v.dim() == 4):
+        raise ValueError("k and v must be 4-d")
     _check_like("k", k, q)
     if not v_colmajor:
         _check_like("v", v, q)
     else:
-        _need(v.dtype == q.dtype and v.device == q.device, "v must share q's dtype and device", TypeError)
-    _need(k.shape[3] == d, f"k has head dim {k.shape[3]}, q has {d}")
-    _need((v.shape[3] if v_colmajor else v.shape[2]) == sk and v.shape[1] == Hkv, "v's shape does not match k's")
-    _need(cache_batch_idx is not None or (k.shape[0] == B and v.shape[0] == B), "k / v batch size differs from q's")
+        if not (v.dtype == q.dtype and v.device == q.device):
+            raise TypeError("v must share q's dtype and device")
+    if not (k.shape[3] == d):
+        raise ValueError(f"k has head dim {k.shape[3]}, q has {d}")
+    if not ((v.shape[3] if v_colmajor else v.shape[2]) == sk and v.shape[1] == Hkv):
+        raise ValueError("v's shape does not match k's")
+    if not (cache_batch_idx is not None or (k.shape[0] == B and v.shape[0] == B)):
+        raise ValueError("k / v batch size differs from q's")
     _check_index("seqused_q", seqused_q, q, B)
     _check_index("seqused_k", seqused_k, q, B)
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
-    _need(bias is None or bias.dim() == 4, "a batch-mode bias is 4-d [B|1, Hq|1, sq, sk]")
+    if not (bias is None or bias.dim() == 4):
+        raise ValueError("a batch-mode bias is 4-d [B|1, Hq|1, sq, sk]")
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (B, Hq, sq, dv), out_dtype, q)
     _check_lse(lse, (B, Hq, sq), q)
@@ -247,16 +289,21 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
     n = cu_seqlens_q.numel() - 1
-    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
-    _need(k.dim() == 3 and v.dim() == 3, "k and v must be 3-d [tokens, heads, dim]")
+    if not (q.stride(-1) == 1):
+        raise ValueError("q must have unit stride in its last dim")
+    if not (k.dim() == 3 and v.dim() == 3):
+        raise ValueError("k and v must be 3-d [tokens, heads, dim]")
     _check_like("k", k, q)
     _check_like("v", v, q)
-    _need(k.shape[2] == d and v.shape[:2] == k.shape[:2], "k / v shapes do not match q")
-    _need(n >= 0, "cu_seqlens_q needs at least one entry")
+    if not (k.shape[2] == d and v.shape[:2] == k.shape[:2]):
+        raise ValueError("k / v shapes do not match q")
+    if not (n >= 0):
+        raise ValueError("cu_seqlens_q needs at least one entry")
     _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
     _check_index("cu_seqlens_k", cu_seqlens_k, q, n + 1)
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
-    _need(bias is None or bias.dim() == 3, "a varlen bias is 3-d [Hq|1, Tq, Kmax]")
+    if not (bias is None or bias.dim() == 3):
+        raise ValueError("a varlen bias is 3-d [Hq|1, Tq, Kmax]")
     dv = v.shape[2]
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (Tq, Hq, dv), out_dtype, q)
@@ -279,21 +326,30 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 
 def _check_pools(q, d, k_pool, v_pool, v_colmajor=False):
-    _need(k_pool.dim() == 4 and v_pool.dim() == 4, "pools must be 4-d [num_pages, page_size, Hkv, dim]")
+    if not (k_pool.dim() == 4 and v_pool.dim() == 4):
+        raise ValueError("pools must be 4-d [num_pages, page_size, Hkv, dim]")
     _check_like("k_pool", k_pool, q)
     if not v_colmajor:
         _check_like("v_pool", v_pool, q)
-    _need(k_pool.shape[3] == d, f"k_pool has head dim {k_pool.shape[3]}, q has {d}")
-    _need(v_pool.shape[:3] == k_pool.shape[:3], "v_pool's [num_pages, page_size, Hkv] differ from k_pool's")
+    if not (k_pool.shape[3] == d):
+        raise ValueError(f"k_pool has head dim {k_pool.shape[3]}, q has {d}")
+    if not (v_pool.shape[:3] == k_pool.shape[:3]):
+        raise ValueError("v_pool's [num_pages, page_size, Hkv] differ from k_pool's")
 
 
 def _check_table(block_table, q, rows):
-    _need(block_table.dtype == torch.int32, "block_table must be int32", TypeError)
-    _need(block_table.dim() == 2, "block_table must be 2-d [rows, pages]")
-    _need(block_table.device == q.device, f"block_table is on {block_table.device}, expected {q.device}")
-    _need(block_table.shape[0] >= rows, f"block_table has {block_table.shape[0]} rows, {rows} needed")
-    _need(block_table.stride(1) == 1 or block_table.shape[1] <= 1, "block_table rows must be contiguous")
-    _need(block_table.stride(0) >= block_table.shape[1], "block_table rows must not overlap")
+    if not (block_table.dtype == torch.int32):
+        raise TypeError("block_table must be int32")
+    if not (block_table.dim() == 2):
+        raise ValueError("block_table must be 2-d [rows, pages]")
+    if not (block_table.device == q.device):
+        raise ValueError(f"block_table is on {block_table.device}, expected {q.device}")
+    if not (block_table.shape[0] >= rows):
+        raise ValueError(f"block_table has {block_table.shape[0]} rows, {rows} needed")
+    if not (block_table.stride(1) == 1 or block_table.shape[1] <= 1):
+        raise ValueError("block_table rows must be contiguous")
+    if not (block_table.stride(0) >= block_table.shape[1]):
+        raise ValueError("block_table rows must not overlap")
 
 
 def _set_v_pool(p, d, k_pool, v_pool):
@@ -321,23 +377,24 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if v_colmajor:
-        _need(v_pool.dim() == 4 and v_pool.shape[0] == num_pages and v_pool.shape[1] == Hkv and
-              v_pool.shape[3] == page_size and v_pool.stride(3) == 1,
-              "column-major v_pool must be [num_pages, Hkv, d, page_size] with unit stride over keys")
-        _need(v_pool.dtype == q.dtype and v_pool.device == q.device, "v_pool must share q's dtype and device",
-              TypeError)
+        if not (v_pool.dim() == 4 and v_pool.shape[0] == num_pages and v_pool.shape[1] == Hkv and v_pool.shape[3] == page_size and v_pool.stride(3) == 1):
+            raise ValueError("column-major v_pool must be [num_pages, Hkv, d, page_size] with unit stride over keys")
+        if not (v_pool.dtype == q.dtype and v_pool.device == q.device):
+            raise TypeError("v_pool must share q's dtype and device")
         v_view = v_pool.permute(0, 3, 1, 2)          # the [num_pages, page_size, Hkv, d] logical view
     else:
         v_view = v_pool
     dv = v_view.shape[3]
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
-    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
+    if not (q.stride(-1) == 1):
+        raise ValueError("q must have unit stride in its last dim")
     _check_pools(q, d, k_pool, v_view, v_colmajor)
     _check_table(block_table, q, B)
     _check_index("seqlens_k", seqlens_k, q, B)
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
-    _need(bias is None or bias.dim() == 4, "a paged bias is 4-d [B|1, Hq|1, sq, Kmax]")
+    if not (bias is None or bias.dim() == 4):
+        raise ValueError("a paged bias is 4-d [B|1, Hq|1, sq, Kmax]")
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (B, Hq, sq, dv), out_dtype, q)
     _check_lse(lse, (B, Hq, sq), q)
@@ -387,15 +444,18 @@ def attn_fwd_varlen_paged(q, k_pool, v_pool, cu_seqlens_q, seqlens_k, block_tabl
         if t is not None and t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")
     n = cu_seqlens_q.numel() - 1
-    _need(n >= 0, "cu_seqlens_q needs at least one entry")
-    _need(q.stride(-1) == 1, "q must have unit stride in its last dim")
+    if not (n >= 0):
+        raise ValueError("cu_seqlens_q needs at least one entry")
+    if not (q.stride(-1) == 1):
+        raise ValueError("q must have unit stride in its last dim")
     _check_pools(q, d, k_pool, v_pool)
     _check_table(block_table, q, n)
     _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
     _check_index("seqlens_k", seqlens_k, q, n)
     _check_index("kv_start", kv_start, q, n)
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
-    _need(bias is None or bias.dim() == 3, "a varlen bias is 3-d [Hq|1, Tq, Kmax]")
+    if not (bias is None or bias.dim() == 3):
+        raise ValueError("a varlen bias is 3-d [Hq|1, Tq, Kmax]")
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (Tq, Hq, v_pool.shape[3]), out_dtype, q)
     _check_lse(lse, (Hq, Tq), q)

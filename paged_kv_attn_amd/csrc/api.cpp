@@ -428,7 +428,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
     a.wl = p->window_left; a.wr = p->window_right;
     if (log_on()) {
       char g[96];
-      snprintf(g, sizeof(g), "grid=%lld workgroups x 256 threads", (long long)B * Hq * ((sq + 15) / 16));
+      snprintf(g, sizeof(g), "grid=%lld workgroups x 256 threads", (long long)attn::f32_workgroups(a));
       log_call("attn_fwd", "f32", p, d, d, B, Hq, Hkv, sq, sk, g);
     }
     return launched(attn::launch_f32(a, d, s));

@@ -138,5 +138,6 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, int dv, int in_type, int 
 hipError_t launch_decode(const DecodeArgs& a, const CombineArgs& c, int d, int dv, bool paged, int B,
                          hipStream_t stream);
 hipError_t launch_f32(const F32Args& a, int d, hipStream_t stream);
+int64_t f32_workgroups(const F32Args& a);  // workgroups of launch_f32(a, ..)
 
 }  // namespace attn

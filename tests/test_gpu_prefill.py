@@ -93,6 +93,17 @@ def test_f32_parity(B, H, s, d, causal, hkv):
     C.assert_parity(out, lse, O, LSE, "f32", f"f32 {B}x{H}x{s}x{d}")
 
 
+@pytest.mark.parametrize("sq,sk,window", [(37, 37, (0, 0)), (20, 3, None), (70, 130, (2, 1)), (9, 1, None)])
+def test_f32_rows_with_fewer_keys_than_key_groups(sq, sk, window):
+    """The fp32 kernel splits each row's keys over four lane groups (key j to
+    group j % 4) and merges them at the end: rows that see 1-3 keys leave some
+    groups without a key, which must add nothing."""
+    case = _dense(1, 4, 2, sq, sk, 64, "f32", seed=sq * 7 + sk, window=window)
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "f32", f"f32 {sq}x{sk} window {window}")
+
+
 def test_f32_softcap_window_seqused():
     case = _dense(2, 2, 2, 150, 170, 64, "f32", seed=9, window=(40, 5), softcap=3.0, seqused_q=[150, 60],
                   seqused_k=[170, 90])
