@@ -104,6 +104,29 @@ def test_f32_rows_with_fewer_keys_than_key_groups(sq, sk, window):
     C.assert_parity(out, lse, O, LSE, "f32", f"f32 {sq}x{sk} window {window}")
 
 
+@pytest.mark.parametrize("seed", range(48))
+def test_f32_random_mix(seed):
+    """Seeded draws over the fp32 path's options: d, GQA ratio, batch, ragged
+    query and key lengths (including no keys), no mask / causal / two-sided
+    window, soft-cap, and per-entry used lengths."""
+    r = np.random.default_rng(30_000 + seed)
+    d, hkv, ratio = int(r.choice([64, 128])), int(r.choice([1, 2])), int(r.choice([1, 2, 4]))
+    B, sq, sk = int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.integers(0, 400))
+    m = int(r.integers(0, 3))
+    causal = m == 1
+    window = (int(r.integers(0, 100)), int(r.integers(0, 20))) if m == 2 else None
+    softcap = float(r.choice([0.0, 3.0]))
+    used = r.random() < 0.3
+    seqused_q = [int(r.integers(0, sq + 1)) for _ in range(B)] if used else None
+    seqused_k = [int(r.integers(0, sk + 1)) for _ in range(B)] if used else None
+    case = _dense(B, hkv * ratio, hkv, sq, sk, d, "f32", seed=30_000 + seed, causal=causal, window=window,
+                  softcap=softcap, seqused_q=seqused_q, seqused_k=seqused_k)
+    out, lse = C.run_dense(case)
+    O, LSE = C.oracle_dense(case)
+    C.assert_parity(out, lse, O, LSE, "f32", f"f32 mix seed {seed}: B={B} Hq={hkv * ratio} Hkv={hkv} sq={sq} "
+                    f"sk={sk} d={d} causal={causal} window={window} softcap={softcap} used={seqused_q}/{seqused_k}")
+
+
 def test_f32_softcap_window_seqused():
     case = _dense(2, 2, 2, 150, 170, 64, "f32", seed=9, window=(40, 5), softcap=3.0, seqused_q=[150, 60],
                   seqused_k=[170, 90])
