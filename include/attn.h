@@ -81,7 +81,8 @@
  *     read on every call) each accepted call writes one line to stderr: the
  *     entry point, the path taken (prefill, split-KV decode, f32), the types,
  *     shape and mask, the launch grid and the split plan (the analogue of the
- *     Composable Kernel page's GetName / PrintParameters of a kernel instance).
+ *     Composable Kernel page's GetName / PrintParameters of a kernel instance);
+ *     each refused or failed call writes "attn: error <status>: <message>".
  */
 #ifndef ATTN_H_
 #define ATTN_H_

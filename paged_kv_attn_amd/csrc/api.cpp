@@ -21,11 +21,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+bool log_on();
+
+// Records the failure for attn_last_error(); under ATTN_LOG also one stderr line.
 attn_status_t fail(attn_status_t st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
+  if (log_on()) fprintf(stderr, "attn: error %d: %s\n", (int)st, g_err);
   return st;
 }
 
@@ -212,7 +216,8 @@ constexpr int kPrefillTileRows = 64;
 constexpr int kDecodeGranRows = 32;
 
 // ---- ATTN_LOG: one stderr line per accepted call (entry point, path, types,
-// shape, mask, launch grid, split plan), read per call like ATTN_VALIDATE ----
+// shape, mask, launch grid, split plan) and one per refused or failed call
+// (status and message), read per call like ATTN_VALIDATE ----
 bool log_on() {
   const char* e = getenv("ATTN_LOG");
   return e && *e && strcmp(e, "0") != 0;

@@ -28,6 +28,8 @@ int prefill_rows_per_tile(int) { return 128; }
 
 int64_t prefill_workgroups(const PrefillArgs& a, int nz) { return (int64_t)a.n_qtiles * a.hkv * nz; }
 
+int64_t f32_workgroups(const F32Args& a) { return (int64_t)a.B * a.hq * ((a.sq + 3) / 4); }
+
 hipError_t launch_prefill(const PrefillArgs& a, int, int, int, int, int, hipStream_t) {
   touch(a);
   return hipSuccess;

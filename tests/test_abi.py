@@ -364,8 +364,9 @@ def test_row_stride_span_refused_on_varlen_and_paged():
 
 def test_attn_log_prints_one_line_per_accepted_call():
     """ATTN_LOG: one stderr line naming the entry point, path, grid and split
-    plan for a call that passed validation (here the launch itself then fails:
-    there is no GPU in this process)."""
+    plan for a call that passed validation, and one line with the status and
+    message for a call that is refused or fails (here every launch fails: there
+    is no GPU in this process)."""
     import subprocess
     import sys
     code = (
@@ -381,13 +382,20 @@ def test_attn_log_prints_one_line_per_accepted_call():
         "ws = lib().attn_workspace_bytes(ctypes.byref(p), 4, 32, 8, 1, 128, 4096)\n"
         "kst = [8 * 4096 * 128, 4096 * 128, 128]\n"
         "lib().attn_fwd(ctypes.byref(p), F, F, F, F, N, 4, 32, 8, 1, 4096, 128, i64_array([32 * 128, 128, 128]),"
-        " i64_array(kst), i64_array(kst), i64_array([32 * 128, 128, 128]), N, N, F, ws, N)\n" % ROOT)
+        " i64_array(kst), i64_array(kst), i64_array([32 * 128, 128, 128]), N, N, F, ws, N)\n"
+        "p.scale = -1.0\n"
+        "lib().attn_fwd(ctypes.byref(p), F, F, F, F, N, 1, 2, 2, 64, 64, 128, i64_array(st), i64_array(st),"
+        " i64_array(st), i64_array(st), N, N, N, 0, N)\n" % ROOT)   # refused: the scale must be > 0
     env = dict(os.environ, ATTN_LOG="1")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
-    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("attn: ")]
+    all_lines = [ln for ln in r.stderr.splitlines() if ln.startswith("attn: ")]
+    lines = [ln for ln in all_lines if not ln.startswith("attn: error")]
+    errors = [ln for ln in all_lines if ln.startswith("attn: error")]
     assert len(lines) == 2, r.stderr
     assert "attn_fwd path=prefill" in lines[0] and "grid=" in lines[0] and "Hq=2" in lines[0]
     assert "path=split-kv decode" in lines[1] and "splits=" in lines[1] and "combine grid=" in lines[1]
+    # the refusal (and, without a GPU, the two failed launches before it)
+    assert errors and errors[-1].startswith("attn: error 1:") and "scale" in errors[-1], r.stderr
     env["ATTN_LOG"] = "0"
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert not [ln for ln in r.stderr.splitlines() if ln.startswith("attn: ")]
