@@ -377,7 +377,8 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if v_colmajor:
-        if not (v_pool.dim() == 4 and v_pool.shape[0] == num_pages and v_pool.shape[1] == Hkv and v_pool.shape[3] == page_size and v_pool.stride(3) == 1):
+        if not (v_pool.dim() == 4 and v_pool.shape[0] == num_pages and v_pool.shape[1] == Hkv
+                and v_pool.shape[3] == page_size and v_pool.stride(3) == 1):
             raise ValueError("column-major v_pool must be [num_pages, Hkv, d, page_size] with unit stride over keys")
         if not (v_pool.dtype == q.dtype and v_pool.device == q.device):
             raise TypeError("v_pool must share q's dtype and device")
