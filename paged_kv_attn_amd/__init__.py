@@ -9,6 +9,7 @@ from ._lib import AttnError, AttnParams  # noqa: F401
 from .api import (  # noqa: F401
     attn_fwd,
     attn_fwd_paged,
+    attn_fwd_paged_noalloc,
     attn_fwd_varlen,
     attn_fwd_varlen_paged,
     attn_last_error,

@@ -374,6 +374,27 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
     [B|1, Hq|1, sq, Kmax]) is indexed by the logical key position. With
     ``v_colmajor`` v_pool is [num_pages, Hkv, d, page_size] (each V page of
     each kv-head stored head-dim-major, keys contiguous). Returns (out, lse)."""
+    return _paged(q, k_pool, v_pool, block_table, seqlens_k, scale, causal, window, softcap, descale, out, lse,
+                  return_lse, kv_split_tokens, workspace, sink_size, sink_logits, alibi_slopes, out_dtype, o_scale,
+                  bias, v_colmajor, noalloc=False)
+
+
+def attn_fwd_paged_noalloc(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, causal=False, window=None,
+                           softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None, return_lse=True,
+                           kv_split_tokens=0, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None,
+                           o_scale=1.0, bias=None, v_colmajor=False):
+    """attn_fwd_paged without a workspace: the split-KV partials go to the
+    library's per-GPU scratch array (calls that overlap on one GPU race on it;
+    a shape whose partials exceed it raises). For callers that cannot allocate
+    during the call, so pass ``out`` (and ``lse``, or return_lse=False)."""
+    return _paged(q, k_pool, v_pool, block_table, seqlens_k, scale, causal, window, softcap, descale, out, lse,
+                  return_lse, kv_split_tokens, None, sink_size, sink_logits, alibi_slopes, out_dtype, o_scale,
+                  bias, v_colmajor, noalloc=True)
+
+
+def _paged(q, k_pool, v_pool, block_table, seqlens_k, scale, causal, window, softcap, descale, out, lse, return_lse,
+           kv_split_tokens, workspace, sink_size, sink_logits, alibi_slopes, out_dtype, o_scale, bias, v_colmajor,
+           noalloc):
     B, Hq, sq, d = q.shape
     num_pages, page_size, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     if v_colmajor:
@@ -416,10 +437,16 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlens_k, *, scale=None, cau
         out = torch.empty((B, Hq, sq, dv), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=q.device)
-    ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, W * page_size)
-    ws = _workspace(ws_bytes, q.device, workspace)
     kv_stride = i64_array([k_pool.stride(0), k_pool.stride(2), k_pool.stride(1)])
     st = lambda t: i64_array(t.stride()[:3])  # noqa: E731
+    if noalloc:
+        check(lib().attn_fwd_paged_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                                           _ptr(lse), _ptr(block_table), int(block_table.stride(0)), _ptr(seqlens_k),
+                                           B, sq, Hq, Hkv, d, page_size, num_pages, st(q), kv_stride, st(out),
+                                           _stream(q)))
+        return out, lse
+    ws_bytes = attn_workspace_bytes(p, B, Hq, Hkv, sq, d, W * page_size)
+    ws = _workspace(ws_bytes, q.device, workspace)
     check(lib().attn_fwd_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
                                _ptr(block_table), int(block_table.stride(0)), _ptr(seqlens_k),
                                B, sq, Hq, Hkv, d, page_size, num_pages, st(q), kv_stride, st(out),

@@ -61,3 +61,59 @@ def test_noalloc_refuses_partials_beyond_the_scratch_array():
     assert need > 64 << 20
     assert _noalloc(case, out, lse, kv_split_tokens=64) == 3
     assert "64 MiB" in pk.attn_last_error() or str(64 << 20) in pk.attn_last_error()
+
+
+def _noalloc_py(case, out, lse, **kw):
+    t = case.t
+    return pk.attn_fwd_paged_noalloc(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seqlens_k"],
+                                     scale=case.scale, window=(case.window_left, case.window_right),
+                                     softcap=case.softcap,
+                                     descale=(case.descale["q"], case.descale["k"], case.descale["v"]),
+                                     out=out, lse=lse, **kw)
+
+
+def test_noalloc_in_a_captured_graph():
+    """The callers it is for capture it: a bf16 and an fp8 decode through the
+    binding's attn_fwd_paged_noalloc, captured in one graph and replayed four
+    times, with eager no-allocation calls of another shape (which overwrite the
+    scratch array) between the replays. Every replay gives the eager call's
+    bits, which equal attn_fwd_paged's with a workspace."""
+    a = synth.paged_case([300, 1000, 64, 2500], 1, 32, 8, 128, 64, "bf16", seed=504, device=DEV)
+    b = synth.paged_case([700, 90], 1, 16, 4, 128, 128, "fp8", seed=505, device=DEV, head_major=True)
+    other = synth.paged_case([4000, 33], 2, 8, 2, 128, 128, "bf16", seed=506, device=DEV, causal=True)
+    bufs = []
+    for c in (a, b):
+        ref_o, ref_l = C.run_paged(c, kv_split_tokens=256)
+        bufs.append((torch.empty_like(ref_o), torch.empty_like(ref_l), ref_o, ref_l))
+    o3, l3 = C.run_paged(other)
+
+    def step():
+        for c, (o, l, _, _) in zip((a, b), bufs):
+            _noalloc_py(c, o, l, kv_split_tokens=256)
+
+    step()   # eager: also the first call on this device, which looks up the array's address
+    torch.cuda.synchronize()
+    for o, l, ref_o, ref_l in bufs:
+        assert torch.equal(C.bits(o), C.bits(ref_o)) and torch.equal(C.bits(l), C.bits(ref_l))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for o, l, _, _ in bufs:
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        o_x, l_x = torch.empty_like(o3), torch.empty_like(l3)
+        _noalloc_py(other, o_x, l_x)            # eager work that reuses the scratch array
+        torch.cuda.synchronize()
+        assert torch.equal(C.bits(o_x), C.bits(o3)) and torch.equal(C.bits(l_x), C.bits(l3))
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (o, l, ref_o, ref_l) in enumerate(bufs):
+            assert torch.equal(C.bits(o), C.bits(ref_o)) and torch.equal(C.bits(l), C.bits(ref_l)), \
+                f"replay {i}, call {k}: differs from the eager call"
