@@ -313,7 +313,8 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p,
  * attn_fwd_paged (the same kernels, bit-identical results). The split-KV
  * partials go to a 64 MiB array that the library keeps on each GPU it runs on
  * until the process ends (its address is looked up on the first call on a
- * device); the call itself allocates nothing. A shape whose partials need more
+ * device, so make one call on a device before capturing calls in a graph);
+ * the call itself allocates nothing. A shape whose partials need more
  * than 64 MiB (attn_workspace_bytes() > 64 MiB) is refused with
  * ATTN_EWORKSPACE before any launch. Every call on one GPU shares that GPU's
  * array: calls that overlap on one GPU (work queued on two streams, or from
