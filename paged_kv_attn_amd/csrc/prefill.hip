@@ -515,6 +515,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] = f32x16{};
 
+  // K operand addresses of the bf16 steps, kept in registers (an XOR with the
+  // lane's swizzle, so not an immediate offset): one add less per step and tile
+  int kaddr[Tr::kQkSteps];
+#pragma unroll
+  for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
+    kaddr[kk] = k_addr(kk);
+    asm volatile("" : "+v"(kaddr[kk]));  // keep the value, do not rematerialise it per tile
+  }
   // S^T = K Q^T for the tile in K slot `slot`: two interleaved 32-key chains
   auto qk = [&](int slot, f32x16& s0, f32x16& s1) {
     const lds_char* kt = kslot(slot);
@@ -533,14 +541,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
     } else {
       // operands of step kk+1 are read while step kk's products run
-      U128 a0 = lds_load16(kt + k_addr(0));
-      U128 a1 = lds_load16(kt + k_addr(0) + 32 * Tr::kKRow);
+      U128 a0 = lds_load16(kt + kaddr[0]);
+      U128 a1 = lds_load16(kt + kaddr[0] + 32 * Tr::kKRow);
 #pragma unroll
       for (int kk = 0; kk < Tr::kQkSteps; ++kk) {
         U128 n0 = a0, n1 = a1;
         if (kk + 1 < Tr::kQkSteps) {
-          n0 = lds_load16(kt + k_addr(kk + 1));
-          n1 = lds_load16(kt + k_addr(kk + 1) + 32 * Tr::kKRow);
+          n0 = lds_load16(kt + kaddr[kk + 1]);
+          n1 = lds_load16(kt + kaddr[kk + 1] + 32 * Tr::kKRow);
         }
         __builtin_amdgcn_sched_barrier(0);
         s0 = mfma32_bf16(as_bf16x8(a0), as_bf16x8(*(const U128*)&qf[kk]), s0);
@@ -571,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       const int lo = lim_lo - j0 - kHStep * h;
       const int sk = a.sink_size - j0 - kHStep * h;
       constexpr bool two_sided = TWO_SIDED;
-      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float ls[4];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -584,7 +592,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             e1 = ((j1r <= hi) && (!two_sided || j1r >= lo || j1r < sk)) ? e1 : kNegInf;
           }
           const float p0 = fast_exp2(e0), p1 = fast_exp2(e1);
-          ls[(r >> 1) & 3] += p0 + p1;
+          if (b == 0 && r < 8) ls[r >> 1] = p0 + p1;  // first pair of each partial sum (0 + x is not folded)
+          else ls[(r >> 1) & 3] += p0 + p1;
           pk[b][r >> 1] = pack_bf16x2(p0, p1);
         }
       }
@@ -664,14 +673,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
     // P = exp2(x c - m c), packed to bf16 pairs in MFMA B-operand order;
     // four independent partial sums
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ls[4];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(s[b][r], c, -mc));
         const float p1 = fast_exp2(__builtin_fmaf(s[b][r + 1], c, -mc));
-        ls[(r >> 1) & 3] += p0 + p1;
+        if (b == 0 && r < 8) ls[r >> 1] = p0 + p1;  // first pair of each partial sum (0 + x is not folded)
+        else ls[(r >> 1) & 3] += p0 + p1;
         pk[b][r >> 1] = pack_bf16x2(p0, p1);
       }
     }
