@@ -511,6 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const bool capped = SOFTCAP && BIAS == kBiasNone && a.softcap_post <= 60.0f;
   float m_run = capped ? a.softcap_post : kNegInf;   // reference max (raised lazily, see below)
   float l_run = 0.0f;      // this lane's partial row sum (its half of the keys)
+  float mc_run = 0.0f;     // m_run c (general softmax path; 0 until a key is visible)
   f32x16 acc[Tr::kDBlocks];
 #pragma unroll
   for (int i = 0; i < Tr::kDBlocks; ++i) acc[i] = f32x16{};
@@ -665,11 +666,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // Lazy rescale: the reference max only moves when the tile max exceeds it
     // by more than 8 in log2 units, so P <= 2^8 and the rescale of O and l is
     // rare. O / l and m + log2(l) are unchanged by the choice of reference.
-    const bool raise = (mt - m_run) * c > 8.0f;   // m_run = -inf, mt finite -> true; both -inf -> false
-    const float alpha = raise ? fast_exp2((m_run - mt) * c) : 1.0f;   // 0 when m_run = -inf
+    const float dc = (mt - m_run) * c;   // +inf when m_run = -inf and mt is finite; NaN when both are -inf
+    const bool raise = dc > 8.0f;
+    const float alpha = raise ? fast_exp2(-dc) : 1.0f;   // 0 when m_run = -inf
     m_run = raise ? mt : m_run;
+    mc_run = raise ? mt * c : mc_run;    // m_run c, or 0 while every key seen so far is masked
     l_run *= alpha;
-    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+    const float mc = mc_run;
 
     // P = exp2(x c - m c), packed to bf16 pairs in MFMA B-operand order;
     // four independent partial sums
