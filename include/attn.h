@@ -194,7 +194,13 @@ typedef struct {
                           page_size) must be a multiple of 8 keys (BF16) or 16 keys (FP8),
                           and (head_dim_v - 1) * row stride * elem + 64 * elem < 2^31. Keys
                           past the used length may hold any bits: they are never used.
-                          Not supported by the varlen entry points (ATTN_ENOTSUP). */
+                          attn_fwd_varlen takes it too: V is then [Hkv, head_dim_v, total_k],
+                          keys contiguous along the packed token axis, addressed as
+                          v + head*v_stride[1] + c*v_stride[0] + token; every cu_seqlens_k entry
+                          must be a multiple of 8 keys (BF16) or 16 keys (FP8), so that each
+                          16-byte chunk of keys belongs to one sequence (device metadata: a
+                          precondition, checked under ATTN_VALIDATE). Not supported by
+                          attn_fwd_varlen_paged (ATTN_ENOTSUP). */
   int64_t v_pool_stride[3]; /* attn_fwd_paged / attn_fwd_varlen_paged: the V pool's {page, head,
                           slot} element strides when they differ from the K pool's (required with
                           head_dim_v != d); all zero = kv_stride for both pools. Same rules as
@@ -232,7 +238,8 @@ attn_status_t attn_fwd(const attn_params_t* p,
 /*
  * Varlen (group) mode. n sequences packed along the token axis:
  * Q [total_q, Hq, d], K [total_k, Hkv, d], V [total_k, Hkv, dv], O [total_q, Hq, dv]
- * (dv = head_dim_v, default d), addressed as base + token*stride[0] + head*stride[1] + c. Sequence s owns query tokens
+ * (dv = head_dim_v, default d), addressed as base + token*stride[0] + head*stride[1] + c (column-major V:
+ * see v_layout). Sequence s owns query tokens
  * cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and key tokens likewise
  * (int32 [n+1] device arrays, the seqstart_q/k pointers of the Composable Kernel
  * page's group-mode MakeKargs). max_seqlen_q / max_seqlen_k bound every

@@ -279,12 +279,14 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0, seq
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, scale=None,
                     causal=False, window=None, softcap=0.0, descale=(1.0, 1.0, 1.0), out=None, lse=None,
                     return_lse=True, sink_size=0, sink_logits=None, alibi_slopes=None, out_dtype=None,
-                    o_scale=1.0, min_seqlen_q=0, bias=None):
+                    o_scale=1.0, min_seqlen_q=0, bias=None, v_colmajor=False):
     """Varlen mode. q [Tq, Hq, d], k / v [Tk, Hkv, d], cu_seqlens int32 [n+1]
     on the device. Sequences with at most ``min_seqlen_q`` query tokens are
     skipped: their rows of out / lse are left as they were. ``bias`` (fp32
     [Hq|1, Tq, Kmax]): the bias of q-head h, packed query token t and the
-    sequence's key j at bias[h, t, j]. Returns (out [Tq, Hq, d], lse [Hq, Tq]
+    sequence's key j at bias[h, t, j]. With ``v_colmajor`` v is [Hkv, dv, Tk]
+    with keys contiguous (bf16 or fp8, dv = d, every cu_seqlens_k entry a
+    multiple of 8 keys, 16 for fp8). Returns (out [Tq, Hq, d], lse [Hq, Tq]
     or None)."""
     Tq, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -295,8 +297,13 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         raise ValueError("k and v must be 3-d [tokens, heads, dim]")
     _check_like("k", k, q)
     _check_like("v", v, q)
-    if not (k.shape[2] == d and v.shape[:2] == k.shape[:2]):
+    if v_colmajor:
+        if not (v.shape[0] == Hkv and v.shape[2] == k.shape[0]):
+            raise ValueError("column-major v must be [Hkv, dv, Tk]")
+    elif not (k.shape[2] == d and v.shape[:2] == k.shape[:2]):
         raise ValueError("k / v shapes do not match q")
+    if not (k.shape[2] == d):
+        raise ValueError(f"k has head dim {k.shape[2]}, q has {d}")
     if not (n >= 0):
         raise ValueError("cu_seqlens_q needs at least one entry")
     _check_index("cu_seqlens_q", cu_seqlens_q, q, n + 1)
@@ -304,7 +311,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     _check_params_tensors(q, sink_logits, bias, alibi_slopes)
     if not (bias is None or bias.dim() == 3):
         raise ValueError("a varlen bias is 3-d [Hq|1, Tq, Kmax]")
-    dv = v.shape[2]
+    dv = v.shape[1] if v_colmajor else v.shape[2]
     out_dtype = _resolve_out_dtype(q, out, out_dtype)
     _check_out(out, (Tq, Hq, dv), out_dtype, q)
     _check_lse(lse, (Hq, Tq), q)
@@ -313,14 +320,18 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     p.min_seqlen_q = int(min_seqlen_q)
     if dv != d:
         p.head_dim_v = dv
+    if v_colmajor:
+        p.v_layout = _lib.ATTN_V_COL_MAJOR
     if out is None:
         out = torch.empty((Tq, Hq, dv), dtype=out_dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
     st = lambda t: i64_array(t.stride()[:2])  # noqa: E731
+    # column-major v: {stride between head-dim rows, stride between heads}
+    vst = i64_array((v.stride(1), v.stride(0))) if v_colmajor else st(v)
     check(lib().attn_fwd_varlen(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), n, Tq, int(max_seqlen_q),
-                                int(max_seqlen_k), Hq, Hkv, d, st(q), st(k), st(v), st(out),
+                                int(max_seqlen_k), Hq, Hkv, d, st(q), st(k), vst, st(out),
                                 ctypes.c_void_p(0), 0, _stream(q)))
     return out, lse
 

@@ -154,8 +154,6 @@ attn_status_t check_mode_fields(const attn_params_t* p, bool batch_mode, bool va
   }
   if (p->min_seqlen_q != 0 && !varlen_mode)
     return fail(ATTN_EINVAL, "min_seqlen_q applies to attn_fwd_varlen only");
-  if (p->v_layout == ATTN_V_COL_MAJOR && varlen_mode)
-    return fail(ATTN_ENOTSUP, "column-major V is supported by attn_fwd and attn_fwd_paged only");
   return ATTN_OK;
 }
 
@@ -182,7 +180,8 @@ attn_status_t check_colmajor_v(const attn_params_t* p, int d, int len, const cha
   if (p->in_dtype == ATTN_F32) return fail(ATTN_ENOTSUP, "column-major V needs bf16 or fp8 inputs");
   if (dim_v(p, d) != d) return fail(ATTN_ENOTSUP, "column-major V needs head_dim_v = d");
   const int eb = elem_bytes(p->in_dtype), chunk = 16 / eb;
-  if (len % chunk) return fail(ATTN_EINVAL, "column-major V needs %s a multiple of %d (got %d)", what, chunk, len);
+  if (len >= 0 && len % chunk)  // len < 0: the row lengths are device metadata (varlen)
+    return fail(ATTN_EINVAL, "column-major V needs %s a multiple of %d (got %d)", what, chunk, len);
   if ((int64_t)(d - 1) * row_stride * eb + 64 * eb >= ((int64_t)1 << 31))
     return fail(ATTN_EINVAL, "column-major V: head-dim row stride too large");
   return ATTN_OK;
@@ -295,10 +294,15 @@ attn_status_t validate_range(const char* name, const int32_t* dev, int count, in
 }
 
 // cu[0] >= 0, non-decreasing, every length <= max_len, cu[n] <= total (total < 0: unbounded)
-attn_status_t validate_cu(const char* name, const int32_t* dev, int n, int max_len, int64_t total, hipStream_t s) {
+attn_status_t validate_cu(const char* name, const int32_t* dev, int n, int max_len, int64_t total, hipStream_t s,
+                          int multiple = 1) {
   std::vector<int32_t> h;
   TRY(fetch_i32(name, dev, (size_t)n + 1, s, h));
   if (h[0] < 0) return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s[0] = %d is negative", name, h[0]);
+  for (int i = 0; i <= n; ++i)
+    if (h[i] % multiple)
+      return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s[%d] = %d is not a multiple of %d (column-major V)", name, i, h[i],
+                  multiple);
   for (int i = 0; i < n; ++i) {
     const int64_t l = (int64_t)h[i + 1] - h[i];
     if (l < 0) return fail(ATTN_EINVAL, "ATTN_VALIDATE: %s decreases at entry %d (%d -> %d)", name, i, h[i], h[i + 1]);
@@ -534,11 +538,16 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   TRY(check_strides("v", v_stride, 2, eb));
   TRY(check_strides("o", o_stride, 2, ob));
   TRY(check_row_span("k", k_stride[0], eb, kPrefillTileRows));
-  TRY(check_row_span("v", v_stride[0], eb, kPrefillTileRows));
+  // column-major V: v_stride[0] is the stride between head-dim rows, keys run
+  // along the packed token axis; every cu_seqlens_k entry a multiple of one
+  // 16-byte chunk of keys (a precondition, checked under ATTN_VALIDATE)
+  const bool v_cm = p->v_layout == ATTN_V_COL_MAJOR;
+  if (v_cm) TRY(check_colmajor_v(p, d, -1, "", v_stride[0]));
+  else TRY(check_row_span("v", v_stride[0], eb, kPrefillTileRows));
   if (n == 0 || max_seqlen_q == 0) return ATTN_OK;
   if (validate_on()) {
     TRY(validate_cu("cu_seqlens_q", cu_seqlens_q, n, max_seqlen_q, total_q, (hipStream_t)stream));
-    TRY(validate_cu("cu_seqlens_k", cu_seqlens_k, n, max_seqlen_k, -1, (hipStream_t)stream));
+    TRY(validate_cu("cu_seqlens_k", cu_seqlens_k, n, max_seqlen_k, -1, (hipStream_t)stream, v_cm ? 16 / eb : 1));
   }
   float c_exp2, pre, post;
   logit_consts(p, &c_exp2, &pre, &post);
@@ -552,6 +561,7 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   a.lse_sb = 0; a.lse_sh = total_q;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
   a.min_seqlen_q = p->min_seqlen_q;
+  a.v_colmajor = v_cm;
   a.hq = Hq; a.hkv = Hkv; a.ratio = ratio;
   const int rows_tile = attn::prefill_rows_per_tile(p->in_dtype);
   a.n_qtiles = (int)(((int64_t)max_seqlen_q * ratio + rows_tile - 1) / rows_tile);
@@ -686,6 +696,8 @@ attn_status_t attn_fwd_varlen_paged(const attn_params_t* p, const void* q, const
                                     const int64_t o_stride[2], void* stream) {
   TRY(check_params(p, d));
   TRY(check_mode_fields(p, false, true));
+  if (p->v_layout == ATTN_V_COL_MAJOR)
+    return fail(ATTN_ENOTSUP, "column-major V is supported by attn_fwd, attn_fwd_varlen and attn_fwd_paged");
   const int dv = dim_v(p, d);
   const int64_t* v_st = v_pool_strides(p, kv_stride);
   if (dv != d && v_st == kv_stride)

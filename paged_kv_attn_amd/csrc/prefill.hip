@@ -104,8 +104,8 @@ enum MaskKind : int { kMaskNone = 0, kMaskRight = 1, kMaskWindow = 2 };
 
 template <int D, int DV, bool FP8, int MODE, int MK, bool SOFTCAP, int BIAS, bool VT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-  static_assert(!VT || (D == DV && MODE != kPrefillVarlen && MODE != kPrefillVarlenPaged),
-                "column-major V: equal head dims, batch or paged mode");
+  static_assert(!VT || (D == DV && MODE != kPrefillVarlenPaged),
+                "column-major V: equal head dims, batch, varlen or paged mode");
   constexpr bool MASK = MK != kMaskNone;
   constexpr bool TWO_SIDED = MK == kMaskWindow;   // the host guarantees a.wl >= 0
   using Tr = Traits<D, DV, FP8>;
@@ -175,7 +175,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     if (Lq <= a.min_seqlen_q) return;  // skipped sequence: its rows stay untouched
     q_off = (int64_t)q0 * a.q_sr;
     k_off = (int64_t)k0 * a.k_sr;
-    v_off = (int64_t)k0 * a.v_sr;
+    // column-major V: keys run along the packed token axis, so the sequence's
+    // keys start k0 elements into each head-dim row (a.v_sr is the row stride)
+    v_off = VT ? (int64_t)k0 : (int64_t)k0 * a.v_sr;
     o_off = (int64_t)q0 * a.o_sr;
     lse_off = q0;
     bias_off = (int64_t)q0 * a.bias_sr;  // group mode: rows follow the packed query tokens
@@ -929,10 +931,10 @@ hipError_t launch_v(const PrefillArgs& a, int nz, bool mask, bool softcap, hipSt
 
 template <int D, int DV, bool FP8, int MODE>
 hipError_t launch_m(const PrefillArgs& a, int nz, bool mask, bool softcap, hipStream_t s) {
-  if constexpr ((MODE == kPrefillBatch || MODE == kPrefillPaged) && D == DV) {
+  if constexpr ((MODE == kPrefillBatch || MODE == kPrefillPaged || MODE == kPrefillVarlen) && D == DV) {
     if (a.v_colmajor) return launch_v<D, DV, FP8, MODE, true>(a, nz, mask, softcap, s);
   } else {
-    if (a.v_colmajor) return hipErrorInvalidValue;  // batch or paged mode with equal head dims only
+    if (a.v_colmajor) return hipErrorInvalidValue;  // batch, varlen or paged mode with equal head dims only
   }
   return launch_v<D, DV, FP8, MODE, false>(a, nz, mask, softcap, s);
 }

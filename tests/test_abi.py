@@ -295,6 +295,20 @@ def test_v_layout_validation():
     r = lib().attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, 4, 32, 8, 1, 4096, 128, i64_array(st),
                        i64_array(kst), i64_array(vst), i64_array(st), NULL, NULL, FAKE, 1 << 30, NULL)
     assert r == 1 and "row stride too large" in _err()
+    # varlen: V [Hkv, d, total_k]; the per-sequence key counts are device
+    # metadata, so only the layout-wide checks apply on the host
+    st = [2 * 128, 128]
+    for kw, vst, msg in ((dict(head_dim_v=64), [1024, 128 * 1024], "head_dim_v"),
+                         (dict(), [1 << 24, 1 << 31], "row stride too large")):
+        p = _params(v_layout=_lib.ATTN_V_COL_MAJOR, **kw)
+        r = lib().attn_fwd_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 2, 10, 5, 5, 2, 2, 128,
+                                  i64_array(st), i64_array(st), i64_array(vst), i64_array(st), NULL, 0, NULL)
+        assert r in (1, 2) and msg in _err(), (kw, _err())
+    p = _params(v_layout=_lib.ATTN_V_COL_MAJOR)            # a valid column-major layout, nothing to do
+    r = lib().attn_fwd_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 0, 0, 5, 5, 2, 2, 128,
+                              i64_array(st), i64_array(st), i64_array([1024, 128 * 1024]), i64_array(st), NULL, 0,
+                              NULL)
+    assert r == 0, _err()
 
 
 def _vpaged(p, page=64, kv_start=NULL, table=FAKE, d=128):

@@ -1,10 +1,11 @@
 """GPU parity of column-major V against the fp64 oracle: V stored
 [B, Hkv, d, sk] (keys contiguous) in batch mode, bf16 and fp8, prefill and the
 split-KV decode path, and column-major V pages ([hdim_v, page_size] per
-kv-head) on paged decode and paged prefill; used lengths that end inside a
-16-byte chunk of keys with NaN-poisoned tails, windows, soft-cap, sinks, ALiBi
-and an elementwise bias. Decode with column-major V is bit-identical to decode
-with row-major V; paged prefill over column-major pages is bit-identical to
+kv-head) on paged decode and paged prefill, and V stored [Hkv, d, total_k] in
+varlen mode; used lengths that end inside a 16-byte chunk of keys with
+NaN-poisoned tails, windows, soft-cap, sinks, ALiBi and an elementwise bias.
+Decode with column-major V is bit-identical to decode with row-major V; paged
+prefill over column-major pages, and varlen prefill, are bit-identical to
 batch-mode prefill with the same keys and column-major V."""
 
 import numpy as np
@@ -162,3 +163,82 @@ def test_paged_colmajor_v_prefill(dtype, sq, page, head_major):
     o_c, l_c = pk.attn_fwd(t["q"], kc, vc, scale=case.scale, causal=True, seqused_k=used, descale=ds,
                            v_colmajor=True)
     assert torch.equal(C.bits(out), C.bits(o_c)) and torch.equal(C.bits(lse), C.bits(l_c))
+
+
+# ---------------------------------------------------------------------------
+# varlen mode: V [Hkv, d, total_k], keys contiguous along the packed token
+# axis, every sequence starting on a 16-byte chunk of keys.
+# ---------------------------------------------------------------------------
+
+def _varlen_vt(case, pad=0):
+    """The case's V as [Hkv, d, Tk] keys-contiguous rows; with ``pad`` the rows
+    are a view of longer, NaN-filled rows (row stride Tk + pad rounded up to 16
+    elements, a multiple of 16 bytes)."""
+    v = case.t["v"]
+    Tk, Hkv, d = v.shape
+    width = -(-(Tk + pad) // 16) * 16
+    big = torch.full((Hkv, d, width), float("nan"), dtype=torch.float32, device=DEV).to(v.dtype)
+    big[:, :, :Tk] = v.permute(1, 2, 0)
+    return big[:, :, :Tk]
+
+
+def _run_varlen_vt(case, vt, **kw):
+    t, m = case.t, case.meta
+    return pk.attn_fwd_varlen(t["q"], t["k"], vt, t["cu_seqlens_q"], t["cu_seqlens_k"], m["max_q"], m["max_k"],
+                              scale=case.scale, window=(case.window_left, case.window_right), softcap=case.softcap,
+                              descale=(case.descale["q"], case.descale["k"], case.descale["v"]), v_colmajor=True,
+                              **kw)
+
+
+@pytest.mark.parametrize("dtype,lens_q,lens_k,Hq,Hkv,d,kw", [
+    ("bf16", [1, 77, 300, 0, 129, 513], [8, 80, 304, 0, 136, 512], 8, 2, 128, dict(causal=True)),
+    ("bf16", [200, 64, 3], [192, 504, 8], 4, 1, 64, dict(window=(37, 0), softcap=30.0)),
+    ("bf16", [130, 257], [256, 128], 4, 4, 128, dict(causal=False)),
+    ("fp8", [300, 17, 200], [304, 32, 512], 16, 4, 128, dict(causal=True)),
+    ("fp8", [129, 64], [1024, 48], 8, 2, 128, dict(window=(200, 0), softcap=30.0)),
+])
+def test_varlen_colmajor_v_parity(dtype, lens_q, lens_k, Hq, Hkv, d, kw):
+    case = synth.varlen_case(lens_q, lens_k, Hq, Hkv, d, dtype, seed=sum(lens_k) + d, device=DEV, **kw)
+    out, lse = _run_varlen_vt(case, _varlen_vt(case, pad=48))
+    O, LSE = C.oracle_varlen(case)
+    C.assert_parity(out, lse.T, O, LSE.T, dtype, f"varlen column-major V {dtype} {lens_k} {kw}")
+    o_r, l_r = C.run_varlen(case)           # row-major V: the same sums, keys in another order
+    assert (o_r.float() - out.float()).abs().max().item() <= 1e-2
+    fin = torch.isfinite(l_r)                # rows with no visible key: -inf on both sides
+    assert torch.equal(fin, torch.isfinite(lse)) and torch.equal(l_r[~fin], lse[~fin])
+    assert (l_r[fin] - lse[fin]).abs().max().item() <= 1e-4
+
+
+def test_varlen_colmajor_v_bitexact_vs_padded_batch():
+    lens_q, lens_k = [1, 77, 300, 129, 513], [8, 80, 304, 136, 512]
+    Hq, Hkv, d = 8, 2, 128
+    case = synth.varlen_case(lens_q, lens_k, Hq, Hkv, d, "bf16", seed=33, causal=True, device=DEV)
+    vt = _varlen_vt(case)
+    out_v, lse_v = _run_varlen_vt(case, vt)
+    cq = case.t["cu_seqlens_q"].cpu().numpy()
+    ck = case.t["cu_seqlens_k"].cpu().numpy()
+    n, mq, mk = len(lens_q), max(lens_q), max(lens_k)
+    qp = torch.full((n, Hq, mq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kp = torch.full((n, Hkv, mk, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vp = torch.full((n, Hkv, d, mk), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for s in range(n):
+        qp[s, :, :lens_q[s]] = case.t["q"][cq[s]:cq[s + 1]].transpose(0, 1)
+        kp[s, :, :lens_k[s]] = case.t["k"][ck[s]:ck[s + 1]].transpose(0, 1)
+        vp[s, :, :, :lens_k[s]] = vt[:, :, ck[s]:ck[s + 1]]
+    uq = torch.tensor(lens_q, dtype=torch.int32, device=DEV)
+    uk = torch.tensor(lens_k, dtype=torch.int32, device=DEV)
+    out_b, lse_b = pk.attn_fwd(qp, kp, vp, scale=case.scale, causal=True, seqused_q=uq, seqused_k=uk,
+                               v_colmajor=True)
+    for s in range(n):
+        a, b = int(cq[s]), int(cq[s + 1])
+        assert torch.equal(C.bits(out_b[s, :, :b - a]), C.bits(out_v[a:b].transpose(0, 1))), f"seq {s}"
+        assert torch.equal(C.bits(lse_b[s, :, :b - a]), C.bits(lse_v[:, a:b])), f"LSE seq {s}"
+
+
+@pytest.mark.parametrize("dtype,bad", [("bf16", 20), ("fp8", 40)])
+def test_varlen_colmajor_v_offsets_checked(monkeypatch, dtype, bad):
+    monkeypatch.setenv("ATTN_VALIDATE", "1")
+    case = synth.varlen_case([16, 16], [bad, 48], 4, 2, 128, dtype, seed=7, device=DEV)
+    with pytest.raises(pk.AttnError) as e:
+        _run_varlen_vt(case, _varlen_vt(case))
+    assert e.value.status == 1 and "cu_seqlens_k[1]" in str(e.value) and "multiple" in str(e.value), str(e.value)
