@@ -298,8 +298,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     _check_like("k", k, q)
     _check_like("v", v, q)
     if v_colmajor:
-        if not (v.shape[0] == Hkv and v.shape[2] == k.shape[0]):
-            raise ValueError("column-major v must be [Hkv, dv, Tk]")
+        if not (v.shape[0] == Hkv and v.shape[2] == k.shape[0] and (v.shape[2] <= 1 or v.stride(2) == 1)):
+            raise ValueError("column-major v must be [Hkv, dv, Tk] with unit stride over keys")
     elif not (k.shape[2] == d and v.shape[:2] == k.shape[:2]):
         raise ValueError("k / v shapes do not match q")
     if not (k.shape[2] == d):

@@ -130,6 +130,8 @@ def test_paged_workspace_is_sized_from_the_table_row_stride():
     ("cu_strided", ValueError, "cu_seqlens_k must be contiguous"),
     ("v_dtype", TypeError, "v has dtype"),
     ("lse_shape", ValueError, "lse has shape"),
+    ("vcm_shape", ValueError, "column-major v must be"),       # [Tk, Hkv, d] passed as column-major
+    ("vcm_strided", ValueError, "unit stride"),                # keys not contiguous
 ])
 def test_attn_fwd_varlen_refuses_mismatched_tensors(what, exc, msg):
     q = torch.zeros(30, 4, 64, dtype=BF)
@@ -146,6 +148,11 @@ def test_attn_fwd_varlen_refuses_mismatched_tensors(what, exc, msg):
         v = v.to(F8)
     elif what == "lse_shape":
         kw["lse"] = torch.zeros(30, 4)
+    elif what == "vcm_shape":
+        kw["v_colmajor"] = True
+    elif what == "vcm_strided":
+        v = torch.zeros(2, 50, 64, dtype=BF).transpose(1, 2)     # [Hkv, d, Tk], stride 64 over keys
+        kw["v_colmajor"] = True
     with pytest.raises(exc, match=msg):
         pk.attn_fwd_varlen(q, k, v, cq, ck, 20, 30, causal=True, **kw)
 
