@@ -242,3 +242,32 @@ def test_varlen_colmajor_v_offsets_checked(monkeypatch, dtype, bad):
     with pytest.raises(pk.AttnError) as e:
         _run_varlen_vt(case, _varlen_vt(case))
     assert e.value.status == 1 and "cu_seqlens_k[1]" in str(e.value) and "multiple" in str(e.value), str(e.value)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_varlen_colmajor_v_random(seed):
+    """Seeded draws over dtype, GQA ratio, head dim, mask, soft-cap and ragged
+    lengths (key counts multiples of one 16-byte chunk, empty sequences included)."""
+    r = np.random.default_rng(7000 + seed)
+    dtype = "fp8" if r.random() < 0.4 else "bf16"
+    chunk = 16 if dtype == "fp8" else 8
+    d = 128 if dtype == "fp8" or r.random() < 0.6 else 64
+    Hkv = int(r.choice([1, 2, 4]))
+    Hq = Hkv * int(r.choice([1, 2, 4, 8]))
+    n = int(r.integers(1, 6))
+    lens_k = [chunk * int(r.integers(0, 48)) for _ in range(n)]
+    lens_q = [int(r.integers(0, 400)) for _ in range(n)]
+    kw = {}
+    mask = r.integers(0, 3)
+    if mask == 1:
+        kw["causal"] = True
+    elif mask == 2:
+        kw["window"] = (int(r.integers(0, 300)), int(r.integers(0, 50)))
+    if r.random() < 0.3:
+        kw["softcap"] = 30.0
+    case = synth.varlen_case(lens_q, lens_k, Hq, Hkv, d, dtype, seed=7100 + seed, device=DEV, **kw)
+    what = f"seed={seed} {dtype} d={d} Hq={Hq} Hkv={Hkv} lens_q={lens_q} lens_k={lens_k} {kw}"
+    print(what, flush=True)
+    out, lse = _run_varlen_vt(case, _varlen_vt(case, pad=int(r.integers(0, 64))))
+    O, LSE = C.oracle_varlen(case)
+    C.assert_parity(out, lse.T, O, LSE.T, dtype, what)
