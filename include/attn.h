@@ -198,8 +198,10 @@ typedef struct {
                           keys contiguous along the packed token axis, addressed as
                           v + head*v_stride[1] + c*v_stride[0] + token; every cu_seqlens_k entry
                           must be a multiple of 8 keys (BF16) or 16 keys (FP8), so that each
-                          16-byte chunk of keys belongs to one sequence (device metadata: a
-                          precondition, checked under ATTN_VALIDATE). Not supported by
+                          16-byte chunk of keys belongs to one sequence. These are device
+                          metadata: ATTN_VALIDATE refuses a call that breaks the rule, and
+                          without it a sequence whose key offset or count is off that grid
+                          reads no key and gets NaN rows of O and LSE. Not supported by
                           attn_fwd_varlen_paged (ATTN_ENOTSUP). */
   int64_t v_pool_stride[3]; /* attn_fwd_paged / attn_fwd_varlen_paged: the V pool's {page, head,
                           slot} element strides when they differ from the K pool's (required with

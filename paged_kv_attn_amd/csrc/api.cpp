@@ -540,7 +540,8 @@ attn_status_t attn_fwd_varlen(const attn_params_t* p, const void* q, const void*
   TRY(check_row_span("k", k_stride[0], eb, kPrefillTileRows));
   // column-major V: v_stride[0] is the stride between head-dim rows, keys run
   // along the packed token axis; every cu_seqlens_k entry a multiple of one
-  // 16-byte chunk of keys (a precondition, checked under ATTN_VALIDATE)
+  // 16-byte chunk of keys (refused under ATTN_VALIDATE; otherwise a sequence
+  // off that grid reads no key and gets NaN rows)
   const bool v_cm = p->v_layout == ATTN_V_COL_MAJOR;
   if (v_cm) TRY(check_colmajor_v(p, d, -1, "", v_stride[0]));
   else TRY(check_row_span("v", v_stride[0], eb, kPrefillTileRows));

@@ -167,7 +167,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   int64_t q_off, k_off, v_off, o_off, lse_off;
   int64_t bias_off = 0;  // elementwise bias: element offset of this sequence's row 0 (all heads)
   int kv0 = 0;       // logical position of key 0 in the sequence's page list
-  bool bad = false;  // varlen-paged: a negative key start -> NaN rows, nothing read
+  // varlen-paged: a negative key start; varlen with column-major V: a key offset
+  // or count off the 16-byte chunk grid -> NaN rows, no key read
+  bool bad = false;
   if (VARLEN) {
     const int q0 = a.cu_q[z], k0 = a.cu_k[z];
     Lq = a.cu_q[z + 1] - q0;
@@ -176,8 +178,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     q_off = (int64_t)q0 * a.q_sr;
     k_off = (int64_t)k0 * a.k_sr;
     // column-major V: keys run along the packed token axis, so the sequence's
-    // keys start k0 elements into each head-dim row (a.v_sr is the row stride)
+    // keys start k0 elements into each head-dim row (a.v_sr is the row stride);
+    // each 16-byte chunk of keys must belong to one sequence
     v_off = VT ? (int64_t)k0 : (int64_t)k0 * a.v_sr;
+    if (VT && ((k0 | Lk) & (16 / Tr::kElem - 1))) {
+      bad = true;
+      Lk = 0;
+    }
     o_off = (int64_t)q0 * a.o_sr;
     lse_off = q0;
     bias_off = (int64_t)q0 * a.bias_sr;  // group mode: rows follow the packed query tokens
@@ -819,7 +826,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
   }
-  if (VPAGED && bad) {  // not computed: NaN rows
+  if ((VPAGED || (VARLEN && VT)) && bad) {  // not computed: NaN rows
     inv = __builtin_nanf("");
     lse2 = __builtin_nanf("");
   }
@@ -864,7 +871,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * dblk + 8 * q4 + 4 * h;
-        if (VPAGED && bad) {  // the E4M3FN NaN byte
+        if ((VPAGED || (VARLEN && VT)) && bad) {  // the E4M3FN NaN byte
           *(uint32_t*)(op + d) = 0x7F7F7F7Fu;
         } else {
           *(uint32_t*)(op + d) = pack_fp8x4_sat(acc[dblk][4 * q4 + 0] * inv, acc[dblk][4 * q4 + 1] * inv,

@@ -271,3 +271,24 @@ def test_varlen_colmajor_v_random(seed):
     out, lse = _run_varlen_vt(case, _varlen_vt(case, pad=int(r.integers(0, 64))))
     O, LSE = C.oracle_varlen(case)
     C.assert_parity(out, lse.T, O, LSE.T, dtype, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_varlen_colmajor_v_off_grid_sequences_get_nan_rows(monkeypatch, dtype):
+    """Without ATTN_VALIDATE, a sequence whose key offset or key count is off the
+    16-byte chunk grid reads no key and gets NaN rows of O and LSE; the other
+    sequences of the call are unaffected."""
+    monkeypatch.delenv("ATTN_VALIDATE", raising=False)
+    c = 16 if dtype == "fp8" else 8
+    lens_k = [2 * c, 2 * c + 4, c - 4, 3 * c]     # seq 1: count off the grid; seq 2: offset and count
+    lens_q = [50, 40, 30, 70]
+    case = synth.varlen_case(lens_q, lens_k, 8, 2, 128, dtype, seed=77, causal=True, device=DEV)
+    out, lse = _run_varlen_vt(case, _varlen_vt(case))
+    O, LSE = C.oracle_varlen(case)
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    for s in range(4):
+        a, b = int(cq[s]), int(cq[s + 1])
+        if s in (1, 2):
+            assert torch.isnan(out[a:b].float()).all() and torch.isnan(lse[:, a:b]).all(), f"seq {s}"
+        else:
+            C.assert_parity(out[a:b], lse[:, a:b].T, O[a:b], LSE[:, a:b].T, dtype, f"seq {s}")
