@@ -323,6 +323,48 @@ def _stats(ts_ms):
     return mean, median, ts[0]
 
 
+def sclk_under_load(run, launch_ms, seconds=1.0):
+    """The shader clock (MHz) that rocm-smi reports about halfway through
+    `seconds` of back-to-back launches of run() (each about launch_ms), read
+    once from a child process; None when rocm-smi is absent or unreadable."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if exe is None:
+        return None
+    got = {}
+
+    def sample():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
+            got["text"] = r.stdout
+        except (OSError, subprocess.SubprocessError):
+            pass
+
+    th = threading.Thread(target=sample)
+    th.start()
+    for _ in range(max(1, int(seconds * 1e3 / max(launch_ms, 1e-3)))):
+        run()
+    torch.cuda.synchronize()
+    th.join()
+    try:
+        cards = json.loads(got.get("text") or "{}")
+    except ValueError:
+        return None
+    for card in sorted(cards):
+        for key, val in cards[card].items():
+            if key.startswith("sclk") and "speed" in key:
+                m = re.search(r"(\d+)", str(val))
+                if m:
+                    return int(m.group(1))
+    return None
+
+
 def time_launches(run, steps, warmup):
     """Mean, median and minimum duration (ms) of `steps` launches of run(),
     each bracketed by HIP events on torch's current stream, after `warmup`."""
@@ -661,6 +703,9 @@ def main():
     print(f"bench: prefill {pre_ms * 1e3:.1f} us (min {pre_min * 1e3:.1f}) {tflops:.1f} TFLOP/s; "
           f"decode {dec_ms * 1e3:.1f} us (min {dec_min * 1e3:.1f}) {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # the shader clock under the headline kernel (untimed; rocm-smi in a child process)
+    sclk = sclk_under_load(run_prefill, pre_ms)
+
     # the other workloads first: the tiny one is host-bound and is timed before
     # any multi-threaded oracle run has loaded the host
     others = {}
@@ -692,6 +737,8 @@ def main():
         "roofline": _roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill",
                               "prefill_kernel<128, bf16, batch, causal>", pre_ms, pre_med, pre_min,
                               "algorithmic_flops", flops),
+        "gpu_clock": {"sclk_mhz": sclk, "source": "rocm-smi --showclocks, read once midway through 1 s of "
+                                                  "back-to-back launches of the prefill kernel (untimed)"},
         "cpu_baseline": cpu,
         "paged_decode": {
             "value": round(gbs, 1), "unit": "GB/s",
