@@ -703,8 +703,10 @@ def main():
     print(f"bench: prefill {pre_ms * 1e3:.1f} us (min {pre_min * 1e3:.1f}) {tflops:.1f} TFLOP/s; "
           f"decode {dec_ms * 1e3:.1f} us (min {dec_min * 1e3:.1f}) {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
-    # the shader clock under the headline kernel (untimed; rocm-smi in a child process)
-    sclk = sclk_under_load(run_prefill, pre_ms)
+    # the shader clock under the headline kernel (untimed; rocm-smi in a child process).
+    # Not in --headline-only runs, which the profiler wraps: the extra launches
+    # would enter its kernel trace and counter passes.
+    sclk = None if args.headline_only else sclk_under_load(run_prefill, pre_ms)
 
     # the other workloads first: the tiny one is host-bound and is timed before
     # any multi-threaded oracle run has loaded the host
@@ -737,8 +739,9 @@ def main():
         "roofline": _roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "prefill",
                               "prefill_kernel<128, bf16, batch, causal>", pre_ms, pre_med, pre_min,
                               "algorithmic_flops", flops),
-        "gpu_clock": {"sclk_mhz": sclk, "source": "rocm-smi --showclocks, read once midway through 1 s of "
-                                                  "back-to-back launches of the prefill kernel (untimed)"},
+        "gpu_clock": None if args.headline_only else {
+            "sclk_mhz": sclk, "source": "rocm-smi --showclocks, read once midway through 1 s of back-to-back "
+                                        "launches of the prefill kernel (untimed)"},
         "cpu_baseline": cpu,
         "paged_decode": {
             "value": round(gbs, 1), "unit": "GB/s",
