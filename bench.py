@@ -66,11 +66,13 @@ def decode_bytes(case, eb: int = 2) -> float:
     return float(kv + q + o + lse + table + m["B"] * 4)
 
 
+# the files a kernel's machine code follows from: its sources and the build
+# options (paged_kv_attn_amd/build.py)
 KERNEL_SOURCES = {
     "prefill": ["paged_kv_attn_amd/csrc/prefill.hip", "paged_kv_attn_amd/csrc/common.hpp",
-                "paged_kv_attn_amd/csrc/kernels.hpp"],
+                "paged_kv_attn_amd/csrc/kernels.hpp", "paged_kv_attn_amd/build.py"],
     "decode": ["paged_kv_attn_amd/csrc/decode.hip", "paged_kv_attn_amd/csrc/common.hpp",
-               "paged_kv_attn_amd/csrc/kernels.hpp"],
+               "paged_kv_attn_amd/csrc/kernels.hpp", "paged_kv_attn_amd/build.py"],
 }
 PROFILES = {"prefill": "profiles/prefill_bf16_causal_b4_h16_s2048_d128.md",
             "decode": "profiles/decode_paged_bf16_64req_hq32_hkv8_d128.md"}
@@ -309,7 +311,8 @@ PROFILES.update({
     "paged_decode_fp8": "profiles/decode_paged_fp8_64req_hq32_hkv8_d128.md",
 })
 KERNEL_SOURCES.update({
-    "tiny_fp32": ["paged_kv_attn_amd/csrc/f32.hip", "paged_kv_attn_amd/csrc/kernels.hpp"],
+    "tiny_fp32": ["paged_kv_attn_amd/csrc/f32.hip", "paged_kv_attn_amd/csrc/kernels.hpp",
+                  "paged_kv_attn_amd/build.py"],
     "varlen_gqa_prefill": KERNEL_SOURCES["prefill"],
     "fp8_softcap_prefill": KERNEL_SOURCES["prefill"],
     "paged_decode_fp8": KERNEL_SOURCES["decode"],
